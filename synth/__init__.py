@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the block-FP8 linear layer.
+
+This module draws random tensors and nothing else: it holds none of the
+quantisation or GEMM arithmetic. Both the CPU oracle (``oracle/``) and the
+HIP library (``block_scaled_fp8_quant_amd``) are fed from here, so they see
+identical bytes.
+
+The pages measure on Llama 3.1 8B, Qwen3-8B(-Base) and the Qwen3-30B
+mixture-of-experts model with a math dataset (upppp.jp NeMo RL FP8 article,
+«重要度サンプリングで精度を保つ», «KVキャッシュとAttentionにも拡張», «まとめ»).
+Neither those weights nor that dataset are used: Gaussian tensors at those
+models' linear-layer shapes stand in for them.
+
+Every tensor is drawn in fp32 on the CPU from its own ``torch.Generator``
+(seeded from the workload, the layer index and a user seed) and rounded to
+bf16 with round-to-nearest-even.
+"""
+
+from dataclasses import dataclass
+
+import torch
+
+# (name, K, N): Y[M, N] = X[M, K] @ W[N, K]^T
+LLAMA31_8B_LINEARS = (
+    ("qkv", 4096, 6144),
+    ("o_proj", 4096, 4096),
+    ("gate_up", 4096, 28672),
+    ("down", 14336, 4096),
+)
+QWEN3_8B_LINEARS = (
+    ("qkv", 4096, 6144),
+    ("o_proj", 4096, 4096),
+    ("gate_up", 4096, 24576),
+    ("down", 12288, 4096),
+)
+
+# Qwen3-30B-A3B mixture-of-experts block
+MOE_TOKENS = 4096
+MOE_HIDDEN = 2048
+MOE_EXPERTS = 128
+MOE_TOPK = 8
+MOE_FFN = 768          # per-expert intermediate size; gate_up N = 2 * 768
+MOE_ZIPF_S = 1.1
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic workload: token count, layer shapes, input statistics."""
+    name: str
+    m: int
+    linears: tuple
+    outlier_frac: float
+    outlier_scale: float
+    pow2: bool
+
+
+WORKLOADS = {
+    # tiny: X [128, 256], W [384, 256], 1% outliers x50
+    "tiny": Workload("tiny", 128, (("tiny", 256, 384),), 0.01, 50.0, False),
+    # Llama-3.1-8B decode step, 256 tokens, 0.5% outliers x30
+    "llama8b_decode": Workload("llama8b_decode", 256, LLAMA31_8B_LINEARS, 0.005, 30.0, False),
+    # Llama-3.1-8B prefill/training, 8 sequences x 2048 tokens
+    "llama8b_prefill": Workload("llama8b_prefill", 16384, LLAMA31_8B_LINEARS, 0.005, 30.0, False),
+    # Qwen3-8B linears with power-of-two scales, 4096 tokens, no outliers
+    "qwen8b_pow2": Workload("qwen8b_pow2", 4096, QWEN3_8B_LINEARS, 0.0, 1.0, True),
+}
+
+_WORKLOAD_IDS = {"tiny": 0, "llama8b_decode": 1, "llama8b_prefill": 2, "qwen8b_pow2": 3, "moe": 4}
+
+
+def _gen(workload, part, seed):
+    g = torch.Generator(device="cpu")
+    g.manual_seed((int(seed) << 16) + (_WORKLOAD_IDS[workload] << 8) + int(part))
+    return g
+
+
+def activation(m, k, gen, outlier_frac=0.0, outlier_scale=1.0):
+    """X ~ N(0, 1) [m, k]; each entry independently becomes an outlier
+    (multiplied by ``outlier_scale``) with probability ``outlier_frac``."""
+    x = torch.randn(m, k, generator=gen, dtype=torch.float32)
+    if outlier_frac > 0:
+        mask = torch.rand(m, k, generator=gen) < outlier_frac
+        x = torch.where(mask, x * outlier_scale, x)
+    return x.to(torch.bfloat16)
+
+
+def weight(n, k, gen, std=0.02):
+    """W ~ N(0, std^2) [n, k] in nn.Linear layout."""
+    return (torch.randn(n, k, generator=gen, dtype=torch.float32) * std).to(torch.bfloat16)
+
+
+def linear_inputs(workload, layer, seed=0, m=None):
+    """(X [M, K], W [N, K]) bf16 for one linear of a dense workload.
+
+    ``layer`` is an index into the workload's linears or its name. ``m``
+    overrides the token count (rows are drawn first, so a smaller ``m``
+    is NOT a prefix of the full draw; use row sampling of the full tensor
+    when a prefix is needed).
+    """
+    wl = WORKLOADS[workload]
+    if isinstance(layer, str):
+        layer = [nm for nm, _, _ in wl.linears].index(layer)
+    name, k, n = wl.linears[layer]
+    rows = wl.m if m is None else m
+    gx = _gen(workload, 2 * layer, seed)
+    gw = _gen(workload, 2 * layer + 1, seed)
+    x = activation(rows, k, gx, wl.outlier_frac, wl.outlier_scale)
+    w = weight(n, k, gw)
+    return x, w
+
+
+def moe_routing(seed=0, tokens=MOE_TOKENS, experts=MOE_EXPERTS, topk=MOE_TOPK, s=MOE_ZIPF_S):
+    """Top-k expert choice per token with p_e proportional to (e+1)^-s.
+
+    Each token draws ``topk`` distinct experts. Returns (token_of_row,
+    expert_of_row, offsets): the (token, expert) pairs stably sorted by
+    expert then token, and int32 offsets[E+1] of each expert's first row.
+    """
+    g = _gen("moe", 0, seed)
+    p = torch.arange(1, experts + 1, dtype=torch.float64) ** (-s)
+    p = (p / p.sum()).to(torch.float32)
+    choice = torch.multinomial(p.expand(tokens, experts), topk, replacement=False, generator=g)
+    tok = torch.arange(tokens).repeat_interleave(topk)
+    exp = choice.reshape(-1)
+    key = exp * tokens + tok                     # sort by expert, then token
+    order = torch.argsort(key, stable=True)
+    tok, exp = tok[order], exp[order]
+    counts = torch.bincount(exp, minlength=experts)
+    offsets = torch.zeros(experts + 1, dtype=torch.int32)
+    offsets[1:] = torch.cumsum(counts, 0).to(torch.int32)
+    return tok, exp, offsets
+
+
+def moe_inputs(seed=0, which="gate_up", tokens=MOE_TOKENS, hidden=MOE_HIDDEN,
+               experts=MOE_EXPERTS, topk=MOE_TOPK, ffn=MOE_FFN):
+    """Grouped-GEMM inputs of the MoE block.
+
+    gate_up: X = the token activations [tokens, hidden] gathered in expert
+    order -> [tokens*topk, hidden]; W [experts, 2*ffn, hidden].
+    down: X [tokens*topk, ffn] drawn directly (the SwiGLU between the two is
+    not part of this path); W [experts, hidden, ffn].
+    Returns (X, W, offsets int32 [experts+1]).
+    """
+    tok, _, offsets = moe_routing(seed, tokens, experts, topk)
+    if which == "gate_up":
+        x_tok = activation(tokens, hidden, _gen("moe", 1, seed))
+        x = x_tok[tok]
+        w = weight(experts * 2 * ffn, hidden, _gen("moe", 2, seed)).reshape(experts, 2 * ffn, hidden)
+    elif which == "down":
+        x = activation(tokens * topk, ffn, _gen("moe", 3, seed))
+        w = weight(experts * hidden, ffn, _gen("moe", 4, seed)).reshape(experts, hidden, ffn)
+    else:
+        raise ValueError(which)
+    return x, w, offsets
+
+
+def small_moe_inputs(seed, tokens, hidden, experts, topk, n):
+    """A reduced MoE case with the same recipe (for parity at oracle sizes):
+    X [tokens*topk, hidden] in expert order, W [experts, n, hidden], offsets."""
+    tok, _, offsets = moe_routing(seed, tokens, experts, topk)
+    x_tok = activation(tokens, hidden, _gen("moe", 5, seed))
+    w = weight(experts * n, hidden, _gen("moe", 6, seed)).reshape(experts, n, hidden)
+    return x_tok[tok], w, offsets
+
+
+def generator(tag, seed=0):
+    """A seeded generator for ad-hoc test inputs (``tag`` < 256)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed((int(seed) << 16) + (0xF0 << 8) + int(tag))
+    return g
