@@ -1,0 +1,251 @@
+"""Throughput of the block-FP8 W8A8 linear-layer path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+for every linear of the workload, 128x128 weight quantisation (weights
+change every optimizer step), 1x128 activation quantisation and the
+block-scaled GEMM; the MoE workload runs the expert-grouped GEMM instead.
+
+Prints ONE JSON line (rank 0, N = 1). ``value`` is GEMM FLOPs per step over
+the measured step time (quantisation included), in TFLOP/s. ``roofline``
+covers the dominant kernel (the GEMM) with its average launch duration
+measured by HIP events on the launch stream inside the timed region.
+``cpu_baseline`` times the CPU oracle on a bounded sample of the same
+workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "block-FP8 W8A8 GEMM TFLOP/s + % FP8 MFMA peak (Llama-8B shapes)"
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+GEMM_KERNELS = ("gemm_kernel", "grouped_gemm_kernel")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="llama8b_prefill",
+                   choices=["llama8b_prefill", "llama8b_decode", "qwen8b_pow2", "moe"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-rows", type=int, default=1024)
+    return p.parse_args()
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "quant.hip", "common.h"):
+        with open(os.path.join(ROOT, "block_scaled_fp8_quant_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def build_layers(workload, dev):
+    """Synthetic bf16 inputs resident on the GPU plus preallocated outputs."""
+    import torch
+    import synth
+    layers = []
+    if workload == "moe":
+        for which in ("gate_up", "down"):
+            x, w, off = synth.moe_inputs(0, which)
+            e, n, k = w.shape
+            m = x.shape[0]
+            layers.append(dict(name="moe_" + which, x=x.to(dev), w=w.to(dev), off=off.to(dev),
+                               m=m, n=n, k=k, e=e, pow2=False,
+                               qa=torch.empty(m, k, dtype=torch.uint8, device=dev),
+                               sa=torch.empty(m, k // 128, dtype=torch.float32, device=dev),
+                               qw=torch.empty(e, n, k, dtype=torch.uint8, device=dev),
+                               sw=torch.empty(e, n // 128, k // 128, dtype=torch.float32, device=dev),
+                               y=torch.empty(m, n, dtype=torch.bfloat16, device=dev),
+                               flops=2.0 * m * n * k))
+            del x, w
+        return layers
+    wl = synth.WORKLOADS[workload]
+    for li, (name, k, n) in enumerate(wl.linears):
+        x, w = synth.linear_inputs(workload, li)
+        m = wl.m
+        layers.append(dict(name=name, x=x.to(dev), w=w.to(dev), m=m, n=n, k=k, e=0, pow2=wl.pow2,
+                           qa=torch.empty(m, k, dtype=torch.uint8, device=dev),
+                           sa=torch.empty(m, k // 128, dtype=torch.float32, device=dev),
+                           qw=torch.empty(n, k, dtype=torch.uint8, device=dev),
+                           sw=torch.empty(n // 128, k // 128, dtype=torch.float32, device=dev),
+                           y=torch.empty(m, n, dtype=torch.bfloat16, device=dev),
+                           flops=2.0 * m * n * k))
+        del x, w
+    return layers
+
+
+def step(fb, layers, events=None):
+    """One pass of the path. With ``events``, brackets every kernel launch
+    with HIP events on the launch stream: events[kind] gets (start, end)."""
+    import torch
+    stream = torch.cuda.current_stream()
+
+    def timed(kind, fn):
+        if events is None:
+            fn()
+            return
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        events.setdefault(kind, []).append((a, b))
+
+    for L in layers:
+        timed("quant_weight", lambda: fb.quant_weight(L["w"], L["pow2"], q=L["qw"], s=L["sw"]))
+    for L in layers:
+        timed("quant_act", lambda: fb.quant_act(L["x"], L["pow2"], q=L["qa"], s=L["sa"]))
+        if L["e"]:
+            timed("gemm", lambda: fb.grouped_gemm(L["qa"], L["sa"], L["qw"], L["sw"], L["off"], y=L["y"]))
+        else:
+            timed("gemm", lambda: fb.gemm(L["qa"], L["sa"], L["qw"], L["sw"], y=L["y"]))
+
+
+def kernel_bytes(layers):
+    """Algorithmic HBM bytes per launch kind, summed over one step."""
+    qa = sum(2 * L["m"] * L["k"] + L["m"] * L["k"] + 4 * L["m"] * L["k"] // 128 for L in layers)
+    rows_w = [L["n"] * L["k"] * max(L["e"], 1) for L in layers]
+    qw = sum(3 * r + 4 * r // 16384 for r in rows_w)
+    return {"quant_act": qa, "quant_weight": qw}
+
+
+def cpu_baseline(workload, rows):
+    """The oracle (untuned) on a bounded sample: for each linear, ``rows``
+    activation rows and two 128-row weight blocks are quantised and
+    multiplied. Inputs are drawn first (untimed, like the GPU's resident
+    inputs); the timed part is oracle work only. Scaled to TFLOP/s of GEMM
+    work like the GPU value."""
+    import numpy as np
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    threads = max([d.get("num_threads", 1) for d in threadpool_info()] + [1])
+    cases = []
+    if workload == "moe":
+        for which in ("gate_up", "down"):
+            x, w, off = synth.moe_inputs(0, which)
+            offs = off.numpy()
+            e = int(np.argmax(np.diff(offs)))
+            lo = int(offs[e])
+            cases.append((x[lo:lo + rows].clone(), w[e][:256].clone(), False))
+            del x, w
+        desc = "%d routed rows of the largest expert x 256 weight rows, gate_up and down" % rows
+    else:
+        wl = synth.WORKLOADS[workload]
+        for li in range(len(wl.linears)):
+            x, w = synth.linear_inputs(workload, li)
+            cases.append((x[:rows].clone(), w[:256].clone(), wl.pow2))
+            del x, w
+        desc = ("first %d activation rows x first 256 weight rows of each of the %d linears: "
+                "oracle quantisation (numpy) + block-wise fp64 GEMM" % (rows, len(wl.linears)))
+    flops = 0.0
+    t0 = time.perf_counter()
+    for xs, ws, pow2 in cases:
+        qa, sa = oracle.quant_act_ref(xs, pow2)
+        qw, sw = oracle.quant_weight_ref(ws, pow2)
+        oracle.gemm_ref(qa, sa, qw, sw)
+        flops += 2.0 * xs.shape[0] * ws.shape[0] * xs.shape[1]
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": desc, "seconds": round(dt, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this path is single-GPU only (no collectives); "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_scaled_fp8_quant_amd as fb
+    fb.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    layers = build_layers(args.workload, dev)
+    flops_step = sum(L["flops"] for L in layers)
+    print("bench: workload %s, %d layers, %.1f GFLOP/step" % (args.workload, len(layers), flops_step / 1e9),
+          file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step(fb, layers)
+    torch.cuda.synchronize()
+
+    events = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(fb, layers, events)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    per_kind = {k: [a.elapsed_time(b) for a, b in v] for k, v in events.items()}
+    gemm_ms = sum(per_kind["gemm"]) / args.steps           # GEMM time per step
+    gemm_avg_ms = sum(per_kind["gemm"]) / len(per_kind["gemm"])
+    gemm_flops_launch = flops_step / len(layers)
+    achieved = gemm_flops_launch / (gemm_avg_ms * 1e-3) / 1e12
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(args.workload)
+        if rec and rec.get("source_hash") == source_hash():
+            traffic = rec.get("gemm_bytes_per_launch")
+    kb = kernel_bytes(layers)
+    breakdown = {
+        "gemm_ms_per_step": round(gemm_ms, 4),
+        "gemm_tflops": round(flops_step / (gemm_ms * 1e-3) / 1e12, 1),
+        "quant_act_ms_per_step": round(sum(per_kind["quant_act"]) / args.steps, 4),
+        "quant_act_gbs": round(kb["quant_act"] / (sum(per_kind["quant_act"]) / args.steps * 1e-3) / 1e9, 1),
+        "quant_weight_ms_per_step": round(sum(per_kind["quant_weight"]) / args.steps, 4),
+        "quant_weight_gbs": round(kb["quant_weight"] / (sum(per_kind["quant_weight"]) / args.steps * 1e-3) / 1e9, 1),
+        "per_layer_gemm_us": {L["name"]: round(sum(per_kind["gemm"][i::len(layers)]) / args.steps * 1e3, 1)
+                              for i, L in enumerate(layers)},
+    }
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {"workload": args.workload,
+                   "m": layers[0]["m"],
+                   "linears": [[L["name"], L["k"], L["n"]] for L in layers],
+                   "pow2": layers[0]["pow2"],
+                   "step": "quant_weight x%d + quant_act x%d + %s x%d" % (
+                       len(layers), len(layers), "grouped_gemm" if layers[0]["e"] else "gemm", len(layers))},
+        "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic},
+        "breakdown": breakdown,
+    }
+    if args.workload in ("llama8b_decode", "moe"):
+        out["roofline"]["note"] = "below the FP8 ridge: HBM-bound shapes"
+    if not args.no_cpu_baseline:
+        print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

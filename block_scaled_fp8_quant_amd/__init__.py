@@ -1,0 +1,210 @@
+"""Block-scaled FP8 (E4M3) W8A8 linear layers on AMD MI355X (gfx950).
+
+A thin ctypes binding over libfp8blk.so (declared in include/fp8blk.h).
+Every step of the computation runs in the library's HIP kernels; this module
+only checks tensor shapes, dtypes and devices, allocates outputs with
+PyTorch and passes raw pointers plus the current HIP stream. There is no
+CPU fallback: if the library is missing, every call raises.
+
+Two layers:
+  * ``fp8blk_quant_act``, ``fp8blk_quant_weight``, ``fp8blk_gemm``,
+    ``fp8blk_grouped_gemm``: the C entry points under their own names
+    (integer device pointers, sizes, stream handle); they raise
+    ``Fp8BlkError`` on a non-OK status;
+  * ``quant_act``, ``quant_weight``, ``gemm``, ``grouped_gemm``: tensor
+    versions that validate shapes and allocate outputs.
+"""
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.so")
+BLOCK = 128
+
+STATUS = {0: "FP8BLK_OK", 1: "FP8BLK_ERR_INVALID_ARG", 2: "FP8BLK_ERR_SHAPE",
+          3: "FP8BLK_ERR_ALIGNMENT", 4: "FP8BLK_ERR_HIP"}
+
+_lib = None
+
+
+class Fp8BlkError(RuntimeError):
+    def __init__(self, func, status, text):
+        super().__init__("%s failed: %s (%s)" % (func, STATUS.get(status, status), text))
+        self.status = status
+
+
+def load():
+    """Load libfp8blk.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfp8blk.so is not built (%s); run __graft_entry__.build() "
+                           "or python -m block_scaled_fp8_quant_amd.build" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sigs = {
+        "fp8blk_quant_act": [vp, i64, i64, vp, vp, i32, vp],
+        "fp8blk_quant_weight": [vp, i64, i64, vp, vp, i32, vp],
+        "fp8blk_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
+        "fp8blk_grouped_gemm": [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.fp8blk_status_string.argtypes = [ctypes.c_int]
+    lib.fp8blk_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _call(name, *args):
+    lib = load()
+    st = getattr(lib, name)(*args)
+    if st != 0:
+        raise Fp8BlkError(name, st, lib.fp8blk_status_string(st).decode())
+    return st
+
+
+# ------------------------------------------------------------ C entry points
+
+def fp8blk_quant_act(x, M, K, q, s, pow2, stream):
+    return _call("fp8blk_quant_act", x, M, K, q, s, int(pow2), stream)
+
+
+def fp8blk_quant_weight(w, N, K, q, s, pow2, stream):
+    return _call("fp8blk_quant_weight", w, N, K, q, s, int(pow2), stream)
+
+
+def fp8blk_gemm(qa, sa, qw, sw, M, N, K, y, stream):
+    return _call("fp8blk_gemm", qa, sa, qw, sw, M, N, K, y, stream)
+
+
+def fp8blk_grouped_gemm(qa, sa, qw, sw, offsets, E, total_M, N, K, y, stream):
+    return _call("fp8blk_grouped_gemm", qa, sa, qw, sw, offsets, E, total_M, N, K, y, stream)
+
+
+# ------------------------------------------------------------ tensor API
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, dtype, shape, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a HIP device" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def quant_act(x, pow2=False, q=None, s=None):
+    """1x128 group quantisation of bf16 X[M, K] -> (Q uint8 [M, K], S fp32 [M, K/128])."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    m, k = x.shape
+    _check(x, "x", torch.bfloat16, (m, k))
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    q = torch.empty((m, k), dtype=torch.uint8, device=x.device) if q is None else q
+    s = torch.empty((m, k // BLOCK), dtype=torch.float32, device=x.device) if s is None else s
+    _check(q, "q", torch.uint8, (m, k), x.device)
+    _check(s, "s", torch.float32, (m, k // BLOCK), x.device)
+    fp8blk_quant_act(x.data_ptr(), m, k, q.data_ptr(), s.data_ptr(), pow2, _stream(x.device))
+    return q, s
+
+
+def quant_weight(w, pow2=False, q=None, s=None):
+    """128x128 block quantisation of bf16 W[N, K] (or an expert stack
+    [E, N, K], quantised as [E*N, K]) -> (Q uint8 like W, S fp32
+    [N/128, K/128] or [E, N/128, K/128])."""
+    torch = _torch()
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [N, K] or [E, N, K]")
+    k = w.shape[-1]
+    rows = w.numel() // k if k else 0
+    if w.shape[-2] % BLOCK or k % BLOCK:
+        raise ValueError("N and K must be multiples of 128")
+    sshape = tuple(w.shape[:-2]) + (w.shape[-2] // BLOCK, k // BLOCK)
+    _check(w, "w", torch.bfloat16, tuple(w.shape))
+    q = torch.empty(tuple(w.shape), dtype=torch.uint8, device=w.device) if q is None else q
+    s = torch.empty(sshape, dtype=torch.float32, device=w.device) if s is None else s
+    _check(q, "q", torch.uint8, tuple(w.shape), w.device)
+    _check(s, "s", torch.float32, sshape, w.device)
+    fp8blk_quant_weight(w.data_ptr(), rows, k, q.data_ptr(), s.data_ptr(), pow2, _stream(w.device))
+    return q, s
+
+
+def gemm(qa, sa, qw, sw, y=None):
+    """Y[M, N] bf16 = block-scaled (QA, SA) x (QW, SW)^T."""
+    torch = _torch()
+    if qa.dim() != 2 or qw.dim() != 2:
+        raise ValueError("qa must be [M, K] and qw [N, K]")
+    m, k = qa.shape
+    n = qw.shape[0]
+    if k % BLOCK or n % BLOCK:
+        raise ValueError("N and K must be multiples of 128")
+    dev = qa.device
+    _check(qa, "qa", torch.uint8, (m, k))
+    _check(sa, "sa", torch.float32, (m, k // BLOCK), dev)
+    _check(qw, "qw", torch.uint8, (n, k), dev)
+    _check(sw, "sw", torch.float32, (n // BLOCK, k // BLOCK), dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if y is None else y
+    _check(y, "y", torch.bfloat16, (m, n), dev)
+    fp8blk_gemm(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), m, n, k, y.data_ptr(),
+                _stream(dev))
+    return y
+
+
+def grouped_gemm(qa, sa, qw, sw, offsets, y=None):
+    """Expert-grouped GEMM: rows offsets[e]..offsets[e+1]-1 of (QA, SA) use
+    expert e's (QW[e], SW[e]). offsets: int32 [E+1] on the device, from 0 to
+    M, nondecreasing (not checked here: checking would need a device sync)."""
+    torch = _torch()
+    if qa.dim() != 2 or qw.dim() != 3:
+        raise ValueError("qa must be [M, K] and qw [E, N, K]")
+    m, k = qa.shape
+    e, n, _ = qw.shape
+    if k % BLOCK or n % BLOCK:
+        raise ValueError("N and K must be multiples of 128")
+    dev = qa.device
+    _check(qa, "qa", torch.uint8, (m, k))
+    _check(sa, "sa", torch.float32, (m, k // BLOCK), dev)
+    _check(qw, "qw", torch.uint8, (e, n, k), dev)
+    _check(sw, "sw", torch.float32, (e, n // BLOCK, k // BLOCK), dev)
+    _check(offsets, "offsets", torch.int32, (e + 1,), dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if y is None else y
+    _check(y, "y", torch.bfloat16, (m, n), dev)
+    fp8blk_grouped_gemm(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), offsets.data_ptr(),
+                        e, m, n, k, y.data_ptr(), _stream(dev))
+    return y
+
+
+def linear(x, qw, sw, pow2=False):
+    """One W8A8 linear layer: quantise X per 1x128 group, then the
+    block-scaled GEMM against pre-quantised weights. Returns Y bf16."""
+    qa, sa = quant_act(x, pow2)
+    return gemm(qa, sa, qw, sw)
+
+
+__all__ = [
+    "BLOCK", "Fp8BlkError", "LIB_PATH", "load",
+    "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
+    "quant_act", "quant_weight", "gemm", "grouped_gemm", "linear",
+]

@@ -1,0 +1,124 @@
+"""The C ABI of libfp8blk.so on the CPU: it loads, exports every function
+include/fp8blk.h declares, and rejects bad arguments with the documented
+status before making any HIP call (so no GPU is needed)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_fp8_quant_amd as fb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8blk.h")
+
+OK, INVALID, SHAPE, ALIGN = 0, 1, 2, 3
+P = 0x10000          # a 16-byte aligned fake device address; never dereferenced
+P4 = 0x10004         # 4-byte but not 16-byte aligned
+NULL = None
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fb.LIB_PATH):
+        pytest.skip("libfp8blk.so not built")
+    return fb.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fp8blk_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
+        "fp8blk_status_string"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = os.popen("nm -D --defined-only %s" % fb.LIB_PATH).read()
+    for name in declared_functions():
+        assert re.search(r"\bT %s\b" % name, out), name
+
+
+def test_status_strings(lib):
+    for st in range(5):
+        assert lib.fp8blk_status_string(st)
+    assert b"unknown" in lib.fp8blk_status_string(99)
+
+
+def test_quant_act_validation(lib):
+    f = lib.fp8blk_quant_act
+    assert f(P, -1, 128, P, P, 0, NULL) == INVALID
+    assert f(P, 4, 0, P, P, 0, NULL) == INVALID
+    assert f(P, 4, 128, P, P, 2, NULL) == INVALID          # pow2 flag
+    assert f(P, 4, 100, P, P, 0, NULL) == SHAPE
+    assert f(NULL, 4, 128, P, P, 0, NULL) == INVALID
+    assert f(P, 4, 128, NULL, P, 0, NULL) == INVALID
+    assert f(P, 4, 128, P, NULL, 0, NULL) == INVALID
+    assert f(P4, 4, 128, P, P, 0, NULL) == ALIGN
+    assert f(P, 4, 128, P4, P, 0, NULL) == ALIGN
+    assert f(P, 4, 128, P, P + 2, 0, NULL) == ALIGN
+    assert f(NULL, 0, 128, NULL, NULL, 1, NULL) == OK       # M == 0 is a no-op
+
+
+def test_quant_weight_validation(lib):
+    f = lib.fp8blk_quant_weight
+    assert f(P, -128, 128, P, P, 0, NULL) == INVALID
+    assert f(P, 128, -128, P, P, 0, NULL) == INVALID
+    assert f(P, 100, 128, P, P, 0, NULL) == SHAPE
+    assert f(P, 128, 200, P, P, 0, NULL) == SHAPE
+    assert f(P, 128, 128, P, P, -1, NULL) == INVALID
+    assert f(NULL, 128, 128, P, P, 0, NULL) == INVALID
+    assert f(P, 128, 128, P4, P, 0, NULL) == ALIGN
+    assert f(NULL, 0, 128, NULL, NULL, 0, NULL) == OK
+
+
+def test_gemm_validation(lib):
+    f = lib.fp8blk_gemm
+    assert f(P, P, P, P, -1, 128, 128, P, NULL) == INVALID
+    assert f(P, P, P, P, 4, 0, 128, P, NULL) == INVALID
+    assert f(P, P, P, P, 4, 128, 0, P, NULL) == INVALID
+    assert f(P, P, P, P, 4, 130, 128, P, NULL) == SHAPE
+    assert f(P, P, P, P, 4, 128, 130, P, NULL) == SHAPE
+    for i in range(5):
+        args = [P, P, P, P]
+        ptrs = args + [P]
+        ptrs[i] = NULL
+        assert f(ptrs[0], ptrs[1], ptrs[2], ptrs[3], 4, 128, 128, ptrs[4], NULL) == INVALID
+    assert f(P4, P, P, P, 4, 128, 128, P, NULL) == ALIGN
+    assert f(P, P, P4, P, 4, 128, 128, P, NULL) == ALIGN
+    assert f(P, P, P, P, 4, 128, 128, P4, NULL) == ALIGN
+    assert f(P, P + 1, P, P, 4, 128, 128, P, NULL) == ALIGN
+    assert f(NULL, NULL, NULL, NULL, 0, 128, 128, NULL, NULL) == OK
+
+
+def test_grouped_gemm_validation(lib):
+    f = lib.fp8blk_grouped_gemm
+    assert f(P, P, P, P, P, 0, 4, 128, 128, P, NULL) == SHAPE          # E < 1
+    assert f(P, P, P, P, P, 2, -1, 128, 128, P, NULL) == INVALID
+    assert f(P, P, P, P, P, 2, 4, 100, 128, P, NULL) == SHAPE
+    assert f(P, P, P, P, NULL, 2, 4, 128, 128, P, NULL) == INVALID      # offsets
+    assert f(P, P, P, P, P + 2, 2, 4, 128, 128, P, NULL) == ALIGN
+    assert f(P, P, P4, P, P, 2, 4, 128, 128, P, NULL) == ALIGN
+    assert f(NULL, NULL, NULL, NULL, NULL, 3, 0, 128, 128, NULL, NULL) == OK
+
+
+def test_python_entry_points_raise(lib):
+    with pytest.raises(fb.Fp8BlkError) as e:
+        fb.fp8blk_gemm(P, P, P, P, 4, 130, 128, P, None)
+    assert e.value.status == SHAPE
+
+
+def test_tensor_api_rejects_cpu_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        fb.quant_act(torch.zeros(2, 128, dtype=torch.bfloat16))
+    with pytest.raises(TypeError):
+        fb.quant_act(torch.zeros(2, 128, dtype=torch.float32).cuda() if torch.cuda.is_available()
+                     else torch.zeros(2, 128, dtype=torch.float32))

@@ -1,0 +1,172 @@
+"""GPU parity of the block-scaled GEMM and the expert-grouped GEMM against
+the oracle, through the C ABI. The oracle quantises the same bf16 inputs
+itself; outputs must lie within |y - y_ref| <= 2^-7 |y_ref| + 1e-3 rms(y_ref)."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_quant_amd as fb
+import oracle
+import synth
+from tests.gpu_util import (
+    assert_codes_equal, assert_within_tolerance, guarded, sample_rows,
+)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def _gemm_guarded(qa, sa, qw, sw):
+    y, check = guarded((qa.shape[0], qw.shape[0]), torch.bfloat16, DEV)
+    fb.gemm(qa, sa, qw, sw, y=y)
+    check()
+    return y
+
+
+def _layer_check(x, w, pow2=False):
+    qa, sa = fb.quant_act(x.to(DEV), pow2)
+    qw, sw = fb.quant_weight(w.to(DEV), pow2)
+    y = _gemm_guarded(qa, sa, qw, sw)
+    qa_r, sa_r = oracle.quant_act_ref(x, pow2)
+    qw_r, sw_r = oracle.quant_weight_ref(w, pow2)
+    assert_codes_equal(qa.cpu().numpy(), qa_r)
+    y_ref = oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r)
+    return assert_within_tolerance(y.float().cpu().numpy(), y_ref), y, y_ref
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_tiny_workload(fp8blk_lib, pow2):
+    x, w = synth.linear_inputs("tiny", 0)
+    _layer_check(x, w, pow2)
+
+
+def test_integer_closed_form_is_exact(fp8blk_lib):
+    """Unit scales and small-integer codes: every output is an integer of
+    magnitude <= 256, exact in fp32 and in bf16, so the GPU must match the
+    integer product bitwise."""
+    g = torch.Generator().manual_seed(21)
+    a = torch.randint(-1, 2, (200, 256), generator=g)
+    w = torch.randint(-1, 2, (384, 256), generator=g)
+    qa = torch.from_numpy(oracle.encode(a.numpy().astype(np.float64))).to(DEV)
+    qw = torch.from_numpy(oracle.encode(w.numpy().astype(np.float64))).to(DEV)
+    sa = torch.ones(200, 2, device=DEV)
+    sw = torch.ones(3, 2, device=DEV)
+    y = _gemm_guarded(qa, sa, qw, sw)
+    want = (a @ w.T).to(torch.float32)
+    assert torch.equal(y.float().cpu(), want)
+
+
+@pytest.mark.parametrize("m,k,n", [
+    (1, 128, 128), (7, 256, 384), (128, 128, 256), (130, 384, 128), (257, 1152, 640),
+    (300, 512, 1024), (64, 4096, 256),
+])
+def test_shapes_spanning_tiles(fp8blk_lib, m, k, n):
+    g = synth.generator(7, seed=m + 3 * k + 5 * n)
+    x = synth.activation(m, k, g, 0.005, 30.0)
+    w = synth.weight(n, k, g)
+    _layer_check(x, w)
+
+
+def test_zero_blocks_and_scale_doubling(fp8blk_lib):
+    g = synth.generator(8)
+    x = synth.activation(96, 384, g)
+    w = synth.weight(256, 384, g)
+    x[:, 128:256] = 0                            # a zero K-block for every row
+    w[128:, :] = 0                               # a zero weight block row
+    qa, sa = fb.quant_act(x.to(DEV))
+    qw, sw = fb.quant_weight(w.to(DEV))
+    assert torch.all(sa[:, 1] == 0)
+    y = fb.gemm(qa, sa, qw, sw)
+    assert torch.all(y[:, 128:].float() == 0)
+    sa2 = sa.clone()
+    sa2[5] *= 2
+    y2 = fb.gemm(qa, sa2, qw, sw)
+    assert torch.equal(y2[5].float(), 2 * y[5].float())
+    assert torch.equal(torch.cat([y2[:5], y2[6:]]), torch.cat([y[:5], y[6:]]))
+    qa_r, sa_r = oracle.quant_act_ref(x)
+    qw_r, sw_r = oracle.quant_weight_ref(w)
+    assert_within_tolerance(y.float().cpu().numpy(), oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r))
+
+
+def test_empty_is_noop(fp8blk_lib):
+    qa = torch.zeros(0, 256, dtype=torch.uint8, device=DEV)
+    sa = torch.zeros(0, 2, device=DEV)
+    qw = torch.zeros(128, 256, dtype=torch.uint8, device=DEV)
+    sw = torch.zeros(1, 2, device=DEV)
+    assert fb.gemm(qa, sa, qw, sw).shape == (0, 128)
+
+
+def test_deterministic(fp8blk_lib):
+    x, w = synth.linear_inputs("llama8b_decode", "qkv")
+    qa, sa = fb.quant_act(x.to(DEV))
+    qw, sw = fb.quant_weight(w.to(DEV))
+    ys = [fb.gemm(qa, sa, qw, sw) for _ in range(3)]
+    assert torch.equal(ys[0], ys[1]) and torch.equal(ys[0], ys[2])
+
+
+# ------------------------------------------------------------ grouped GEMM
+
+def _grouped_check(x, w, off, rows=None):
+    """GPU grouped GEMM vs the oracle, on all rows or on the given rows."""
+    e_count, n, k = w.shape
+    qa, sa = fb.quant_act(x.to(DEV))
+    qw, sw = fb.quant_weight(w.to(DEV))
+    y, check = guarded((x.shape[0], n), torch.bfloat16, DEV)
+    fb.grouped_gemm(qa, sa, qw, sw, off.to(DEV), y=y)
+    check()
+    offs = off.numpy().astype(np.int64)
+    if rows is None:
+        qa_r, sa_r = oracle.quant_act_ref(x)
+        qw_r, sw_r = oracle.quant_weight_ref(w.reshape(-1, k))
+        y_ref = oracle.grouped_gemm_ref(qa_r, sa_r, qw_r.reshape(e_count, n, k),
+                                        sw_r.reshape(e_count, n // 128, k // 128), offs)
+        assert_codes_equal(qa.cpu().numpy(), qa_r)
+        return assert_within_tolerance(y.float().cpu().numpy(), y_ref, what="grouped gemm")
+    experts = np.searchsorted(offs, rows, side="right") - 1
+    y_ref = np.zeros((len(rows), n))
+    qa_r, sa_r = oracle.quant_act_ref(x[torch.from_numpy(rows)])
+    for e in np.unique(experts):
+        qw_r, sw_r = oracle.quant_weight_ref(w[e])
+        sel = experts == e
+        y_ref[sel] = oracle.gemm_ref(qa_r[sel], sa_r[sel], qw_r, sw_r)
+    y_s = y[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    return assert_within_tolerance(y_s, y_ref, what="sampled grouped gemm")
+
+
+def test_grouped_small_moe(fp8blk_lib):
+    x, w, off = synth.small_moe_inputs(1, tokens=96, hidden=384, experts=8, topk=2, n=256)
+    _grouped_check(x, w, off)
+
+
+def test_grouped_with_empty_and_ragged_experts(fp8blk_lib):
+    counts = [0, 1, 129, 0, 256, 3, 0]
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32)
+    g = synth.generator(9)
+    x = synth.activation(int(off[-1]), 256, g, 0.01, 50.0)
+    w = synth.weight(len(counts) * 128, 256, g).reshape(len(counts), 128, 256)
+    _grouped_check(x, w, off)
+
+
+def test_grouped_single_expert_equals_gemm(fp8blk_lib):
+    x, w = synth.linear_inputs("tiny", 0)
+    qa, sa = fb.quant_act(x.to(DEV))
+    qw, sw = fb.quant_weight(w.to(DEV))
+    off = torch.tensor([0, x.shape[0]], dtype=torch.int32, device=DEV)
+    yg = fb.grouped_gemm(qa, sa, qw[None], sw[None], off)
+    assert torch.equal(yg, fb.gemm(qa, sa, qw, sw))
+
+
+@pytest.mark.parametrize("which", ["gate_up", "down"])
+def test_grouped_full_size_sampled(fp8blk_lib, which):
+    """The Qwen3-30B-A3B-shaped MoE layer at full size (32768 routed rows,
+    128 experts), sampled rows from the largest, smallest and random experts."""
+    print("full-size moe %s" % which, flush=True)
+    x, w, off = synth.moe_inputs(0, which)
+    offs = off.numpy().astype(np.int64)
+    counts = np.diff(offs)
+    gen = synth.generator(10)
+    rows = set(sample_rows(x.shape[0], 16, gen).tolist())
+    for e in (int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 10 ** 9)))):
+        rows |= {int(offs[e]), int(offs[e + 1] - 1)}
+    _grouped_check(x, w, off, rows=np.array(sorted(rows)))
