@@ -24,6 +24,9 @@ HIPCC_FLAGS = [
     "-shared",
     # no packed-fp32 VALU instructions anywhere in the device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the GEMM folds every partial with VALU FMAs,
+    # which cannot read accumulation registers directly
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -11,20 +11,41 @@
 // Kernel structure:
 //   * one workgroup computes a BM x BN output tile; its K loop steps one
 //     scale block (128) at a time, so the K tile IS the scale block;
-//   * A and B K-tiles (row-major, K contiguous) are staged through LDS,
-//     double buffered: the global loads of block b+1 are issued before the
-//     MFMAs of block b and written to the other LDS buffer afterwards; one
-//     barrier per K step;
-//   * LDS rows are 128 bytes; the 16-byte chunk c of row r is stored at
-//     chunk c ^ (r & 7), so the 16 rows an MFMA operand read touches hit
-//     distinct banks;
-//   * each wave owns a WM x WN sub-tile made of 16x16 tiles; one
+//   * A and B K-tiles (row-major, K contiguous) and the tile's row scales
+//     are staged through LDS, double buffered. The copies are direct
+//     global->LDS loads (global_load_lds_dwordx4 / _dword): they need no
+//     staging registers and run while the MFMAs of the previous block do;
+//   * LDS rows are 128 bytes; the 16-byte chunk c of row r sits at chunk
+//     c ^ (r & 7), so the 16 rows an MFMA operand read touches hit distinct
+//     banks. A direct load writes lane l's 16 bytes at slot l of a 1 KB
+//     window, so the swizzle is applied on the global side: the lane that
+//     fills slot (row, p) fetches logical chunk p ^ (row & 7);
+//   * each wave owns a WM x WN sub-tile of 16x16 tiles. One
 //     v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit block scales)
-//     yields the exact-in-fp32 partial dot product of one whole scale
-//     block, which is folded into the fp32 accumulator with one FMA:
-//     acc += partial * (SA[m][b] * SW[n/128][b]);
-//   * the epilogue rounds to bf16 (nearest even) and stores.
+//     gives the exact fp32 partial dot product of one whole scale block;
+//     a row of them is issued before the partials are folded into the fp32
+//     accumulators with one FMA each: acc += partial * (SA[m][b] * SW[n/128][b]);
+//   * the epilogue rounds to bf16 (nearest even) and stores;
+//   * workgroups are handed out round-robin over the 8 XCDs; the tile order
+//     gives each XCD a contiguous band of tiles so neighbours share A rows
+//     and B columns in that XCD's L2.
 #include "common.h"
+
+#ifndef FP8BLK_GEMM_BM
+#define FP8BLK_GEMM_BM 256
+#endif
+#ifndef FP8BLK_GEMM_BN
+#define FP8BLK_GEMM_BN 256
+#endif
+#ifndef FP8BLK_GEMM_WAVES_M
+#define FP8BLK_GEMM_WAVES_M 2
+#endif
+#ifndef FP8BLK_GEMM_WAVES_N
+#define FP8BLK_GEMM_WAVES_N 4
+#endif
+#ifndef FP8BLK_GEMM_GROUP_M
+#define FP8BLK_GEMM_GROUP_M 8
+#endif
 
 namespace fp8blk {
 namespace {
@@ -32,141 +53,195 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BK = kBlock;                  // K step = one scale block
-constexpr int BM = 128, BN = 128;           // workgroup tile
-constexpr int WAVES_M = 2, WAVES_N = 2;
-constexpr int NT = 64 * WAVES_M * WAVES_N;  // threads per workgroup
-constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-constexpr int TM = WM / 16, TN = WN / 16;   // 16x16 MFMA tiles per wave
-constexpr int A_LD = BM * (BK / 16) / NT;   // 16-byte loads per thread per K step
-constexpr int B_LD = BN * (BK / 16) / NT;
-static_assert(A_LD * NT == BM * 8 && B_LD * NT == BN * 8, "tile/threads mismatch");
-static_assert(BM <= NT, "one thread per A row loads the row scale");
-static_assert(kBlock % WN == 0, "a wave's columns lie in one weight block");
+constexpr int BK = kBlock;  // K step = one scale block
 
-struct Smem {
-  uint8_t a[2][BM * BK];
-  uint8_t b[2][BN * BK];
-  float sa[2][BM];
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+  static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  // 1 KB direct-load windows (8 rows of 128 bytes) per wave per K step
+  static constexpr int A_WIN = BM / 8 / WAVES, B_WIN = BN / 8 / WAVES;
+  static_assert(A_WIN * 8 * WAVES == BM && B_WIN * 8 * WAVES == BN, "rows per wave");
+  static_assert(BM % 64 == 0 && BM / 64 <= WAVES, "row scales: one dword window per wave");
+  static_assert(kBlock % WN == 0, "a wave's columns lie in one weight block");
+  static_assert(WM % 16 == 0 && WN % 16 == 0, "16x16 MFMA tiles");
+  static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
+  static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4;
+  static constexpr int LDS = 2 * STAGE;
 };
+
+using Cfg = Tile<FP8BLK_GEMM_BM, FP8BLK_GEMM_BN, FP8BLK_GEMM_WAVES_M, FP8BLK_GEMM_WAVES_N>;
+static_assert(Cfg::LDS <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
 
-// Read the 32 K-bytes of operand row `row` that lane group g = lane/16
-// supplies to the 16x16x128 MFMA. A and B use the same lane->K mapping, so
-// the dot product over the block is independent of how the instruction
-// orders K inside it.
+// The 32 K-bytes of operand row `row` that lane group g = lane/16 supplies to
+// the 16x16x128 MFMA. A and B use the same lane->K mapping, so the block's
+// dot product does not depend on how the instruction orders K inside it.
 __device__ __forceinline__ v8i read_frag(const uint8_t* tile, int row, int g) {
   const v4i lo = *reinterpret_cast<const v4i*>(tile + swz(row, 2 * g));
   const v4i hi = *reinterpret_cast<const v4i*>(tile + swz(row, 2 * g + 1));
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// Workgroup barrier without the release/acquire fences of __syncthreads():
+// those would wait for every outstanding global load, including the direct
+// loads of the next stage that are meant to stay in flight. LDS reads are
+// completed first; the memory clobber keeps the compiler from moving LDS
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Wait until at most N of this wave's global loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_window) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_window, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, uint8_t* lds_window) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_window, 4, 0, 0);
+}
+
+// Issue the direct loads of K block kb into LDS stage `st` (this wave's share).
+template <class C>
+__device__ __forceinline__ void issue_stage(uint8_t* smem, int st, int64_t kb, const uint8_t* const* a_row,
+                                            const uint8_t* const* b_row, const float* sa_row, int wave,
+                                            int chunk_off) {
+  uint8_t* stage = smem + st * C::STAGE;
+#pragma unroll
+  for (int i = 0; i < C::A_WIN; ++i)
+    dma16(a_row[i] + kb * BK + chunk_off, stage + (wave * C::A_WIN + i) * 1024);
+#pragma unroll
+  for (int i = 0; i < C::B_WIN; ++i)
+    dma16(b_row[i] + kb * BK + chunk_off, stage + C::A_BYTES + (wave * C::B_WIN + i) * 1024);
+  if (wave < C::BM / 64) dma4(sa_row + kb, stage + C::A_BYTES + C::B_BYTES + wave * 256);
+}
+
 // One BM x BN output tile at (m0, n0) of Y[M][N] = A[M][K] W[N][K]^T, with
 // rows >= M of A read as row M-1 (valid memory) and never stored. M >= 1.
+template <class C>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
                                           const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                           int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-                                          int64_t m0, int64_t n0, Smem& sm) {
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wm = (wave / WAVES_N) * WM;
-  const int wn = (wave % WAVES_N) * WN;
+                                          int64_t m0, int64_t n0, uint8_t* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
+  const int wm = (wave / C::WAVES_N) * C::WM;
+  const int wn = (wave % C::WAVES_N) * C::WN;
   const int g = lane >> 4;
   const int64_t KB = K / BK;
 
-  const uint4* a_src[A_LD];
-  int a_dst[A_LD];
+  // Direct-load sources: lane l fills slot l of a window = row l/8 of the
+  // window's 8 rows, physical chunk l%8, i.e. logical chunk (l%8) ^ (l/8).
+  const int win_row = lane >> 3;
+  const int chunk_off = (((lane & 7) ^ win_row) << 4);
+  const uint8_t* a_row[C::A_WIN];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int cid = t + i * NT, row = cid >> 3, c = cid & 7;
-    const int64_t gm = m0 + row < M ? m0 + row : M - 1;
-    a_src[i] = reinterpret_cast<const uint4*>(qa + gm * K) + c;
-    a_dst[i] = swz(row, c);
+  for (int i = 0; i < C::A_WIN; ++i) {
+    const int64_t r = m0 + (wave * C::A_WIN + i) * 8 + win_row;
+    a_row[i] = qa + (r < M ? r : M - 1) * K;
   }
-  const uint4* b_src[B_LD];
-  int b_dst[B_LD];
+  const uint8_t* b_row[C::B_WIN];
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int cid = t + i * NT, row = cid >> 3, c = cid & 7;
-    b_src[i] = reinterpret_cast<const uint4*>(qw + (n0 + row) * K) + c;
-    b_dst[i] = swz(row, c);
+  for (int i = 0; i < C::B_WIN; ++i) {
+    const int64_t r = n0 + (wave * C::B_WIN + i) * 8 + win_row;
+    b_row[i] = qw + (r < N ? r : N - 1) * K;
   }
-  const float* sa_src = sa + (m0 + t < M ? m0 + t : M - 1) * KB;
-  const float* sw_src = sw + ((n0 + wn) / kBlock) * KB;
+  const int64_t sr = m0 + wave * 64 + lane;
+  const float* sa_row = sa + (sr < M ? sr : M - 1) * KB;
+  // N % 128 == 0 and WN divides 128: a wave's columns are all in or all out
+  const bool cols_valid = n0 + wn < N;
+  const float* sw_row = sw + (cols_valid ? (n0 + wn) / kBlock : N / kBlock - 1) * KB;
 
-  uint4 ra[A_LD], rb[B_LD];
-  float rsa = 0.0f;
-  auto gload = [&](int64_t kb) {
+  v4f acc[C::TM][C::TN];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = a_src[i][kb * (BK / 16)];
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = b_src[i][kb * (BK / 16)];
-    if (t < BM) rsa = sa_src[kb];
-  };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) *reinterpret_cast<uint4*>(&sm.a[st][a_dst[i]]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) *reinterpret_cast<uint4*>(&sm.b[st][b_dst[i]]) = rb[i];
-    if (t < BM) sm.sa[st][t] = rsa;
-  };
-
-  v4f acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  issue_stage<C>(smem, 0, 0, a_row, b_row, sa_row, wave, chunk_off);
   for (int64_t kb = 0; kb < KB; ++kb) {
     const int st = (int)(kb & 1);
-    if (kb + 1 < KB) gload(kb + 1);
-    const float swv = sw_src[kb];
-    v8i bfr[TN];
-#pragma unroll
-    for (int j = 0; j < TN; ++j) bfr[j] = read_frag(sm.b[st], wn + 16 * j + (lane & 15), g);
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const v8i afr = read_frag(sm.a[st], wm + 16 * i + (lane & 15), g);
-      const v4f sa4 = *reinterpret_cast<const v4f*>(&sm.sa[st][wm + 16 * i + 4 * g]);
-      const v4f sc = sa4 * swv;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[r], sc[r], acc[i][j][r]);
-      }
+    if (kb + 1 < KB) {
+      issue_stage<C>(smem, st ^ 1, kb + 1, a_row, b_row, sa_row, wave, chunk_off);
+      // wait for this stage's loads only; the next stage's stay in flight
+      if (wave < C::BM / 64)
+        wait_vmcnt<C::A_WIN + C::B_WIN + 1>();
+      else
+        wait_vmcnt<C::A_WIN + C::B_WIN>();
+    } else {
+      wait_vmcnt<0>();
     }
-    if (kb + 1 < KB) sstore(st ^ 1);
-    __syncthreads();
+    lds_barrier();  // every wave's loads of this stage have landed
+
+    const uint8_t* sA = smem + st * C::STAGE;
+    const uint8_t* sB = sA + C::A_BYTES;
+    const float* sSA = reinterpret_cast<const float*>(sB + C::B_BYTES);
+    const float swv = sw_row[kb];
+    v8i bfr[C::TN];
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j) bfr[j] = read_frag(sB, wn + 16 * j + (lane & 15), g);
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const v8i afr = read_frag(sA, wm + 16 * i + (lane & 15), g);
+      const v4f sc = *reinterpret_cast<const v4f*>(&sSA[wm + 16 * i + 4 * g]) * swv;
+      v4f p[C::TN];
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 127, 0, 127);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[j][r], sc[r], acc[i][j][r]);
+    }
+    lds_barrier();  // every wave is done with stage st before it is refilled
   }
 
   // 16x16 accumulator layout: lane holds rows 4*(lane/16) + r, column lane%16
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int64_t row = m0 + wm + 16 * i + 4 * g + r;
-      if (row < M) {
+      if (row < M && cols_valid) {
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < C::TN; ++j)
           y[row * N + n0 + wn + 16 * j + (lane & 15)] = to_bf16_bits(acc[i][j][r]);
       }
     }
 }
 
-__global__ __launch_bounds__(NT) void gemm_kernel(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
-                                                  const uint8_t* __restrict__ qw, const float* __restrict__ sw,
-                                                  int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-                                                  int n_tiles) {
-  __shared__ Smem sm;
-  const int64_t m_tile = blockIdx.x / n_tiles, n_tile = blockIdx.x % n_tiles;
-  gemm_tile(qa, sa, qw, sw, M, N, K, y, m_tile * BM, n_tile * BN, sm);
+// Tile order: blocks are dealt to XCDs round-robin (block b runs on XCD
+// b % 8); renumber so each XCD sees a contiguous range, then walk that
+// range in bands of GROUP_M tile rows so that concurrently running tiles
+// share A rows and B columns.
+__device__ __forceinline__ void tile_of_block(int64_t bid, int64_t nblocks, int64_t m_tiles, int64_t n_tiles,
+                                              int64_t& m_tile, int64_t& n_tile) {
+  int64_t lid = bid;
+  if (nblocks % 8 == 0) lid = (bid % 8) * (nblocks / 8) + bid / 8;
+  const int64_t per_group = (int64_t)FP8BLK_GEMM_GROUP_M * n_tiles;
+  const int64_t group = lid / per_group;
+  const int64_t first_m = group * FP8BLK_GEMM_GROUP_M;
+  const int64_t rows = m_tiles - first_m < FP8BLK_GEMM_GROUP_M ? m_tiles - first_m : FP8BLK_GEMM_GROUP_M;
+  const int64_t in_group = lid % per_group;
+  m_tile = first_m + in_group % rows;
+  n_tile = in_group / rows;
+}
+
+__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
+                                                       const uint8_t* __restrict__ qw, const float* __restrict__ sw,
+                                                       int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
+                                                       int64_t m_tiles, int64_t n_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS];
+  int64_t m_tile, n_tile;
+  tile_of_block(blockIdx.x, gridDim.x, m_tiles, n_tiles, m_tile, n_tile);
+  gemm_tile<Cfg>(qa, sa, qw, sw, M, N, K, y, m_tile * Cfg::BM, n_tile * Cfg::BN, smem);
 }
 
 // Find which expert owns M-tile `t` of the concatenated per-expert tile
@@ -179,7 +254,7 @@ __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int
   int base = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
-    const int cnt = e < E ? (off[e + 1] - off[e] + BM - 1) / BM : 0;
+    const int cnt = e < E ? (off[e + 1] - off[e] + Cfg::BM - 1) / Cfg::BM : 0;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -199,22 +274,22 @@ __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int
   return false;
 }
 
-__global__ __launch_bounds__(NT) void grouped_gemm_kernel(const uint8_t* __restrict__ qa,
-                                                          const float* __restrict__ sa,
-                                                          const uint8_t* __restrict__ qw,
-                                                          const float* __restrict__ sw,
-                                                          const int32_t* __restrict__ offsets, int E,
-                                                          int64_t N, int64_t K, uint16_t* __restrict__ y,
-                                                          int n_tiles) {
-  __shared__ Smem sm;
+__global__ __launch_bounds__(Cfg::NT) void grouped_gemm_kernel(const uint8_t* __restrict__ qa,
+                                                               const float* __restrict__ sa,
+                                                               const uint8_t* __restrict__ qw,
+                                                               const float* __restrict__ sw,
+                                                               const int32_t* __restrict__ offsets, int E,
+                                                               int64_t N, int64_t K, uint16_t* __restrict__ y,
+                                                               int n_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS];
   const int t = blockIdx.x / n_tiles, n_tile = blockIdx.x % n_tiles;
   int e, tile;
   if (!locate_tile(offsets, E, t, e, tile)) return;  // uniform over the workgroup
   const int64_t row0 = offsets[e];
   const int64_t rows = offsets[e + 1] - row0;
   const int64_t KB = K / BK;
-  gemm_tile(qa + row0 * K, sa + row0 * KB, qw + (int64_t)e * N * K, sw + (int64_t)e * (N / kBlock) * KB,
-            rows, N, K, y + row0 * N, (int64_t)tile * BM, (int64_t)n_tile * BN, sm);
+  gemm_tile<Cfg>(qa + row0 * K, sa + row0 * KB, qw + (int64_t)e * N * K, sw + (int64_t)e * (N / kBlock) * KB,
+                 rows, N, K, y + row0 * N, (int64_t)tile * Cfg::BM, (int64_t)n_tile * Cfg::BN, smem);
 }
 
 fp8blk_status check_gemm_args(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
@@ -237,11 +312,11 @@ extern "C" fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa, const u
                                      int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const fp8blk_status st = check_gemm_args(qa, sa, qw, sw, M, N, K, y);
   if (st != FP8BLK_OK || M == 0) return st;
-  const int64_t n_tiles = N / BN;
-  const int64_t m_tiles = (M + BM - 1) / BM;
-  if (n_tiles * m_tiles > (1 << 24) || N % BN) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)(n_tiles * m_tiles)), dim3(NT), 0, stream, qa, sa, qw, sw, M,
-                     N, K, y, (int)n_tiles);
+  const int64_t n_tiles = (N + Cfg::BN - 1) / Cfg::BN;
+  const int64_t m_tiles = (M + Cfg::BM - 1) / Cfg::BM;
+  if (n_tiles * m_tiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)(n_tiles * m_tiles)), dim3(Cfg::NT), 0, stream, qa, sa, qw, sw,
+                     M, N, K, y, m_tiles, n_tiles);
   return launch_status();
 }
 
@@ -255,11 +330,11 @@ extern "C" fp8blk_status fp8blk_grouped_gemm(const uint8_t* qa, const float* sa,
   if (st != FP8BLK_OK || total_M == 0) return st;
   if (!offsets) return FP8BLK_ERR_INVALID_ARG;
   if (!aligned(offsets, 4)) return FP8BLK_ERR_ALIGNMENT;
-  const int64_t n_tiles = N / BN;
+  const int64_t n_tiles = (N + Cfg::BN - 1) / Cfg::BN;
   // upper bound on the number of M-tiles: sum_e ceil(M_e/BM) <= total_M/BM + E
-  const int64_t m_tiles = total_M / BM + E;
-  if (n_tiles * m_tiles > (1 << 24) || N % BN) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((uint32_t)(n_tiles * m_tiles)), dim3(NT), 0, stream, qa, sa, qw,
-                     sw, offsets, (int)E, N, K, y, (int)n_tiles);
+  const int64_t m_tiles = total_M / Cfg::BM + E;
+  if (n_tiles * m_tiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((uint32_t)(n_tiles * m_tiles)), dim3(Cfg::NT), 0, stream, qa, sa,
+                     qw, sw, offsets, (int)E, N, K, y, (int)n_tiles);
   return launch_status();
 }
