@@ -25,7 +25,9 @@
 //     gives the exact fp32 partial dot product of one whole scale block;
 //     a row of them is issued before the partials are folded into the fp32
 //     accumulators with one FMA each: acc += partial * (SA[m][b] * SW[n/128][b]);
-//   * the epilogue rounds to bf16 (nearest even) and stores;
+//     the MFMA produces the transposed tile so that each lane's quad is 4
+//     consecutive outputs of one row (one activation scale per quad);
+//   * the epilogue rounds to bf16 (nearest even) and stores 8 bytes a lane;
 //   * workgroups are handed out round-robin over the 8 XCDs; the tile order
 //     gives each XCD a contiguous band of tiles so neighbours share A rows
 //     and B columns in that XCD's L2.
@@ -46,6 +48,9 @@
 #ifndef FP8BLK_GEMM_GROUP_M
 #define FP8BLK_GEMM_GROUP_M 8
 #endif
+#ifndef FP8BLK_GEMM_SWZ_SHIFT
+#define FP8BLK_GEMM_SWZ_SHIFT 1
+#endif
 
 namespace fp8blk {
 namespace {
@@ -54,6 +59,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int BK = kBlock;  // K step = one scale block
 
@@ -72,13 +78,18 @@ struct Tile {
   static_assert(WM % 16 == 0 && WN % 16 == 0, "16x16 MFMA tiles");
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
   static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = 2 * STAGE;  // double buffered
 };
 
 using Cfg = Tile<FP8BLK_GEMM_BM, FP8BLK_GEMM_BN, FP8BLK_GEMM_WAVES_M, FP8BLK_GEMM_WAVES_N>;
 static_assert(Cfg::LDS <= 160 * 1024, "LDS budget");
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ (row & 7)) << 4); }
+// 16-byte chunk c of LDS row r is stored at chunk c ^ key(r), so the 16
+// rows that one operand read touches (same logical chunk) are spread over
+// different physical chunks. key = (r >> 1) & 7 and key = r & 7 measured
+// the same (every 1 KB ds_read_b128 takes 8 LDS cycles with either).
+__device__ __forceinline__ int swz_key(int row) { return (row >> FP8BLK_GEMM_SWZ_SHIFT) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key(row)) << 4); }
 
 // The 32 K-bytes of operand row `row` that lane group g = lane/16 supplies to
 // the 16x16x128 MFMA. A and B use the same lane->K mapping, so the block's
@@ -100,60 +111,86 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-__device__ __forceinline__ void dma16(const void* src, uint8_t* lds_window) {
+__device__ __forceinline__ void dma16(const uint8_t* src, lds_u8* lds_window) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_window, 16, 0, 0);
 }
-__device__ __forceinline__ void dma4(const void* src, uint8_t* lds_window) {
+__device__ __forceinline__ void dma4(const uint8_t* src, lds_u8* lds_window) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_window, 4, 0, 0);
 }
 
-// Issue the direct loads of K block kb into LDS stage `st` (this wave's share).
+// Per-lane constants of the direct loads. A load fills one 1 KB LDS window
+// (8 rows of 128 bytes); lane l writes slot l = (row l/8, physical chunk
+// l%8), so it fetches logical chunk (l%8) ^ key(row). Sources are a
+// wave-uniform base (advanced by 128 bytes per K step) plus a 32-bit lane
+// offset: row * K + chunk * 16 within the tile's rows.
 template <class C>
-__device__ __forceinline__ void issue_stage(uint8_t* smem, int st, int64_t kb, const uint8_t* const* a_row,
-                                            const uint8_t* const* b_row, const float* sa_row, int wave,
-                                            int chunk_off) {
-  uint8_t* stage = smem + st * C::STAGE;
+struct LoadPlan {
+  uint32_t a_off[C::A_WIN], b_off[C::B_WIN], s_off;
+};
+
+template <class C>
+__device__ __forceinline__ void issue_stage(lds_u8* stage, const uint8_t* a_base, const uint8_t* b_base,
+                                            const uint8_t* s_base, const LoadPlan<C>& lp, int wave) {
 #pragma unroll
-  for (int i = 0; i < C::A_WIN; ++i)
-    dma16(a_row[i] + kb * BK + chunk_off, stage + (wave * C::A_WIN + i) * 1024);
+  for (int i = 0; i < C::A_WIN; ++i) dma16(a_base + lp.a_off[i], stage + (wave * C::A_WIN + i) * 1024);
 #pragma unroll
   for (int i = 0; i < C::B_WIN; ++i)
-    dma16(b_row[i] + kb * BK + chunk_off, stage + C::A_BYTES + (wave * C::B_WIN + i) * 1024);
-  if (wave < C::BM / 64) dma4(sa_row + kb, stage + C::A_BYTES + C::B_BYTES + wave * 256);
+    dma16(b_base + lp.b_off[i], stage + C::A_BYTES + (wave * C::B_WIN + i) * 1024);
+  if (wave < C::BM / 64) dma4(s_base + lp.s_off, stage + C::A_BYTES + C::B_BYTES + wave * 256);
+}
+
+// acc[j] += p[j] * sc for the TN accumulator quads of one m-subtile.
+template <class C>
+__device__ __forceinline__ void fold_row(v4f (&acc)[C::TN], const v4f (&p)[C::TN], float sc) {
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[j][r], sc, acc[j][r]);
 }
 
 // One BM x BN output tile at (m0, n0) of Y[M][N] = A[M][K] W[N][K]^T, with
 // rows >= M of A read as row M-1 (valid memory) and never stored. M >= 1.
+//
+// The MFMA computes the transposed tile: source 0 is a 16-row weight
+// fragment (n), source 1 a 16-row activation fragment (m), so lane l holds
+// Y[m = l%16][n = 4*(l/16) + r], r < 4. Each lane therefore needs a single
+// activation scale per 16-row m-subtile (16 lanes read 16 consecutive
+// floats: no LDS bank conflict), the weight scale is uniform over the
+// wave, and the 4 accumulators of a quad are 4 consecutive outputs of one
+// row, stored as one 8-byte write.
 template <class C>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
                                           const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                           int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-                                          int64_t m0, int64_t n0, uint8_t* smem) {
+                                          int64_t m0, int64_t n0, uint8_t* smem_generic) {
+  lds_u8* smem = (lds_u8*)smem_generic;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int wm = (wave / C::WAVES_N) * C::WM;
   const int wn = (wave % C::WAVES_N) * C::WN;
-  const int g = lane >> 4;
+  const int g = lane >> 4, c16 = lane & 15;
   const int64_t KB = K / BK;
 
-  // Direct-load sources: lane l fills slot l of a window = row l/8 of the
-  // window's 8 rows, physical chunk l%8, i.e. logical chunk (l%8) ^ (l/8).
-  const int win_row = lane >> 3;
-  const int chunk_off = (((lane & 7) ^ win_row) << 4);
-  const uint8_t* a_row[C::A_WIN];
+  LoadPlan<C> lp;
 #pragma unroll
   for (int i = 0; i < C::A_WIN; ++i) {
-    const int64_t r = m0 + (wave * C::A_WIN + i) * 8 + win_row;
-    a_row[i] = qa + (r < M ? r : M - 1) * K;
+    const int row = (wave * C::A_WIN + i) * 8 + (lane >> 3);
+    const int64_t r = m0 + row < M ? row : M - 1 - m0;
+    lp.a_off[i] = (uint32_t)(r * K) + (((lane & 7) ^ swz_key(row)) << 4);
   }
-  const uint8_t* b_row[C::B_WIN];
 #pragma unroll
   for (int i = 0; i < C::B_WIN; ++i) {
-    const int64_t r = n0 + (wave * C::B_WIN + i) * 8 + win_row;
-    b_row[i] = qw + (r < N ? r : N - 1) * K;
+    const int row = (wave * C::B_WIN + i) * 8 + (lane >> 3);
+    const int64_t r = n0 + row < N ? row : N - 1 - n0;
+    lp.b_off[i] = (uint32_t)(r * K) + (((lane & 7) ^ swz_key(row)) << 4);
   }
-  const int64_t sr = m0 + wave * 64 + lane;
-  const float* sa_row = sa + (sr < M ? sr : M - 1) * KB;
+  {
+    const int64_t r = m0 + wave * 64 + lane < M ? wave * 64 + lane : M - 1 - m0;
+    lp.s_off = (uint32_t)(r * KB * 4);
+  }
+  const uint8_t* a_base = qa + m0 * K;
+  const uint8_t* b_base = qw + n0 * K;
+  const uint8_t* s_base = reinterpret_cast<const uint8_t*>(sa + m0 * KB);
   // N % 128 == 0 and WN divides 128: a wave's columns are all in or all out
   const bool cols_valid = n0 + wn < N;
   const float* sw_row = sw + (cols_valid ? (n0 + wn) / kBlock : N / kBlock - 1) * KB;
@@ -165,56 +202,53 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-  issue_stage<C>(smem, 0, 0, a_row, b_row, sa_row, wave, chunk_off);
+  // Two LDS stages. Iteration kb: wait for this wave's loads of block kb;
+  // barrier (every wave's block-kb data has landed, and every wave is done
+  // reading block kb-1, so its stage is free); refill that stage with block
+  // kb+1; compute block kb.
+  issue_stage<C>(smem, a_base, b_base, s_base, lp, wave);
   for (int64_t kb = 0; kb < KB; ++kb) {
     const int st = (int)(kb & 1);
-    if (kb + 1 < KB) {
-      issue_stage<C>(smem, st ^ 1, kb + 1, a_row, b_row, sa_row, wave, chunk_off);
-      // wait for this stage's loads only; the next stage's stay in flight
-      if (wave < C::BM / 64)
-        wait_vmcnt<C::A_WIN + C::B_WIN + 1>();
-      else
-        wait_vmcnt<C::A_WIN + C::B_WIN>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    lds_barrier();  // every wave's loads of this stage have landed
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (kb + 1 < KB)
+      issue_stage<C>(smem + (st ^ 1) * C::STAGE, a_base + (kb + 1) * BK, b_base + (kb + 1) * BK,
+                     s_base + (kb + 1) * 4, lp, wave);
 
-    const uint8_t* sA = smem + st * C::STAGE;
+    const uint8_t* sA = smem_generic + st * C::STAGE;
     const uint8_t* sB = sA + C::A_BYTES;
     const float* sSA = reinterpret_cast<const float*>(sB + C::B_BYTES);
     const float swv = sw_row[kb];
-    v8i bfr[C::TN];
+    v8i wfr[C::TN];
 #pragma unroll
-    for (int j = 0; j < C::TN; ++j) bfr[j] = read_frag(sB, wn + 16 * j + (lane & 15), g);
+    for (int j = 0; j < C::TN; ++j) wfr[j] = read_frag(sB, wn + 16 * j + c16, g);
 #pragma unroll
     for (int i = 0; i < C::TM; ++i) {
-      const v8i afr = read_frag(sA, wm + 16 * i + (lane & 15), g);
-      const v4f sc = *reinterpret_cast<const v4f*>(&sSA[wm + 16 * i + 4 * g]) * swv;
+      const v8i afr = read_frag(sA, wm + 16 * i + c16, g);
+      const float sc = sSA[wm + 16 * i + c16] * swv;
       v4f p[C::TN];
 #pragma unroll
       for (int j = 0; j < C::TN; ++j)
-        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(afr, bfr[j], zero, 0, 0, 0, 127, 0, 127);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = __builtin_fmaf(p[j][r], sc[r], acc[i][j][r]);
+        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], afr, zero, 0, 0, 0, 127, 0, 127);
+      fold_row<C>(acc[i], p, sc);
     }
-    lds_barrier();  // every wave is done with stage st before it is refilled
   }
 
-  // 16x16 accumulator layout: lane holds rows 4*(lane/16) + r, column lane%16
+  if (!cols_valid) return;
+  // lane holds Y[m0 + wm + 16i + l%16][n0 + wn + 16j + 4*(l/16) + r], r < 4
 #pragma unroll
-  for (int i = 0; i < C::TM; ++i)
+  for (int i = 0; i < C::TM; ++i) {
+    const int64_t row = m0 + wm + 16 * i + c16;
+    if (row < M) {
+      uint16_t* yr = y + row * N + n0 + wn + 4 * g;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t row = m0 + wm + 16 * i + 4 * g + r;
-      if (row < M && cols_valid) {
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          y[row * N + n0 + wn + 16 * j + (lane & 15)] = to_bf16_bits(acc[i][j][r]);
+      for (int j = 0; j < C::TN; ++j) {
+        const uint32_t lo = (uint32_t)to_bf16_bits(acc[i][j][0]) | ((uint32_t)to_bf16_bits(acc[i][j][1]) << 16);
+        const uint32_t hi = (uint32_t)to_bf16_bits(acc[i][j][2]) | ((uint32_t)to_bf16_bits(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(yr + 16 * j) = make_uint2(lo, hi);
       }
     }
+  }
 }
 
 // Tile order: blocks are dealt to XCDs round-robin (block b runs on XCD
