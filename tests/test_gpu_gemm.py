@@ -170,3 +170,47 @@ def test_grouped_full_size_sampled(fp8blk_lib, which):
     for e in (int(np.argmax(counts)), int(np.argmin(np.where(counts > 0, counts, 10 ** 9)))):
         rows |= {int(offs[e]), int(offs[e + 1] - 1)}
     _grouped_check(x, w, off, rows=np.array(sorted(rows)))
+
+
+def test_power_of_two_scales_mixed_and_zero(fp8blk_lib):
+    """Power-of-two scales, the same data with one scale nudged off a power of
+    two, and an all-zero group (zero scale) all match the oracle."""
+    g = synth.generator(11)
+    x = synth.activation(300, 512, g, 0.01, 50.0)
+    w = synth.weight(384, 512, g)
+    qa, sa = fb.quant_act(x.to(DEV), pow2=True)
+    qw, sw = fb.quant_weight(w.to(DEV), pow2=True)
+    qa_r, sa_r = oracle.quant_act_ref(x, pow2=True)
+    qw_r, sw_r = oracle.quant_weight_ref(w, pow2=True)
+    assert_within_tolerance(fb.gemm(qa, sa, qw, sw).float().cpu().numpy(),
+                            oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r), what="pow2 scales")
+    # one scale off a power of two
+    sa2 = sa.clone()
+    sa2[3, 1] *= 1.5
+    sa2_r = sa_r.copy()
+    sa2_r[3, 1] *= np.float32(1.5)
+    assert_within_tolerance(fb.gemm(qa, sa2, qw, sw).float().cpu().numpy(),
+                            oracle.gemm_ref(qa_r, sa2_r, qw_r, sw_r), what="mixed scales")
+    # an all-zero activation group: zero scale, exact zero contribution
+    x3 = x.clone()
+    x3[5, 128:256] = 0
+    qa3, sa3 = fb.quant_act(x3.to(DEV), pow2=True)
+    qa3_r, sa3_r = oracle.quant_act_ref(x3, pow2=True)
+    assert float(sa3[5, 1]) == 0.0
+    assert_within_tolerance(fb.gemm(qa3, sa3, qw, sw).float().cpu().numpy(),
+                            oracle.gemm_ref(qa3_r, sa3_r, qw_r, sw_r), what="zero scale")
+
+
+def test_power_of_two_extreme_exponents(fp8blk_lib):
+    """Power-of-two scales far from 1 (the operands scaled by 2^-100 and
+    2^90) still match the oracle."""
+    g = synth.generator(12)
+    for shift in (-100, 90):
+        x = (synth.activation(64, 256, g).float() * 2.0 ** shift).to(torch.bfloat16)
+        w = synth.weight(128, 256, g)
+        qa, sa = fb.quant_act(x.to(DEV), pow2=True)
+        qw, sw = fb.quant_weight(w.to(DEV), pow2=True)
+        qa_r, sa_r = oracle.quant_act_ref(x, pow2=True)
+        qw_r, sw_r = oracle.quant_weight_ref(w, pow2=True)
+        assert_within_tolerance(fb.gemm(qa, sa, qw, sw).float().cpu().numpy(),
+                                oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r), what="pow2 shift %d" % shift)
