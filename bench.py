@@ -13,6 +13,15 @@ measured by HIP events on the launch stream inside the timed region.
 workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+HBM traffic of the GEMM comes from two rocprofv3 counter passes over this
+same script (FETCH_SIZE, then WRITE_SIZE), each calibrated by a 1 GiB
+device copy run in the same process (--copy-yardstick):
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d F -o f -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-yardstick
+  rocprofv3 --pmc WRITE_SIZE --output-format csv -d W -o w -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-yardstick
+  python bench.py --summarize-traffic F/f_counter_collection.csv W/w_counter_collection.csv
+which writes profiles/traffic.json (keyed by a hash of the kernel sources,
+so a later kernel change turns the reported traffic back into null).
 """
 
 import argparse
@@ -40,7 +49,12 @@ def parse():
     p.add_argument("--workload", default="llama8b_prefill",
                    choices=["llama8b_prefill", "llama8b_decode", "qwen8b_pow2", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=1024)
+    p.add_argument("--cpu-sample-rows", type=int, default=4096)
+    p.add_argument("--cpu-sample-wrows", type=int, default=1024)
+    p.add_argument("--copy-yardstick", action="store_true",
+                   help="after timing, run a 1 GiB device copy (counter calibration)")
+    p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="turn two rocprofv3 --pmc CSVs into profiles/traffic.json and exit")
     return p.parse_args()
 
 
@@ -122,7 +136,7 @@ def kernel_bytes(layers):
     return {"quant_act": qa, "quant_weight": qw}
 
 
-def cpu_baseline(workload, rows):
+def cpu_baseline(workload, rows, wrows):
     """The oracle (untuned) on a bounded sample: for each linear, ``rows``
     activation rows and two 128-row weight blocks are quantised and
     multiplied. Inputs are drawn first (untimed, like the GPU's resident
@@ -140,17 +154,17 @@ def cpu_baseline(workload, rows):
             offs = off.numpy()
             e = int(np.argmax(np.diff(offs)))
             lo = int(offs[e])
-            cases.append((x[lo:lo + rows].clone(), w[e][:256].clone(), False))
+            cases.append((x[lo:lo + rows].clone(), w[e][:wrows].clone(), False))
             del x, w
-        desc = "%d routed rows of the largest expert x 256 weight rows, gate_up and down" % rows
+        desc = "%d routed rows of the largest expert x %d weight rows, gate_up and down" % (rows, wrows)
     else:
         wl = synth.WORKLOADS[workload]
         for li in range(len(wl.linears)):
             x, w = synth.linear_inputs(workload, li)
-            cases.append((x[:rows].clone(), w[:256].clone(), wl.pow2))
+            cases.append((x[:rows].clone(), w[:wrows].clone(), wl.pow2))
             del x, w
-        desc = ("first %d activation rows x first 256 weight rows of each of the %d linears: "
-                "oracle quantisation (numpy) + block-wise fp64 GEMM" % (rows, len(wl.linears)))
+        desc = ("first %d activation rows x first %d weight rows of each of the %d linears: "
+                "oracle quantisation (numpy) + block-wise fp64 GEMM" % (rows, wrows, len(wl.linears)))
     flops = 0.0
     t0 = time.perf_counter()
     for xs, ws, pow2 in cases:
@@ -163,8 +177,75 @@ def cpu_baseline(workload, rows):
             "sample": desc, "seconds": round(dt, 2)}
 
 
+COPY_BYTES = 1 << 30
+
+
+def copy_yardstick():
+    """A plain 1 GiB device-to-device copy: the counters' calibration."""
+    import torch
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda:0").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def summarize_traffic(fetch_csv, write_csv):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the GEMM kernel, scaled
+    by what the same counters read for the 1 GiB copy, into bytes."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+
+    def pick(d, key):
+        for name, v in d.items():
+            if key in name:
+                return v
+        raise KeyError(key)
+
+    gemm_key = "gemm_kernel"
+    copy_key = "copyBuffer"
+    g_f, g_w = pick(fetch, gemm_key), pick(write, gemm_key)
+    c_f, c_w = max(pick(fetch, copy_key)), max(pick(write, copy_key))
+    f_scale = COPY_BYTES / (c_f * 1024.0)
+    w_scale = COPY_BYTES / (c_w * 1024.0)
+    rec = {
+        "source_hash": source_hash(),
+        "gemm_fetch_kib_per_dispatch": statistics.mean(g_f),
+        "gemm_write_kib_per_dispatch": statistics.mean(g_w),
+        "gemm_dispatches": len(g_f),
+        "copy_fetch_kib": c_f, "copy_write_kib": c_w, "copy_bytes": COPY_BYTES,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "gemm_bytes_per_launch": statistics.mean(g_f) * 1024 * f_scale + statistics.mean(g_w) * 1024 * w_scale,
+    }
+    return rec
+
+
 def main():
     args = parse()
+    if args.summarize_traffic:
+        rec = summarize_traffic(*args.summarize_traffic)
+        db = {}
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                db = json.load(f)
+        db[args.workload] = rec
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(db, f, indent=1, sort_keys=True)
+            f.write("\n")
+        print(json.dumps(rec))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this path is single-GPU only (no collectives); "
               "--gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -192,6 +273,8 @@ def main():
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
+    if args.copy_yardstick:
+        copy_yardstick()
     per_kind = {k: [a.elapsed_time(b) for a, b in v] for k, v in events.items()}
     gemm_ms = sum(per_kind["gemm"]) / args.steps           # GEMM time per step
     gemm_avg_ms = sum(per_kind["gemm"]) / len(per_kind["gemm"])
@@ -204,6 +287,9 @@ def main():
         if rec and rec.get("source_hash") == source_hash():
             traffic = rec.get("gemm_bytes_per_launch")
     kb = kernel_bytes(layers)
+    gemm_alg_bytes = sum(L["m"] * L["k"] + L["n"] * L["k"] * max(L["e"], 1) + 4 * L["m"] * L["k"] // 128
+                         + 4 * L["n"] * L["k"] * max(L["e"], 1) // 16384 + 2 * L["m"] * L["n"]
+                         for L in layers) / len(layers)
     breakdown = {
         "gemm_ms_per_step": round(gemm_ms, 4),
         "gemm_tflops": round(flops_step / (gemm_ms * 1e-3) / 1e12, 1),
@@ -236,14 +322,17 @@ def main():
                        len(layers), len(layers), "grouped_gemm" if layers[0]["e"] else "gemm", len(layers))},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": traffic},
+                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes_per_launch": round(gemm_alg_bytes),
+                     "flops_per_launch": gemm_flops_launch, "avg_launch_ms": round(gemm_avg_ms, 4)},
         "breakdown": breakdown,
     }
     if args.workload in ("llama8b_decode", "moe"):
         out["roofline"]["note"] = "below the FP8 ridge: HBM-bound shapes"
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows)
     print(json.dumps(out), flush=True)
 
 
