@@ -33,23 +33,8 @@
 //     and B columns in that XCD's L2.
 #include "common.h"
 
-#ifndef FP8BLK_GEMM_BM
-#define FP8BLK_GEMM_BM 256
-#endif
-#ifndef FP8BLK_GEMM_BN
-#define FP8BLK_GEMM_BN 256
-#endif
-#ifndef FP8BLK_GEMM_WAVES_M
-#define FP8BLK_GEMM_WAVES_M 2
-#endif
-#ifndef FP8BLK_GEMM_WAVES_N
-#define FP8BLK_GEMM_WAVES_N 4
-#endif
 #ifndef FP8BLK_GEMM_GROUP_M
 #define FP8BLK_GEMM_GROUP_M 8
-#endif
-#ifndef FP8BLK_GEMM_SWZ_SHIFT
-#define FP8BLK_GEMM_SWZ_SHIFT 1
 #endif
 
 namespace fp8blk {
@@ -81,14 +66,21 @@ struct Tile {
   static constexpr int LDS = 2 * STAGE;  // double buffered
 };
 
-using Cfg = Tile<FP8BLK_GEMM_BM, FP8BLK_GEMM_BN, FP8BLK_GEMM_WAVES_M, FP8BLK_GEMM_WAVES_N>;
-static_assert(Cfg::LDS <= 160 * 1024, "LDS budget");
+// Tile configurations, picked per call from the problem shape (host side):
+//   Big   256x256, 8 waves of 128x64: large M and N (one workgroup per CU);
+//   Mid   128x128, 4 waves of 64x64: medium problems, expert groups of ~100+ rows;
+//   Small  64x64,  4 waves of 64x16: few rows (decode steps, small experts),
+//          enough workgroups to occupy every CU.
+using Big = Tile<256, 256, 2, 4>;
+using Mid = Tile<128, 128, 2, 2>;
+using Small = Tile<64, 64, 1, 4>;
+static_assert(Big::LDS <= 160 * 1024 && Mid::LDS <= 80 * 1024 && Small::LDS <= 40 * 1024, "LDS budget");
 
 // 16-byte chunk c of LDS row r is stored at chunk c ^ key(r), so the 16
 // rows that one operand read touches (same logical chunk) are spread over
 // different physical chunks. key = (r >> 1) & 7 and key = r & 7 measured
 // the same (every 1 KB ds_read_b128 takes 8 LDS cycles with either).
-__device__ __forceinline__ int swz_key(int row) { return (row >> FP8BLK_GEMM_SWZ_SHIFT) & 7; }
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * BK + ((chunk ^ swz_key(row)) << 4); }
 
 // The 32 K-bytes of operand row `row` that lane group g = lane/16 supplies to
@@ -268,6 +260,7 @@ __device__ __forceinline__ void tile_of_block(int64_t bid, int64_t nblocks, int6
   n_tile = in_group / rows;
 }
 
+template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
                                                        const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                                        int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
@@ -282,13 +275,14 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const uint8_t* __restrict
 // lists (expert e has ceil(M_e / BM) tiles). Every lane of the wave
 // computes the same answer: lanes take 64 experts at a time and a wave
 // prefix sum turns per-expert tile counts into tile ranges.
+template <int BM>
 __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int E, int t, int& expert,
                                             int& tile_in_expert) {
   const int lane = threadIdx.x & 63;
   int base = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
-    const int cnt = e < E ? (off[e + 1] - off[e] + Cfg::BM - 1) / Cfg::BM : 0;
+    const int cnt = e < E ? (off[e + 1] - off[e] + BM - 1) / BM : 0;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -308,6 +302,7 @@ __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int
   return false;
 }
 
+template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT) void grouped_gemm_kernel(const uint8_t* __restrict__ qa,
                                                                const float* __restrict__ sa,
                                                                const uint8_t* __restrict__ qw,
@@ -318,7 +313,7 @@ __global__ __launch_bounds__(Cfg::NT) void grouped_gemm_kernel(const uint8_t* __
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS];
   const int t = blockIdx.x / n_tiles, n_tile = blockIdx.x % n_tiles;
   int e, tile;
-  if (!locate_tile(offsets, E, t, e, tile)) return;  // uniform over the workgroup
+  if (!locate_tile<Cfg::BM>(offsets, E, t, e, tile)) return;  // uniform over the workgroup
   const int64_t row0 = offsets[e];
   const int64_t rows = offsets[e + 1] - row0;
   const int64_t KB = K / BK;
@@ -342,18 +337,56 @@ fp8blk_status check_gemm_args(const uint8_t* qa, const float* sa, const uint8_t*
 
 using namespace fp8blk;
 
+namespace fp8blk {
+namespace {
+
+constexpr int64_t kCUs = 256;  // MI355X compute units
+
+template <class Cfg>
+fp8blk_status launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw, int64_t M,
+                          int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  const int64_t n_tiles = (N + Cfg::BN - 1) / Cfg::BN;
+  const int64_t m_tiles = (M + Cfg::BM - 1) / Cfg::BM;
+  if (n_tiles * m_tiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(gemm_kernel<Cfg>, dim3((uint32_t)(n_tiles * m_tiles)), dim3(Cfg::NT), 0, stream, qa, sa, qw,
+                     sw, M, N, K, y, m_tiles, n_tiles);
+  return launch_status();
+}
+
+template <class Cfg>
+fp8blk_status launch_grouped(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                             const int32_t* offsets, int64_t E, int64_t total_M, int64_t N, int64_t K, uint16_t* y,
+                             hipStream_t stream) {
+  const int64_t n_tiles = (N + Cfg::BN - 1) / Cfg::BN;
+  // upper bound on the number of M-tiles: sum_e ceil(M_e/BM) <= total_M/BM + E
+  const int64_t m_tiles = total_M / Cfg::BM + E;
+  if (n_tiles * m_tiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3((uint32_t)(n_tiles * m_tiles)), dim3(Cfg::NT), 0, stream, qa,
+                     sa, qw, sw, offsets, (int)E, N, K, y, (int)n_tiles);
+  return launch_status();
+}
+
+template <class Cfg>
+int64_t tiles_of(int64_t M, int64_t N) {
+  return ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+}
+
+}  // namespace
+}  // namespace fp8blk
+
+// The largest tile that still gives every CU at least two workgroups' worth
+// of tiles; below that, the smallest.
 extern "C" fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                                      int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const fp8blk_status st = check_gemm_args(qa, sa, qw, sw, M, N, K, y);
   if (st != FP8BLK_OK || M == 0) return st;
-  const int64_t n_tiles = (N + Cfg::BN - 1) / Cfg::BN;
-  const int64_t m_tiles = (M + Cfg::BM - 1) / Cfg::BM;
-  if (n_tiles * m_tiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(gemm_kernel, dim3((uint32_t)(n_tiles * m_tiles)), dim3(Cfg::NT), 0, stream, qa, sa, qw, sw,
-                     M, N, K, y, m_tiles, n_tiles);
-  return launch_status();
+  if (tiles_of<Big>(M, N) >= kCUs) return launch_gemm<Big>(qa, sa, qw, sw, M, N, K, y, stream);
+  if (tiles_of<Mid>(M, N) >= 2 * kCUs) return launch_gemm<Mid>(qa, sa, qw, sw, M, N, K, y, stream);
+  return launch_gemm<Small>(qa, sa, qw, sw, M, N, K, y, stream);
 }
 
+// Expert groups: 128-row tiles when the average expert has at least 128
+// rows, else 64-row tiles (less padding in partly filled tiles).
 extern "C" fp8blk_status fp8blk_grouped_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw,
                                              const float* sw, const int32_t* offsets, int64_t E,
                                              int64_t total_M, int64_t N, int64_t K, uint16_t* y,
@@ -364,11 +397,6 @@ extern "C" fp8blk_status fp8blk_grouped_gemm(const uint8_t* qa, const float* sa,
   if (st != FP8BLK_OK || total_M == 0) return st;
   if (!offsets) return FP8BLK_ERR_INVALID_ARG;
   if (!aligned(offsets, 4)) return FP8BLK_ERR_ALIGNMENT;
-  const int64_t n_tiles = (N + Cfg::BN - 1) / Cfg::BN;
-  // upper bound on the number of M-tiles: sum_e ceil(M_e/BM) <= total_M/BM + E
-  const int64_t m_tiles = total_M / Cfg::BM + E;
-  if (n_tiles * m_tiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(grouped_gemm_kernel, dim3((uint32_t)(n_tiles * m_tiles)), dim3(Cfg::NT), 0, stream, qa, sa,
-                     qw, sw, offsets, (int)E, N, K, y, (int)n_tiles);
-  return launch_status();
+  if (total_M >= 128 * E) return launch_grouped<Mid>(qa, sa, qw, sw, offsets, E, total_M, N, K, y, stream);
+  return launch_grouped<Small>(qa, sa, qw, sw, offsets, E, total_M, N, K, y, stream);
 }

@@ -214,3 +214,15 @@ def test_power_of_two_extreme_exponents(fp8blk_lib):
         qw_r, sw_r = oracle.quant_weight_ref(w, pow2=True)
         assert_within_tolerance(fb.gemm(qa, sa, qw, sw).float().cpu().numpy(),
                                 oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r), what="pow2 shift %d" % shift)
+
+
+@pytest.mark.parametrize("m,k,n", [
+    (300, 256, 640),      # few tiles: 64x64 tiles
+    (2048, 256, 4096),    # 128x128 tiles
+    (2100, 384, 8320),    # 256x256 tiles, with an M tail and a half-width N tail
+])
+def test_each_tile_configuration(fp8blk_lib, m, k, n):
+    g = synth.generator(13, seed=m + n)
+    x = synth.activation(m, k, g, 0.005, 30.0)
+    w = synth.weight(n, k, g)
+    _layer_check(x, w)
