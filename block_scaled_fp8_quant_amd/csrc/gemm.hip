@@ -11,22 +11,28 @@
 // Kernel structure:
 //   * one workgroup computes a BM x BN output tile; its K loop steps one
 //     scale block (128) at a time, so the K tile IS the scale block;
-//   * A and B K-tiles (row-major, K contiguous) and the tile's row scales
-//     are staged through LDS, double buffered. The copies are direct
-//     global->LDS loads (global_load_lds_dwordx4 / _dword): they need no
-//     staging registers and run while the MFMAs of the previous block do;
+//   * A and B K-tiles (row-major, K contiguous) and the block's scales are
+//     staged through LDS, double buffered. The copies are direct
+//     global->LDS buffer loads (buffer_load_dwordx4 / _dword ... lds): no
+//     staging registers, and they run while the MFMAs of the previous block
+//     do. The buffer range check turns rows past the end of an operand into
+//     zeros, so partial tiles need no clamping;
 //   * LDS rows are 128 bytes; the 16-byte chunk c of row r sits at chunk
-//     c ^ (r & 7), so the 16 rows an MFMA operand read touches hit distinct
-//     banks. A direct load writes lane l's 16 bytes at slot l of a 1 KB
+//     c ^ key(r), so the 16 rows an MFMA operand read touches spread over
+//     the banks. A direct load writes lane l's 16 bytes at slot l of a 1 KB
 //     window, so the swizzle is applied on the global side: the lane that
-//     fills slot (row, p) fetches logical chunk p ^ (row & 7);
+//     fills slot (row, p) fetches logical chunk p ^ key(row);
 //   * each wave owns a WM x WN sub-tile of 16x16 tiles. One
 //     v_mfma_scale_f32_16x16x128_f8f6f4 (E4M3 x E4M3, unit block scales)
 //     gives the exact fp32 partial dot product of one whole scale block;
-//     a row of them is issued before the partials are folded into the fp32
-//     accumulators with one FMA each: acc += partial * (SA[m][b] * SW[n/128][b]);
-//     the MFMA produces the transposed tile so that each lane's quad is 4
+//     the partials are folded into the fp32 accumulators with one FMA each,
+//     acc += partial * (SA[m][b] * SW[n/128][b]), one 16-row m-subtile
+//     behind the MFMAs so that no fold waits for an MFMA just issued; the
+//     MFMA produces the transposed tile so that each lane's quad is 4
 //     consecutive outputs of one row (one activation scale per quad);
+//   * the K loop body is one basic block (no branches), so the compiler
+//     cannot sink the MFMAs behind the barrier; the last m-subtile's MFMAs
+//     of a block run while the next block's fragments are read;
 //   * the epilogue rounds to bf16 (nearest even) and stores 8 bytes a lane;
 //   * workgroups are handed out round-robin over the 8 XCDs; the tile order
 //     gives each XCD a contiguous band of tiles so neighbours share A rows
@@ -47,6 +53,8 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 constexpr int BK = kBlock;  // K step = one scale block
+// 32-bit lane offsets into a tile's rows: 256 * K must stay below 2^32
+constexpr int64_t kMaxK = int64_t(1) << 24;
 
 template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
 struct Tile {
@@ -58,11 +66,12 @@ struct Tile {
   // 1 KB direct-load windows (8 rows of 128 bytes) per wave per K step
   static constexpr int A_WIN = BM / 8 / WAVES, B_WIN = BN / 8 / WAVES;
   static_assert(A_WIN * 8 * WAVES == BM && B_WIN * 8 * WAVES == BN, "rows per wave");
-  static_assert(BM % 64 == 0 && BM / 64 <= WAVES, "row scales: one dword window per wave");
+  static_assert(BM % 64 == 0 && BM / 64 < WAVES, "row scales: one dword window per wave, one wave left for the weight scales");
   static_assert(kBlock % WN == 0, "a wave's columns lie in one weight block");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "16x16 MFMA tiles");
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
-  static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4;
+  // A tile, B tile, BM row scales, then a 256-byte window of weight scales
+  static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4 + 256;
   static constexpr int LDS = 2 * STAGE;  // double buffered
 };
 
@@ -103,32 +112,56 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
-__device__ __forceinline__ void dma16(const uint8_t* src, lds_u8* lds_window) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_window, 16, 0, 0);
+// Direct global->LDS loads through buffer resources. A resource covers the
+// tile's rows from its first row to the end of the operand (at most 4 GB);
+// the hardware range check returns zeros for rows past the end, so partial
+// tiles need no clamping. Lane offsets are 32-bit: BM * K < 2^32.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;  // raw (stride 0) dword-addressed resource
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
 }
-__device__ __forceinline__ void dma4(const uint8_t* src, lds_u8* lds_window) {
-  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds_window, 4, 0, 0);
+__device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, lds_u8* lds_window) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_window, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff, lds_u8* lds_window) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_window, 4, voff, soff, 0, 0);
 }
 
 // Per-lane constants of the direct loads. A load fills one 1 KB LDS window
 // (8 rows of 128 bytes); lane l writes slot l = (row l/8, physical chunk
-// l%8), so it fetches logical chunk (l%8) ^ key(row). Sources are a
-// wave-uniform base (advanced by 128 bytes per K step) plus a 32-bit lane
-// offset: row * K + chunk * 16 within the tile's rows.
+// l%8), so it fetches logical chunk (l%8) ^ key(row): byte offset
+// row * K + chunk * 16 within the tile's rows, plus 128 bytes per K step.
 template <class C>
 struct LoadPlan {
   uint32_t a_off[C::A_WIN], b_off[C::B_WIN], s_off;
+  const void *a, *b, *s;        // first byte of the tile's rows (scales: row or column block)
+  uint32_t a_len, b_len, s_len;  // bytes from there to the operand's end (clamped to 4 GB - 1)
 };
 
+__device__ __forceinline__ uint32_t clamp_len(int64_t bytes) {
+  return bytes < 0xFFFFFFFFll ? (uint32_t)bytes : 0xFFFFFFFFu;
+}
+
+// Direct loads of K block kb into `stage`; with live == false every
+// resource has length zero, so the loads fetch nothing. No branches: the
+// loop around this must stay one basic block. The first BM/64 waves load
+// the tile's activation scales (64 rows each); the others all load the
+// same BN/128 weight scales into the stage's last window.
 template <class C>
-__device__ __forceinline__ void issue_stage(lds_u8* stage, const uint8_t* a_base, const uint8_t* b_base,
-                                            const uint8_t* s_base, const LoadPlan<C>& lp, int wave) {
+__device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp, int kb, int wave, bool live) {
+  const uint32_t koff = (uint32_t)kb * BK;
+  const rsrc_t a = make_rsrc(lp.a, live ? lp.a_len : 0u);
+  const rsrc_t b = make_rsrc(lp.b, live ? lp.b_len : 0u);
+  const rsrc_t s = make_rsrc(lp.s, live ? lp.s_len : 0u);
 #pragma unroll
-  for (int i = 0; i < C::A_WIN; ++i) dma16(a_base + lp.a_off[i], stage + (wave * C::A_WIN + i) * 1024);
+  for (int i = 0; i < C::A_WIN; ++i) dma16(a, lp.a_off[i], koff, stage + (wave * C::A_WIN + i) * 1024);
 #pragma unroll
   for (int i = 0; i < C::B_WIN; ++i)
-    dma16(b_base + lp.b_off[i], stage + C::A_BYTES + (wave * C::B_WIN + i) * 1024);
-  if (wave < C::BM / 64) dma4(s_base + lp.s_off, stage + C::A_BYTES + C::B_BYTES + wave * 256);
+    dma16(b, lp.b_off[i], koff, stage + C::A_BYTES + (wave * C::B_WIN + i) * 1024);
+  const int window = wave < C::BM / 64 ? wave : C::BM / 64;
+  dma4(s, lp.s_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + window * 256);
 }
 
 // acc[j] += p[j] * sc for the TN accumulator quads of one m-subtile.
@@ -140,8 +173,19 @@ __device__ __forceinline__ void fold_row(v4f (&acc)[C::TN], const v4f (&p)[C::TN
     for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[j][r], sc, acc[j][r]);
 }
 
-// One BM x BN output tile at (m0, n0) of Y[M][N] = A[M][K] W[N][K]^T, with
-// rows >= M of A read as row M-1 (valid memory) and never stored. M >= 1.
+template <class C>
+__device__ __forceinline__ void mfma_row(v4f (&p)[C::TN], const v8i (&wfr)[C::TN], const v8i& afr) {
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+    p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], afr, zero, 0, 0, 0, 127, 0, 127);
+}
+
+// Compiler scheduling fence: nothing is moved across it.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// One BM x BN output tile at (m0, n0) of Y[M][N] = A[M][K] W[N][K]^T; rows
+// >= M of A and >= N of W read as zeros and are never stored. M >= 1.
 //
 // The MFMA computes the transposed tile: source 0 is a 16-row weight
 // fragment (n), source 1 a 16-row activation fragment (m), so lane l holds
@@ -155,76 +199,137 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
                                           const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                           int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
                                           int64_t m0, int64_t n0, uint8_t* smem_generic) {
+  static_assert(C::TM % 4 == 0, "activation fragments alternate between two registers; scales read 4 at a time");
   lds_u8* smem = (lds_u8*)smem_generic;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int wm = (wave / C::WAVES_N) * C::WM;
   const int wn = (wave % C::WAVES_N) * C::WN;
   const int g = lane >> 4, c16 = lane & 15;
-  const int64_t KB = K / BK;
+  const int KB = __builtin_amdgcn_readfirstlane((int)(K / BK));  // K <= 2^24
 
   LoadPlan<C> lp;
 #pragma unroll
   for (int i = 0; i < C::A_WIN; ++i) {
     const int row = (wave * C::A_WIN + i) * 8 + (lane >> 3);
-    const int64_t r = m0 + row < M ? row : M - 1 - m0;
-    lp.a_off[i] = (uint32_t)(r * K) + (((lane & 7) ^ swz_key(row)) << 4);
+    lp.a_off[i] = (uint32_t)row * (uint32_t)K + (((lane & 7) ^ swz_key(row)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < C::B_WIN; ++i) {
     const int row = (wave * C::B_WIN + i) * 8 + (lane >> 3);
-    const int64_t r = n0 + row < N ? row : N - 1 - n0;
-    lp.b_off[i] = (uint32_t)(r * K) + (((lane & 7) ^ swz_key(row)) << 4);
+    lp.b_off[i] = (uint32_t)row * (uint32_t)K + (((lane & 7) ^ swz_key(row)) << 4);
   }
-  {
-    const int64_t r = m0 + wave * 64 + lane < M ? wave * 64 + lane : M - 1 - m0;
-    lp.s_off = (uint32_t)(r * KB * 4);
+  lp.a = qa + m0 * K;
+  lp.b = qw + n0 * K;
+  lp.a_len = clamp_len((M - m0) * K);
+  lp.b_len = clamp_len((N - n0) * K);
+  if (wave < C::BM / 64) {
+    // Activation scales, permuted so that the TM scales one lane needs
+    // (rows wm + 16i + l%16, i < TM) are contiguous: slot t = h*WM + c*TM + i
+    // holds tile row h*WM + 16i + c.
+    const int t = wave * 64 + lane, h = t / C::WM, rem = t % C::WM;
+    const int row = h * C::WM + 16 * (rem % C::TM) + rem / C::TM;
+    lp.s = sa + m0 * KB;
+    lp.s_len = clamp_len((M - m0) * KB * 4);
+    lp.s_off = (uint32_t)row * (uint32_t)(KB * 4);
+  } else {  // weight scales of column blocks n0/128 + lane (lanes past the tile's blocks repeat)
+    constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;  // a 64-wide tile lies in one block
+    lp.s = sw + (n0 / kBlock) * KB;
+    lp.s_len = clamp_len((N / kBlock - n0 / kBlock) * KB * 4);
+    lp.s_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KB * 4);
   }
-  const uint8_t* a_base = qa + m0 * K;
-  const uint8_t* b_base = qw + n0 * K;
-  const uint8_t* s_base = reinterpret_cast<const uint8_t*>(sa + m0 * KB);
   // N % 128 == 0 and WN divides 128: a wave's columns are all in or all out
   const bool cols_valid = n0 + wn < N;
-  const float* sw_row = sw + (cols_valid ? (n0 + wn) / kBlock : N / kBlock - 1) * KB;
 
   v4f acc[C::TM][C::TN];
 #pragma unroll
   for (int i = 0; i < C::TM; ++i)
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
-  // Two LDS stages. Iteration kb: wait for this wave's loads of block kb;
-  // barrier (every wave's block-kb data has landed, and every wave is done
-  // reading block kb-1, so its stage is free); refill that stage with block
-  // kb+1; compute block kb.
-  issue_stage<C>(smem, a_base, b_base, s_base, lp, wave);
-  for (int64_t kb = 0; kb < KB; ++kb) {
-    const int st = (int)(kb & 1);
-    wait_vmcnt<0>();
-    lds_barrier();
-    if (kb + 1 < KB)
-      issue_stage<C>(smem + (st ^ 1) * C::STAGE, a_base + (kb + 1) * BK, b_base + (kb + 1) * BK,
-                     s_base + (kb + 1) * 4, lp, wave);
+  // Two LDS stages, each holding a K block of both operands and its scales.
+  // Step kb: rows 0..TM-2, each reading the next row's activation fragment
+  // ahead and folding the previous row's partials while its own MFMAs run;
+  // then wait for this wave's loads of block kb+1 and barrier (every wave
+  // has read all of block kb, block kb+1 is in LDS); refill block kb's stage
+  // with block kb+2; issue the last row's MFMAs and read block kb+1's first
+  // fragments while they run. The last row is folded during the next step.
+  // The loop body is branch-free: past the last block the refill uses
+  // resources of length zero (out-of-range loads fetch nothing) and the
+  // fragments read ahead are not used.
+  issue_stage<C>(smem, lp, 0, wave, true);
+  wait_vmcnt<0>();
+  lds_barrier();
+  issue_stage<C>(smem + C::STAGE, lp, 1, wave, KB > 1);
+  // Step kb, one basic block: (1) the previous step's last-row MFMAs, then
+  // this stage's weight fragments, first activation fragment and scales are
+  // read while they run; (2) rows 0..TM-2, each reading the next row's
+  // activation fragment and folding the previous row's partials while its
+  // own MFMAs run; (3) wait for this wave's loads of block kb+1 and barrier
+  // (every wave has read all of block kb, and block kb+1 is in LDS), then
+  // refill block kb's stage with block kb+2. Folds trail their MFMAs by one
+  // row, so no fold waits for an MFMA just issued.
+  v8i wfr[C::TN], afr[2];
+  v4f srow[C::TM / 4];
+  float swv = 0.f;
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) wfr[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  afr[0] = afr[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  v4f pp[C::TN];  // partials of the previous row, not yet folded
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) pp[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  float sc_prev = 0.f, sc_last = 0.f;
 
+  for (int kb = 0; kb < KB; ++kb) {
+    const int st = kb & 1;
     const uint8_t* sA = smem_generic + st * C::STAGE;
-    const uint8_t* sB = sA + C::A_BYTES;
-    const float* sSA = reinterpret_cast<const float*>(sB + C::B_BYTES);
-    const float swv = sw_row[kb];
-    v8i wfr[C::TN];
-#pragma unroll
-    for (int j = 0; j < C::TN; ++j) wfr[j] = read_frag(sB, wn + 16 * j + c16, g);
-#pragma unroll
-    for (int i = 0; i < C::TM; ++i) {
-      const v8i afr = read_frag(sA, wm + 16 * i + c16, g);
-      const float sc = sSA[wm + 16 * i + c16] * swv;
+    {  // (1); on the first step the operands are zero
       v4f p[C::TN];
+      mfma_row<C>(p, wfr, afr[(C::TM - 1) & 1]);
+      sched_fence();
 #pragma unroll
-      for (int j = 0; j < C::TN; ++j)
-        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], afr, zero, 0, 0, 0, 127, 0, 127);
-      fold_row<C>(acc[i], p, sc);
+      for (int j = 0; j < C::TN; ++j) wfr[j] = read_frag(sA + C::A_BYTES, wn + 16 * j + c16, g);
+      afr[0] = read_frag(sA, wm + c16, g);
+      const float* sc = reinterpret_cast<const float*>(sA + C::A_BYTES + C::B_BYTES);
+#pragma unroll
+      for (int q = 0; q < C::TM / 4; ++q) srow[q] = *reinterpret_cast<const v4f*>(sc + wm + c16 * C::TM + 4 * q);
+      swv = sc[C::BM + wn / kBlock];
+      fold_row<C>(acc[C::TM - 2], pp, sc_prev);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
+      sc_prev = sc_last;
+      sched_fence();
     }
+#pragma unroll
+    for (int i = 0; i < C::TM - 1; ++i) {  // (2)
+      afr[(i + 1) & 1] = read_frag(sA, wm + 16 * (i + 1) + c16, g);
+      v4f p[C::TN];
+      mfma_row<C>(p, wfr, afr[i & 1]);
+      fold_row<C>(acc[i == 0 ? C::TM - 1 : i - 1], pp, sc_prev);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
+      sc_prev = srow[i / 4][i % 4] * swv;
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next fragment reads
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four fold FMAs
+      }
+      sched_fence();
+    }
+    sc_last = srow[(C::TM - 1) / 4][(C::TM - 1) % 4] * swv;
+    wait_vmcnt<0>();  // (3)
+    lds_barrier();
+    issue_stage<C>(smem + st * C::STAGE, lp, kb + 2, wave, kb + 2 < KB);
+    sched_fence();
   }
+  {
+    v4f p[C::TN];
+    mfma_row<C>(p, wfr, afr[(C::TM - 1) & 1]);
+    fold_row<C>(acc[C::TM - 2], pp, sc_prev);
+    fold_row<C>(acc[C::TM - 1], p, sc_last);
+  }
+  wait_vmcnt<0>();  // no load may still be writing LDS when the workgroup ends
 
   if (!cols_valid) return;
   // lane holds Y[m0 + wm + 16i + l%16][n0 + wn + 16j + 4*(l/16) + r], r < 4
@@ -324,7 +429,7 @@ __global__ __launch_bounds__(Cfg::NT) void grouped_gemm_kernel(const uint8_t* __
 fp8blk_status check_gemm_args(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                               int64_t M, int64_t N, int64_t K, const uint16_t* y) {
   if (M < 0 || N <= 0 || K <= 0) return FP8BLK_ERR_INVALID_ARG;
-  if (N % kBlock || K % kBlock) return FP8BLK_ERR_SHAPE;
+  if (N % kBlock || K % kBlock || K > kMaxK) return FP8BLK_ERR_SHAPE;
   if (M == 0) return FP8BLK_OK;
   if (!qa || !sa || !qw || !sw || !y) return FP8BLK_ERR_INVALID_ARG;
   if (!aligned(qa, 16) || !aligned(qw, 16) || !aligned(y, 16) || !aligned(sa, 4) || !aligned(sw, 4))

@@ -52,7 +52,7 @@ extern "C" {
 typedef enum {
   FP8BLK_OK = 0,
   FP8BLK_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad flag */
-  FP8BLK_ERR_SHAPE = 2,       /* K or N not a multiple of 128, E < 1 */
+  FP8BLK_ERR_SHAPE = 2,       /* K or N not a multiple of 128, GEMM K > 2^24, E < 1 */
   FP8BLK_ERR_ALIGNMENT = 3,   /* data pointer not 16-byte aligned, scales not 4-byte */
   FP8BLK_ERR_HIP = 4          /* a kernel launch failed */
 } fp8blk_status;
@@ -91,7 +91,8 @@ fp8blk_status fp8blk_quant_weight(const uint16_t* w, int64_t N, int64_t K,
  *   qa [M][K] codes, sa [M][K/128]  -- as written by fp8blk_quant_act
  *   qw [N][K] codes, sw [N/128][K/128] -- as written by fp8blk_quant_weight
  *   y  [M][N] bf16 out (16-byte aligned)
- *   M >= 0 (M == 0: no-op), N > 0, K > 0, N % 128 == 0, K % 128 == 0.
+ *   M >= 0 (M == 0: no-op), N > 0, K > 0, N % 128 == 0, K % 128 == 0,
+ *   K <= 2^24 (the kernels address a 256-row tile with 32-bit offsets).
  */
 fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa,
                           const uint8_t* qw, const float* sw,
@@ -109,7 +110,8 @@ fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa,
  *            offsets[E] = total_M (not checked; read on the device only, so
  *            the call needs no host synchronisation); empty experts allowed
  *   y  [total_M][N] bf16 out
- *   E >= 1, total_M >= 0 (0: no-op), N, K > 0, N % 128 == 0, K % 128 == 0.
+ *   E >= 1, total_M >= 0 (0: no-op), N, K > 0, N % 128 == 0, K % 128 == 0,
+ *   K <= 2^24.
  */
 fp8blk_status fp8blk_grouped_gemm(const uint8_t* qa, const float* sa,
                                   const uint8_t* qw, const float* sw,

@@ -86,6 +86,7 @@ def test_gemm_validation(lib):
     assert f(P, P, P, P, 4, 128, 0, P, NULL) == INVALID
     assert f(P, P, P, P, 4, 130, 128, P, NULL) == SHAPE
     assert f(P, P, P, P, 4, 128, 130, P, NULL) == SHAPE
+    assert f(P, P, P, P, 4, 128, (1 << 24) + 128, P, NULL) == SHAPE    # 32-bit tile offsets
     for i in range(5):
         args = [P, P, P, P]
         ptrs = args + [P]
@@ -103,6 +104,7 @@ def test_grouped_gemm_validation(lib):
     assert f(P, P, P, P, P, 0, 4, 128, 128, P, NULL) == SHAPE          # E < 1
     assert f(P, P, P, P, P, 2, -1, 128, 128, P, NULL) == INVALID
     assert f(P, P, P, P, P, 2, 4, 100, 128, P, NULL) == SHAPE
+    assert f(P, P, P, P, P, 2, 4, 128, (1 << 24) + 128, P, NULL) == SHAPE
     assert f(P, P, P, P, NULL, 2, 4, 128, 128, P, NULL) == INVALID      # offsets
     assert f(P, P, P, P, P + 2, 2, 4, 128, 128, P, NULL) == ALIGN
     assert f(P, P, P4, P, P, 2, 4, 128, 128, P, NULL) == ALIGN
