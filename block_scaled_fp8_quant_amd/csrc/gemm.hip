@@ -56,9 +56,9 @@ constexpr int BK = kBlock;  // K step = one scale block
 // 32-bit lane offsets into a tile's rows: 256 * K must stay below 2^32
 constexpr int64_t kMaxK = int64_t(1) << 24;
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 2>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -72,18 +72,31 @@ struct Tile {
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
   // A tile, B tile, BM row scales, then a 256-byte window of weight scales
   static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4 + 256;
-  static constexpr int LDS = 2 * STAGE;  // double buffered
+  static constexpr int LDS = STAGES * STAGE;
+  // direct loads one wave issues per stage: its A and B windows and one scale window
+  static constexpr int LOADS_PER_STAGE = A_WIN + B_WIN + 1;
+  static_assert(STAGES == 2 || STAGES == 4 || STAGES == 8, "stage index is kb mod STAGES");
+  static_assert(LOADS_PER_STAGE * (STAGES - 1) <= 63, "outstanding loads fit the vmcnt counter");
 };
 
 // Tile configurations, picked per call from the problem shape (host side):
-//   Big   256x256, 8 waves of 128x64: large M and N (one workgroup per CU);
-//   Mid   128x128, 4 waves of 64x64: medium problems, expert groups of ~100+ rows;
-//   Small  64x64,  4 waves of 64x16: few rows (decode steps, small experts),
-//          enough workgroups to occupy every CU.
+//   Big   256x256, 8 waves of 128x64, 2 stages: large M and N (one workgroup
+//         per CU);
+//   Mid   128x128, 4 waves of 64x64, 2 stages: medium problems, expert groups
+//         of ~100+ rows (two workgroups per CU);
+//   Small  64x64,  4 waves of 64x16, 4 stages: few rows (decode steps, small
+//         experts); a step holds little MFMA work, so three blocks stay in
+//         flight to cover the load latency (two workgroups per CU).
+#ifndef FP8BLK_MID_STAGES
+#define FP8BLK_MID_STAGES 2
+#endif
+#ifndef FP8BLK_SMALL_STAGES
+#define FP8BLK_SMALL_STAGES 4
+#endif
 using Big = Tile<256, 256, 2, 4>;
-using Mid = Tile<128, 128, 2, 2>;
-using Small = Tile<64, 64, 1, 4>;
-static_assert(Big::LDS <= 160 * 1024 && Mid::LDS <= 80 * 1024 && Small::LDS <= 40 * 1024, "LDS budget");
+using Mid = Tile<128, 128, 2, 2, FP8BLK_MID_STAGES>;
+using Small = Tile<64, 64, 1, 4, FP8BLK_SMALL_STAGES>;
+static_assert(Big::LDS <= 160 * 1024 && Mid::LDS <= 160 * 1024 && Small::LDS <= 160 * 1024, "LDS budget");
 
 // 16-byte chunk c of LDS row r is stored at chunk c ^ key(r), so the 16
 // rows that one operand read touches (same logical chunk) are spread over
@@ -128,6 +141,16 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ void wait_vm0() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until at most N of this wave's global loads are outstanding (loads
+// complete in order, so the older ones have landed). N <= 63.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N <= 63, "vmcnt field");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
@@ -266,28 +289,24 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
 #pragma unroll
     for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // Two LDS stages, each holding a K block of both operands and its scales.
-  // Step kb: rows 0..TM-2, each reading the next row's activation fragment
-  // ahead and folding the previous row's partials while its own MFMAs run;
-  // then wait for this wave's loads of block kb+1 and barrier (every wave
-  // has read all of block kb, block kb+1 is in LDS); refill block kb's stage
-  // with block kb+2; issue the last row's MFMAs and read block kb+1's first
-  // fragments while they run. The last row is folded during the next step.
-  // The loop body is branch-free: past the last block the refill uses
-  // resources of length zero (out-of-range loads fetch nothing) and the
-  // fragments read ahead are not used.
-  issue_stage<C>(smem, lp, 0, wave, true);
-  wait_vm0();
+  // STAGES LDS stages, each holding a K block of both operands and its
+  // scales; block kb lives in stage kb % STAGES and STAGES-1 blocks are in
+  // flight while one is computed. The loop body is branch-free: past the
+  // last block the refill uses resources of length zero (out-of-range loads
+  // fetch nothing) and the fragments read ahead are not used.
+  constexpr int S = C::STAGES, LPS = C::LOADS_PER_STAGE;
+#pragma unroll
+  for (int b = 0; b < S; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
+  wait_vm<LPS * (S - 1)>();  // block 0 has landed
   lds_barrier();
-  issue_stage<C>(smem + C::STAGE, lp, 1, wave, KB > 1);
   // Step kb, one basic block: (1) the previous step's last-row MFMAs, then
   // this stage's weight fragments, first activation fragment and scales are
   // read while they run; (2) rows 0..TM-2, each reading the next row's
   // activation fragment and folding the previous row's partials while its
   // own MFMAs run; (3) wait for this wave's loads of block kb+1 and barrier
   // (every wave has read all of block kb, and block kb+1 is in LDS), then
-  // refill block kb's stage with block kb+2. Folds trail their MFMAs by one
-  // row, so no fold waits for an MFMA just issued.
+  // refill block kb's stage with block kb+STAGES. Folds trail their MFMAs by
+  // one row, so no fold waits for an MFMA just issued.
   v8i wfr[C::TN], afr[2];
   v4f srow[C::TM / 4];
   float swv = 0.f;
@@ -300,7 +319,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
   float sc_prev = 0.f, sc_last = 0.f;
 
   for (int kb = 0; kb < KB; ++kb) {
-    const int st = kb & 1;
+    const int st = kb & (S - 1);
     const uint8_t* sA = smem_generic + st * C::STAGE;
     {  // (1); on the first step the operands are zero
       v4f p[C::TN];
@@ -337,9 +356,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
       sched_fence();
     }
     sc_last = srow[(C::TM - 1) / 4][(C::TM - 1) % 4] * swv;
-    wait_vm0();  // (3)
+    wait_vm<LPS * (S - 2)>();  // (3) block kb+1 has landed
     lds_barrier();
-    issue_stage<C>(smem + st * C::STAGE, lp, kb + 2, wave, kb + 2 < KB);
+    issue_stage<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
     sched_fence();
   }
   {
