@@ -322,20 +322,33 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     const int st = kb & (S - 1);
     const uint8_t* sA = smem_generic + st * C::STAGE;
     {  // (1); on the first step the operands are zero
+      // The last row's MFMA j is the last use of weight fragment j, so the
+      // next block's fragment j is read into it right after: the reads spread
+      // over the tail MFMAs, and row 0 can start once its first fragments land.
       v4f p[C::TN];
-      mfma_row<C>(p, wfr, afr[(C::TM - 1) & 1]);
-      sched_fence();
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) wfr[j] = read_frag(sA + C::A_BYTES, wn + 16 * j + c16, g);
       afr[0] = read_frag(sA, wm + c16, g);
       const float* sc = reinterpret_cast<const float*>(sA + C::A_BYTES + C::B_BYTES);
 #pragma unroll
       for (int q = 0; q < C::TM / 4; ++q) srow[q] = *reinterpret_cast<const v4f*>(sc + wm + c16 * C::TM + 4 * q);
       swv = sc[C::BM + wn / kBlock];
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], afr[(C::TM - 1) & 1], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                0, 0, 0, 127, 0, 127);
+        wfr[j] = read_frag(sA + C::A_BYTES, wn + 16 * j + c16, g);
+      }
       fold_row<C>(acc[C::TM - 2], pp, sc_prev);
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
       sc_prev = sc_last;
+      // first activation fragment and the scales (TM / 4 + 3 reads)
+      if (C::TM == 8) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+      if (C::TM == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // tail MFMA j
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next block's weight fragment j
+      }
       sched_fence();
     }
 #pragma unroll
