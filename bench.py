@@ -180,6 +180,24 @@ def cpu_baseline(workload, rows, wrows):
 COPY_BYTES = 1 << 30
 
 
+def roofline(flops, alg_bytes, avg_ms, traffic):
+    """The GEMM's roofline entry: MFMA-bound when its arithmetic intensity
+    (flops per algorithmic byte) is above the FP8 ridge (peak flops / peak
+    HBM bandwidth, 625 flop/B), else HBM-bound (achieved = algorithmic bytes
+    per launch / average launch time)."""
+    ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    intensity = flops / alg_bytes
+    sec = avg_ms * 1e-3
+    if intensity >= ridge:
+        bound, achieved, peak, unit = "mfma", flops / sec / 1e12, FP8_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", alg_bytes / sec / 1e9, HBM_PEAK_GBS, "GB/s"
+    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": None if traffic is None else round(traffic),
+            "algorithmic_bytes_per_launch": round(alg_bytes), "flops_per_launch": flops,
+            "intensity_flop_per_byte": round(intensity, 1), "avg_launch_ms": round(avg_ms, 4)}
+
+
 def copy_yardstick():
     """A plain 1 GiB device-to-device copy: the counters' calibration."""
     import torch
@@ -321,15 +339,9 @@ def main():
                    "step": "quant_weight x%d + quant_act x%d + %s x%d" % (
                        len(layers), len(layers), "grouped_gemm" if layers[0]["e"] else "gemm", len(layers))},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None if traffic is None else round(traffic),
-                     "algorithmic_bytes_per_launch": round(gemm_alg_bytes),
-                     "flops_per_launch": gemm_flops_launch, "avg_launch_ms": round(gemm_avg_ms, 4)},
+        "roofline": roofline(gemm_flops_launch, gemm_alg_bytes, gemm_avg_ms, traffic),
         "breakdown": breakdown,
     }
-    if args.workload in ("llama8b_decode", "moe"):
-        out["roofline"]["note"] = "below the FP8 ridge: HBM-bound shapes"
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows)
