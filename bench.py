@@ -49,8 +49,8 @@ def parse():
     p.add_argument("--workload", default="llama8b_prefill",
                    choices=["llama8b_prefill", "llama8b_decode", "qwen8b_pow2", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-rows", type=int, default=4096)
-    p.add_argument("--cpu-sample-wrows", type=int, default=1024)
+    p.add_argument("--cpu-sample-rows", type=int, default=8192)
+    p.add_argument("--cpu-sample-wrows", type=int, default=1536)
     p.add_argument("--copy-yardstick", action="store_true",
                    help="after timing, run a 1 GiB device copy (counter calibration)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),

@@ -72,7 +72,7 @@ struct Tile {
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
   // A tile, B tile, BM row scales, then a 256-byte window of weight scales
   static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4 + 256;
-  static constexpr int LDS = STAGES * STAGE;
+  static constexpr int LDS = STAGES * STAGE + 4 * WAVES;  // stages, then one scale verdict per wave
   // direct loads one wave issues per stage: its A and B windows and one scale window
   static constexpr int LOADS_PER_STAGE = A_WIN + B_WIN + 1;
   static_assert(STAGES == 2 || STAGES == 4 || STAGES == 8, "stage index is kb mod STAGES");
@@ -226,6 +226,210 @@ __device__ __forceinline__ void mfma_row(v4f (&p)[C::TN], const v8i (&wfr)[C::TN
 // Compiler scheduling fence: nothing is moved across it.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
+// A scale the MFMA can apply itself: 0 (an all-zero group or block, whose
+// codes are all zero) or an exact power of two 2^-126 .. 2^127 (positive,
+// zero mantissa, normal exponent). Its E8M0 code is then the fp32 exponent
+// field.
+__device__ __forceinline__ bool e8m0_exact(uint32_t b) {  // bitwise, no branches
+  const uint32_t e = (b >> 23) & 0xFFu;
+  return (b == 0u) | (((b & 0x807FFFFFu) == 0u) & (e != 0u) & (e != 0xFFu));
+}
+__device__ __forceinline__ uint32_t e8m0_of(float s) { return (__float_as_uint(s) >> 23) & 0xFFu; }
+
+__device__ __forceinline__ bool v4_e8m0_exact(v4i v) {
+  return e8m0_exact((uint32_t)v[0]) & e8m0_exact((uint32_t)v[1]) & e8m0_exact((uint32_t)v[2]) &
+         e8m0_exact((uint32_t)v[3]);
+}
+__device__ __forceinline__ bool wave_all(bool ok) { return __builtin_amdgcn_ballot_w64(!ok) == 0; }
+
+// Whether every scale of a tile is e8m0_exact, decided once per workgroup:
+// wave w checks BM/WAVES of the tile's activation-scale rows (each row's KB
+// scales are contiguous, so a wave's share is one run of floats; rows past
+// M read as zero) and the last wave also the weight scales of the tile's
+// column blocks. The first 8 KB of each share is loaded before the tile's
+// first direct loads, so waiting for it leaves those in flight; the rest
+// (K > 8192) is read after. Each wave's verdict goes to LDS and is read by
+// all after the barrier that follows the first direct loads.
+template <class C>
+struct ScaleScan {
+  static constexpr int ROWS = C::BM / C::WAVES;  // activation-scale rows per wave
+  static constexpr int FIRST = 8;                // 1 KB loads per wave issued early
+  rsrc_t a, w;
+  uint32_t a_bytes, w_bytes;
+  v4i a0[FIRST], w0;
+};
+
+template <class C>
+__device__ __forceinline__ void scan_begin(ScaleScan<C>& sc, const float* sa, const float* sw, int64_t M, int64_t N,
+                                           int64_t m0, int64_t n0, int wave, int KB, int lane) {
+  using S = ScaleScan<C>;
+  const int64_t r0 = m0 + (int64_t)wave * S::ROWS;
+  const int64_t rows = M - r0;
+  const int64_t a_rows = rows <= 0 ? 0 : (rows < S::ROWS ? rows : S::ROWS);
+  sc.a_bytes = (uint32_t)S::ROWS * (uint32_t)KB * 4u;
+  sc.a = make_rsrc(sa + r0 * KB, clamp_len(a_rows * KB * 4));
+  // last wave: the tile's weight-scale blocks n0/128 .. (n0+BN-1)/128 that exist
+  constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;
+  const int64_t blocks = N / kBlock - n0 / kBlock;
+  const int64_t w_blocks = blocks < kColBlocks ? blocks : kColBlocks;
+  sc.w_bytes = wave == C::WAVES - 1 ? (uint32_t)(w_blocks * KB * 4) : 0u;
+  sc.w = make_rsrc(sw + (n0 / kBlock) * KB, sc.w_bytes);
+#pragma unroll
+  for (int u = 0; u < S::FIRST; ++u)
+    sc.a0[u] = __builtin_amdgcn_raw_buffer_load_b128(sc.a, (uint32_t)u * 1024u + (uint32_t)lane * 16u, 0, 0);
+  sc.w0 = __builtin_amdgcn_raw_buffer_load_b128(sc.w, (uint32_t)lane * 16u, 0, 0);
+}
+
+// This wave's verdict (wave-uniform). Loads past a resource's end read as
+// zero, which passes, so no load is conditional.
+template <class C>
+__device__ __forceinline__ bool scan_end(const ScaleScan<C>& sc, int lane) {
+  using S = ScaleScan<C>;
+  bool ok = v4_e8m0_exact(sc.w0);
+#pragma unroll
+  for (int u = 0; u < S::FIRST; ++u) ok = ok & v4_e8m0_exact(sc.a0[u]);
+  for (uint32_t off = S::FIRST * 1024u; off < sc.a_bytes; off += 8192u) {
+    v4i v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(sc.a, off + (uint32_t)u * 1024u + (uint32_t)lane * 16u, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ok = ok & v4_e8m0_exact(v[u]);
+  }
+  for (uint32_t off = 1024u; off < sc.w_bytes; off += 4096u) {
+    v4i v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      v[u] = __builtin_amdgcn_raw_buffer_load_b128(sc.w, off + (uint32_t)u * 1024u + (uint32_t)lane * 16u, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) ok = ok & v4_e8m0_exact(v[u]);
+  }
+  return wave_all(ok);
+}
+
+// The K loop of one wave, entered after the barrier that follows block 0's
+// arrival (every wave of the workgroup runs the same variant). POW2 == false: each block's 16x16 partials come from
+// unit-scale MFMAs and are folded into the fp32 accumulators with one FMA,
+// acc += partial * (SA * SW). POW2 == true (every scale of the wave is 0 or
+// a power of two): the MFMA applies SW and SA itself as E8M0 block scales
+// (source 0 = weights: the wave's SW; source 1 = activations: the lane's
+// row's SA) and accumulates into acc directly, with no fold.
+template <class C, bool POW2>
+__device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, const LoadPlan<C>& lp, int wave, int KB,
+                                       int wm, int wn, int g, int c16, v4f (&acc)[C::TM][C::TN]) {
+  constexpr int S = C::STAGES, LPS = C::LOADS_PER_STAGE;
+  // Step kb, one basic block: (1) the previous step's last-row MFMAs, then
+  // this stage's weight fragments, first activation fragment and scales are
+  // read while they run; (2) rows 0..TM-2, each reading the next row's
+  // activation fragment and folding the previous row's partials while its
+  // own MFMAs run; (3) wait for this wave's loads of block kb+1 and barrier
+  // (every wave has read all of block kb, and block kb+1 is in LDS), then
+  // refill block kb's stage with block kb+STAGES. Folds trail their MFMAs by
+  // one row, so no fold waits for an MFMA just issued.
+  v8i wfr[C::TN], afr[2];
+  v4f srow[C::TM / 4];
+  float swv = 0.f;
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) wfr[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  afr[0] = afr[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  v4f pp[C::TN];  // partials of the previous row, not yet folded
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j) pp[j] = v4f{0.f, 0.f, 0.f, 0.f};
+  float sc_prev = 0.f, sc_last = 0.f;
+  uint32_t ew = 0, ea_last = 0;  // E8M0 scales (POW2)
+  const v4f zero = {0.f, 0.f, 0.f, 0.f};
+
+  for (int kb = 0; kb < KB; ++kb) {
+    const int st = kb & (S - 1);
+    const uint8_t* sA = smem_generic + st * C::STAGE;
+    {  // (1); on the first step the operands are zero
+      // The last row's MFMA j is the last use of weight fragment j, so the
+      // next block's fragment j is read into it right after: the reads spread
+      // over the tail MFMAs, and row 0 can start once its first fragments land.
+      v4f p[C::TN];
+      afr[0] = read_frag(sA, wm + c16, g);
+      const float* sc = reinterpret_cast<const float*>(sA + C::A_BYTES + C::B_BYTES);
+#pragma unroll
+      for (int q = 0; q < C::TM / 4; ++q) srow[q] = *reinterpret_cast<const v4f*>(sc + wm + c16 * C::TM + 4 * q);
+      const float swv_new = sc[C::BM + wn / kBlock];
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        if constexpr (POW2)
+          acc[C::TM - 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wfr[j], afr[(C::TM - 1) & 1], acc[C::TM - 1][j], 0, 0, 0, (int)ew, 0, (int)ea_last);
+        else
+          p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], afr[(C::TM - 1) & 1], zero, 0, 0, 0, 127,
+                                                                  0, 127);
+        wfr[j] = read_frag(sA + C::A_BYTES, wn + 16 * j + c16, g);
+      }
+      if constexpr (!POW2) {
+        fold_row<C>(acc[C::TM - 2], pp, sc_prev);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
+        sc_prev = sc_last;
+      }
+      swv = swv_new;
+      ew = e8m0_of(swv);
+      // first activation fragment and the scales (TM / 4 + 3 reads)
+      if (C::TM == 8) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
+      if (C::TM == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // tail MFMA j
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next block's weight fragment j
+      }
+      sched_fence();
+    }
+#pragma unroll
+    for (int i = 0; i < C::TM - 1; ++i) {  // (2)
+      afr[(i + 1) & 1] = read_frag(sA, wm + 16 * (i + 1) + c16, g);
+      if constexpr (POW2) {
+        const uint32_t ea = e8m0_of(srow[i / 4][i % 4]);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], afr[i & 1], acc[i][j], 0, 0, 0, (int)ew,
+                                                                       0, (int)ea);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next fragment reads
+      } else {
+        v4f p[C::TN];
+        mfma_row<C>(p, wfr, afr[i & 1]);
+        fold_row<C>(acc[i == 0 ? C::TM - 1 : i - 1], pp, sc_prev);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
+        sc_prev = srow[i / 4][i % 4] * swv;
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next fragment reads
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four fold FMAs
+        }
+      }
+      sched_fence();
+    }
+    if constexpr (POW2)
+      ea_last = e8m0_of(srow[(C::TM - 1) / 4][(C::TM - 1) % 4]);
+    else
+      sc_last = srow[(C::TM - 1) / 4][(C::TM - 1) % 4] * swv;
+    wait_vm<LPS * (S - 2)>();  // (3) block kb+1 has landed
+    lds_barrier();
+    issue_stage<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
+    sched_fence();
+  }
+  if constexpr (POW2) {
+#pragma unroll
+    for (int j = 0; j < C::TN; ++j)
+      acc[C::TM - 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], afr[(C::TM - 1) & 1],
+                                                                           acc[C::TM - 1][j], 0, 0, 0, (int)ew, 0,
+                                                                           (int)ea_last);
+  } else {
+    v4f p[C::TN];
+    mfma_row<C>(p, wfr, afr[(C::TM - 1) & 1]);
+    fold_row<C>(acc[C::TM - 2], pp, sc_prev);
+    fold_row<C>(acc[C::TM - 1], p, sc_last);
+  }
+  wait_vm0();  // no load may still be writing LDS when the workgroup ends
+}
+
 // One BM x BN output tile at (m0, n0) of Y[M][N] = A[M][K] W[N][K]^T; rows
 // >= M of A and >= N of W read as zeros and are never stored. M >= 1.
 //
@@ -294,93 +498,22 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
   // flight while one is computed. The loop body is branch-free: past the
   // last block the refill uses resources of length zero (out-of-range loads
   // fetch nothing) and the fragments read ahead are not used.
-  constexpr int S = C::STAGES, LPS = C::LOADS_PER_STAGE;
+  ScaleScan<C> scan;
+  scan_begin<C>(scan, sa, sw, M, N, m0, n0, wave, KB, lane);
 #pragma unroll
-  for (int b = 0; b < S; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
-  wait_vm<LPS * (S - 1)>();  // block 0 has landed
+  for (int b = 0; b < C::STAGES; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
+  uint32_t* verdict = reinterpret_cast<uint32_t*>(smem_generic + C::STAGES * C::STAGE);
+  const bool ok = scan_end<C>(scan, lane);
+  if (lane == 0) verdict[wave] = ok ? 1u : 0u;
+  wait_vm<C::LOADS_PER_STAGE * (C::STAGES - 1)>();  // block 0 has landed (the scan's later loads too)
   lds_barrier();
-  // Step kb, one basic block: (1) the previous step's last-row MFMAs, then
-  // this stage's weight fragments, first activation fragment and scales are
-  // read while they run; (2) rows 0..TM-2, each reading the next row's
-  // activation fragment and folding the previous row's partials while its
-  // own MFMAs run; (3) wait for this wave's loads of block kb+1 and barrier
-  // (every wave has read all of block kb, and block kb+1 is in LDS), then
-  // refill block kb's stage with block kb+STAGES. Folds trail their MFMAs by
-  // one row, so no fold waits for an MFMA just issued.
-  v8i wfr[C::TN], afr[2];
-  v4f srow[C::TM / 4];
-  float swv = 0.f;
+  bool pow2 = true;
 #pragma unroll
-  for (int j = 0; j < C::TN; ++j) wfr[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  afr[0] = afr[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-  v4f pp[C::TN];  // partials of the previous row, not yet folded
-#pragma unroll
-  for (int j = 0; j < C::TN; ++j) pp[j] = v4f{0.f, 0.f, 0.f, 0.f};
-  float sc_prev = 0.f, sc_last = 0.f;
-
-  for (int kb = 0; kb < KB; ++kb) {
-    const int st = kb & (S - 1);
-    const uint8_t* sA = smem_generic + st * C::STAGE;
-    {  // (1); on the first step the operands are zero
-      // The last row's MFMA j is the last use of weight fragment j, so the
-      // next block's fragment j is read into it right after: the reads spread
-      // over the tail MFMAs, and row 0 can start once its first fragments land.
-      v4f p[C::TN];
-      afr[0] = read_frag(sA, wm + c16, g);
-      const float* sc = reinterpret_cast<const float*>(sA + C::A_BYTES + C::B_BYTES);
-#pragma unroll
-      for (int q = 0; q < C::TM / 4; ++q) srow[q] = *reinterpret_cast<const v4f*>(sc + wm + c16 * C::TM + 4 * q);
-      swv = sc[C::BM + wn / kBlock];
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        p[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wfr[j], afr[(C::TM - 1) & 1], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                0, 0, 0, 127, 0, 127);
-        wfr[j] = read_frag(sA + C::A_BYTES, wn + 16 * j + c16, g);
-      }
-      fold_row<C>(acc[C::TM - 2], pp, sc_prev);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
-      sc_prev = sc_last;
-      // first activation fragment and the scales (TM / 4 + 3 reads)
-      if (C::TM == 8) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-      if (C::TM == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // tail MFMA j
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next block's weight fragment j
-      }
-      sched_fence();
-    }
-#pragma unroll
-    for (int i = 0; i < C::TM - 1; ++i) {  // (2)
-      afr[(i + 1) & 1] = read_frag(sA, wm + 16 * (i + 1) + c16, g);
-      v4f p[C::TN];
-      mfma_row<C>(p, wfr, afr[i & 1]);
-      fold_row<C>(acc[i == 0 ? C::TM - 1 : i - 1], pp, sc_prev);
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
-      sc_prev = srow[i / 4][i % 4] * swv;
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next fragment reads
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four fold FMAs
-      }
-      sched_fence();
-    }
-    sc_last = srow[(C::TM - 1) / 4][(C::TM - 1) % 4] * swv;
-    wait_vm<LPS * (S - 2)>();  // (3) block kb+1 has landed
-    lds_barrier();
-    issue_stage<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
-    sched_fence();
-  }
-  {
-    v4f p[C::TN];
-    mfma_row<C>(p, wfr, afr[(C::TM - 1) & 1]);
-    fold_row<C>(acc[C::TM - 2], pp, sc_prev);
-    fold_row<C>(acc[C::TM - 1], p, sc_last);
-  }
-  wait_vm0();  // no load may still be writing LDS when the workgroup ends
+  for (int w = 0; w < C::WAVES; ++w) pow2 = pow2 & (verdict[w] != 0u);
+  if (pow2)
+    k_loop<C, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+  else
+    k_loop<C, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
 
   if (!cols_valid) return;
   // lane holds Y[m0 + wm + 16i + l%16][n0 + wn + 16j + 4*(l/16) + r], r < 4
