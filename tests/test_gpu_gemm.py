@@ -216,13 +216,33 @@ def test_power_of_two_extreme_exponents(fp8blk_lib):
                                 oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r), what="pow2 shift %d" % shift)
 
 
+@pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("m,k,n", [
     (300, 256, 640),      # few tiles: 64x64 tiles
     (2048, 256, 4096),    # 128x128 tiles
     (2100, 384, 8320),    # 256x256 tiles, with an M tail and a half-width N tail
 ])
-def test_each_tile_configuration(fp8blk_lib, m, k, n):
+def test_each_tile_configuration(fp8blk_lib, m, k, n, pow2):
+    """Every tile configuration, with fold scales and with power-of-two
+    scales (which the MFMA applies itself)."""
     g = synth.generator(13, seed=m + n)
     x = synth.activation(m, k, g, 0.005, 30.0)
     w = synth.weight(n, k, g)
-    _layer_check(x, w)
+    _layer_check(x, w, pow2)
+
+
+def test_power_of_two_one_scale_off_big_tile(fp8blk_lib):
+    """256x256 tiles with power-of-two scales everywhere except one activation
+    scale: that tile folds, every other tile scales inside the MFMA; all match
+    the oracle."""
+    g = synth.generator(14)
+    x = synth.activation(2048, 256, g, 0.01, 50.0)
+    w = synth.weight(8192, 256, g)
+    qa, sa = fb.quant_act(x.to(DEV), pow2=True)
+    qw, sw = fb.quant_weight(w.to(DEV), pow2=True)
+    qa_r, sa_r = oracle.quant_act_ref(x, pow2=True)
+    qw_r, sw_r = oracle.quant_weight_ref(w, pow2=True)
+    sa[700, 1] *= 1.25
+    sa_r[700, 1] *= np.float32(1.25)
+    y = _gemm_guarded(qa, sa, qw, sw)
+    assert_within_tolerance(y.float().cpu().numpy(), oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r), what="one scale off")
