@@ -231,6 +231,17 @@ def test_each_tile_configuration(fp8blk_lib, m, k, n, pow2):
     _layer_check(x, w, pow2)
 
 
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("k", [128, 384])
+def test_big_tile_one_and_odd_k_blocks(fp8blk_lib, k, pow2):
+    """256x256 tiles with a single K block and with an odd number of blocks
+    (the pipeline's prologue and the zero-length refills past the end)."""
+    g = synth.generator(15, seed=k)
+    x = synth.activation(4096, k, g, 0.005, 30.0)
+    w = synth.weight(4096, k, g)
+    _layer_check(x, w, pow2)
+
+
 def test_power_of_two_one_scale_off_big_tile(fp8blk_lib):
     """256x256 tiles with power-of-two scales everywhere except one activation
     scale: that tile folds, every other tile scales inside the MFMA; all match
