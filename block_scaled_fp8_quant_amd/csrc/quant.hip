@@ -192,7 +192,7 @@ extern "C" const char* fp8blk_status_string(fp8blk_status status) {
   switch (status) {
     case FP8BLK_OK: return "ok";
     case FP8BLK_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or bad flag)";
-    case FP8BLK_ERR_SHAPE: return "unsupported shape (K and N must be multiples of 128, E >= 1)";
+    case FP8BLK_ERR_SHAPE: return "unsupported shape (K and N must be multiples of 128, GEMM K <= 2^24, E >= 1)";
     case FP8BLK_ERR_ALIGNMENT: return "misaligned pointer (data 16 bytes, scales 4 bytes)";
     case FP8BLK_ERR_HIP: return "HIP kernel launch failed";
   }
