@@ -19,6 +19,10 @@ What it computes (sources are web pages about NVIDIA NeMo RL's FP8 recipe):
 * Both pages (upppp.jp «まとめ», greentreeone.com «Реальные прирост
   производительности»): the recipe also holds on a mixture-of-experts model,
   which is served here by a grouped GEMM over expert-sorted rows.
+* Both pages (upppp.jp «重要度サンプリングで精度を保つ», greentreeone.com
+  «Реальные прирост производительности»): the quantization kernels are
+  overhead and their fusion is the way past it; ``producers`` holds the two
+  producers fused with the activation quantization (RMSNorm, SiLU * up).
 
 The pages give no scale formula, no E4M3 variant, no rounding mode and no
 accumulation scheme. The readings taken where they are silent are written
@@ -48,6 +52,11 @@ from .quant import (
     quant_act_ref,
     quant_weight_ref,
 )
+from .producers import (
+    rmsnorm_ref,
+    silu_mul_ref,
+    round_bf16,
+)
 from .gemm import (
     dequant_act,
     dequant_weight,
@@ -64,4 +73,5 @@ __all__ = [
     "quant_act_ref", "quant_weight_ref",
     "dequant_act", "dequant_weight", "gemm_ref", "gemm_ref_blas",
     "grouped_gemm_ref", "gemm_rows_ref", "tolerance_ok",
+    "rmsnorm_ref", "silu_mul_ref", "round_bf16",
 ]
