@@ -8,11 +8,13 @@ CPU fallback: if the library is missing, every call raises.
 
 Two layers:
   * ``fp8blk_quant_act``, ``fp8blk_quant_weight``, ``fp8blk_gemm``,
-    ``fp8blk_grouped_gemm``: the C entry points under their own names
+    ``fp8blk_grouped_gemm``, ``fp8blk_rmsnorm_quant_act``,
+    ``fp8blk_silu_mul_quant_act``: the C entry points under their own names
     (integer device pointers, sizes, stream handle); they raise
     ``Fp8BlkError`` on a non-OK status;
-  * ``quant_act``, ``quant_weight``, ``gemm``, ``grouped_gemm``: tensor
-    versions that validate shapes and allocate outputs.
+  * ``quant_act``, ``quant_weight``, ``gemm``, ``grouped_gemm``,
+    ``rmsnorm_quant_act``, ``silu_mul_quant_act``: tensor versions that
+    validate shapes and allocate outputs.
 """
 
 import ctypes
@@ -42,12 +44,14 @@ def load():
         raise RuntimeError("libfp8blk.so is not built (%s); run __graft_entry__.build() "
                            "or python -m block_scaled_fp8_quant_amd.build" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     sigs = {
         "fp8blk_quant_act": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_quant_weight": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8blk_grouped_gemm": [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp],
+        "fp8blk_rmsnorm_quant_act": [vp, vp, f32, i64, i64, vp, vp, vp, i32, vp],
+        "fp8blk_silu_mul_quant_act": [vp, i64, i64, vp, vp, vp, i32, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -83,6 +87,14 @@ def fp8blk_gemm(qa, sa, qw, sw, M, N, K, y, stream):
 
 def fp8blk_grouped_gemm(qa, sa, qw, sw, offsets, E, total_M, N, K, y, stream):
     return _call("fp8blk_grouped_gemm", qa, sa, qw, sw, offsets, E, total_M, N, K, y, stream)
+
+
+def fp8blk_rmsnorm_quant_act(x, gamma, eps, M, K, q, s, y, pow2, stream):
+    return _call("fp8blk_rmsnorm_quant_act", x, gamma, eps, M, K, q, s, y, int(pow2), stream)
+
+
+def fp8blk_silu_mul_quant_act(gu, M, F, q, s, y, pow2, stream):
+    return _call("fp8blk_silu_mul_quant_act", gu, M, F, q, s, y, int(pow2), stream)
 
 
 # ------------------------------------------------------------ tensor API
@@ -196,6 +208,55 @@ def grouped_gemm(qa, sa, qw, sw, offsets, y=None):
     return y
 
 
+def _fused_outputs(m, k, dev, want_y, q, s, y):
+    torch = _torch()
+    q = torch.empty((m, k), dtype=torch.uint8, device=dev) if q is None else q
+    s = torch.empty((m, k // BLOCK), dtype=torch.float32, device=dev) if s is None else s
+    if y is None and want_y:
+        y = torch.empty((m, k), dtype=torch.bfloat16, device=dev)
+    _check(q, "q", torch.uint8, (m, k), dev)
+    _check(s, "s", torch.float32, (m, k // BLOCK), dev)
+    if y is not None:
+        _check(y, "y", torch.bfloat16, (m, k), dev)
+    return q, s, y
+
+
+def rmsnorm_quant_act(x, gamma, eps, pow2=False, want_y=False, q=None, s=None, y=None):
+    """RMSNorm of bf16 X[M, K] with weights gamma[K], rounded to bf16 and
+    quantised per 1x128 group in one kernel -> (Q uint8 [M, K], S fp32
+    [M, K/128], Y bf16 [M, K] or None). Y (the normalised bf16 values) is
+    written if want_y or a y tensor is given."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    m, k = x.shape
+    _check(x, "x", torch.bfloat16, (m, k))
+    _check(gamma, "gamma", torch.bfloat16, (k,), x.device)
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 128")
+    q, s, y = _fused_outputs(m, k, x.device, want_y, q, s, y)
+    fp8blk_rmsnorm_quant_act(x.data_ptr(), gamma.data_ptr(), float(eps), m, k, q.data_ptr(), s.data_ptr(),
+                             None if y is None else y.data_ptr(), pow2, _stream(x.device))
+    return q, s, y
+
+
+def silu_mul_quant_act(gu, pow2=False, want_y=False, q=None, s=None, y=None):
+    """SiLU(gate) * up of bf16 GU[M, 2F] = [gate | up], rounded to bf16 and
+    quantised per 1x128 group in one kernel -> (Q uint8 [M, F], S fp32
+    [M, F/128], Y bf16 [M, F] or None)."""
+    torch = _torch()
+    if gu.dim() != 2 or gu.shape[1] % 2:
+        raise ValueError("gu must be 2-D [M, 2F]")
+    m, f = gu.shape[0], gu.shape[1] // 2
+    _check(gu, "gu", torch.bfloat16, (m, 2 * f))
+    if f % BLOCK:
+        raise ValueError("F must be a multiple of 128")
+    q, s, y = _fused_outputs(m, f, gu.device, want_y, q, s, y)
+    fp8blk_silu_mul_quant_act(gu.data_ptr(), m, f, q.data_ptr(), s.data_ptr(),
+                              None if y is None else y.data_ptr(), pow2, _stream(gu.device))
+    return q, s, y
+
+
 def linear(x, qw, sw, pow2=False):
     """One W8A8 linear layer: quantise X per 1x128 group, then the
     block-scaled GEMM against pre-quantised weights. Returns Y bf16."""
@@ -206,5 +267,7 @@ def linear(x, qw, sw, pow2=False):
 __all__ = [
     "BLOCK", "Fp8BlkError", "LIB_PATH", "load",
     "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
-    "quant_act", "quant_weight", "gemm", "grouped_gemm", "linear",
+    "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act",
+    "quant_act", "quant_weight", "gemm", "grouped_gemm", "rmsnorm_quant_act", "silu_mul_quant_act",
+    "linear",
 ]

@@ -152,6 +152,161 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const u32x4* __restri
   if (t == 0) s[blockIdx.x] = sc;
 }
 
+// ---------------------------------------------------------------------------
+// Producers fused with the activation quantization (the pages name the
+// quantization kernels as overhead and their fusion as the way past it:
+// upppp.jp «重要度サンプリングで精度を保つ», greentreeone.com «Реальные
+// прирост производительности»). Each computes the producer's output in fp32,
+// rounds it once to bf16 (what the unfused producer would write), and
+// quantizes those bf16 values exactly as quant_act_kernel does; the bf16
+// values can also be written out (y != nullptr).
+
+// Sum over the 16 lanes of a DPP row, then over the four rows: every lane
+// gets the wave total. All 64 lanes must be active.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
+}
+
+// Quantize one lane's 8 bf16 values w[0..3] as part of the 128-wide group
+// formed by its 16-lane DPP row, and store codes, scale and (optionally)
+// the bf16 values. `live` is uniform over the row; every lane of the wave
+// must call this (DPP).
+__device__ __forceinline__ void quant_store8(const uint32_t w[4], int pow2, bool live, u32x2* q_unit,
+                                             float* s_group, bool first_lane, u32x4* y_unit) {
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  m = row16_max(m);
+  const float sc = group_scale(m, pow2);
+  const u32x2 codes = encode8(w, sc);
+  if (live) {
+    __builtin_nontemporal_store(codes, q_unit);
+    if (first_lane) *s_group = sc;
+    if (y_unit) __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, y_unit);
+  }
+}
+
+// RMSNorm + quantization: one wave per row of K (K % 128 == 0) elements.
+// The row is walked in 512-element chunks (lane l holds elements 8l..8l+7
+// of a chunk, so each 16-lane row holds one 128-wide group); the first
+// kCachedChunks stay in registers between the two passes, later ones are
+// read again (from L2).
+constexpr int kCachedChunks = 8;  // K <= 4096 kept in registers
+
+// Second pass over one chunk: y = bf16(x * r * gamma), then quantize. Every
+// lane of the wave calls it (DPP inside); lanes past the row end store nothing.
+__device__ __forceinline__ void rmsnorm_quant_chunk(u32x4 v, const u32x4* __restrict__ gamma, float r, int64_t u,
+                                                    int64_t units, int64_t row, int64_t kb, int lane,
+                                                    u32x2* __restrict__ q, float* __restrict__ s,
+                                                    u32x4* __restrict__ y, int pow2) {
+  const bool live = u < units;  // whole 16-lane rows (K % 128 == 0)
+  const u32x4 gv = live ? gamma[u] : u32x4{0, 0, 0, 0};
+  const uint32_t xw[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = pack_bf16(bf16_lo(xw[i]) * r * bf16_lo(gw[i]), bf16_hi(xw[i]) * r * bf16_hi(gw[i]));
+  quant_store8(w, pow2, live, &q[row * units + u], &s[row * kb + u / 16], (lane & 15) == 0,
+               y ? &y[row * units + u] : nullptr);
+}
+
+__global__ __launch_bounds__(256) void rmsnorm_quant_act_kernel(const u32x4* __restrict__ x,
+                                                                const u32x4* __restrict__ gamma, float eps,
+                                                                int64_t M, int64_t K, u32x2* __restrict__ q,
+                                                                float* __restrict__ s, u32x4* __restrict__ y,
+                                                                int pow2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= M) return;  // uniform over the wave
+  const int64_t units = K / 8;                     // 16-byte units per row
+  const int64_t chunks = (units + 63) / 64;
+  const u32x4* xr = x + row * units;
+
+  u32x4 cache[kCachedChunks];
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < kCachedChunks; ++c) {
+    const int64_t u = (int64_t)c * 64 + lane;
+    cache[c] = (c < chunks && u < units) ? __builtin_nontemporal_load(&xr[u]) : u32x4{0, 0, 0, 0};
+    const uint32_t w[4] = {cache[c].x, cache[c].y, cache[c].z, cache[c].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+      ss = __builtin_fmaf(a, a, ss);
+      ss = __builtin_fmaf(b, b, ss);
+    }
+  }
+  for (int64_t c = kCachedChunks; c < chunks; ++c) {
+    const int64_t u = c * 64 + lane;
+    const u32x4 v = u < units ? xr[u] : u32x4{0, 0, 0, 0};
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
+      ss = __builtin_fmaf(a, a, ss);
+      ss = __builtin_fmaf(b, b, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  // r = 1 / sqrt(mean + eps): correctly rounded fp32 division and square root
+  const float r = 1.0f / sqrtf(ss / (float)K + eps);
+
+  const int64_t kb = K / kBlock;
+#pragma unroll
+  for (int c = 0; c < kCachedChunks; ++c)
+    if (c < chunks)  // uniform
+      rmsnorm_quant_chunk(cache[c], gamma, r, c * 64 + lane, units, row, kb, lane, q, s, y, pow2);
+  for (int64_t c = kCachedChunks; c < chunks; ++c) {
+    const int64_t u = c * 64 + lane;
+    rmsnorm_quant_chunk(u < units ? xr[u] : u32x4{0, 0, 0, 0}, gamma, r, u, units, row, kb, lane, q, s, y, pow2);
+  }
+}
+
+// SiLU(gate) * up + quantization. gu is [M][2F] = [gate | up] per row; the
+// output groups are the M * F/128 groups of h = silu(g) * u, laid out like
+// quant_act_kernel's (a 16-lane row per group, 16 groups per wave).
+__global__ __launch_bounds__(256) void silu_mul_quant_act_kernel(const u32x4* __restrict__ gu,
+                                                                 u32x2* __restrict__ q, float* __restrict__ s,
+                                                                 u32x4* __restrict__ y, int64_t groups,
+                                                                 int64_t fb, int pow2) {
+  const int lane = threadIdx.x & 63;
+  const int64_t g_wave = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 16;
+  u32x4 gv[4], uv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t gi = g_wave + k * 4 + (lane >> 4);
+    const int64_t m = gi / fb, b = gi % fb;
+    const int64_t src = m * (2 * fb * 16) + b * 16 + (lane & 15);  // 16-byte units; up starts fb*16 later
+    gv[k] = gi < groups ? __builtin_nontemporal_load(&gu[src]) : u32x4{0, 0, 0, 0};
+    uv[k] = gi < groups ? __builtin_nontemporal_load(&gu[src + fb * 16]) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int64_t gi = g_wave + k * 4 + (lane >> 4);
+    const uint32_t gw[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w}, uw[4] = {uv[k].x, uv[k].y, uv[k].z, uv[k].w};
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float g0 = bf16_lo(gw[i]), g1 = bf16_hi(gw[i]);
+      const float h0 = g0 / (1.0f + expf(-g0)) * bf16_lo(uw[i]);
+      const float h1 = g1 / (1.0f + expf(-g1)) * bf16_hi(uw[i]);
+      w[i] = pack_bf16(h0, h1);
+    }
+    const int64_t unit = gi * 16 + (lane & 15);
+    quant_store8(w, pow2, gi < groups, &q[unit], &s[gi], (lane & 15) == 0, y ? &y[unit] : nullptr);
+  }
+}
+
 }  // namespace
 }  // namespace fp8blk
 
@@ -185,6 +340,41 @@ extern "C" fp8blk_status fp8blk_quant_weight(const uint16_t* w, int64_t N, int64
   hipLaunchKernelGGL(quant_weight_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
                      reinterpret_cast<const u32x4*>(w), reinterpret_cast<u32x2*>(q), s, kblocks, K,
                      pow2);
+  return launch_status();
+}
+
+extern "C" fp8blk_status fp8blk_rmsnorm_quant_act(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,
+                                                  int64_t K, uint8_t* q, float* s, uint16_t* y, int pow2,
+                                                  hipStream_t stream) {
+  if (M < 0 || K <= 0 || (pow2 != 0 && pow2 != 1) || !(eps >= 0.0f) || !(eps < INFINITY))
+    return FP8BLK_ERR_INVALID_ARG;
+  if (K % kBlock) return FP8BLK_ERR_SHAPE;
+  if (M == 0) return FP8BLK_OK;
+  if (!x || !gamma || !q || !s) return FP8BLK_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(q, 16) || !aligned(s, 4) || (y && !aligned(y, 16)))
+    return FP8BLK_ERR_ALIGNMENT;
+  const int64_t blocks = (M + 3) / 4;  // one wave per row
+  if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(rmsnorm_quant_act_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<const u32x4*>(gamma), eps, M, K,
+                     reinterpret_cast<u32x2*>(q), s, reinterpret_cast<u32x4*>(y), pow2);
+  return launch_status();
+}
+
+extern "C" fp8blk_status fp8blk_silu_mul_quant_act(const uint16_t* gu, int64_t M, int64_t F, uint8_t* q, float* s,
+                                                   uint16_t* y, int pow2, hipStream_t stream) {
+  if (M < 0 || F <= 0 || (pow2 != 0 && pow2 != 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (F % kBlock) return FP8BLK_ERR_SHAPE;
+  if (M == 0) return FP8BLK_OK;
+  if (!gu || !q || !s) return FP8BLK_ERR_INVALID_ARG;
+  if (!aligned(gu, 16) || !aligned(q, 16) || !aligned(s, 4) || (y && !aligned(y, 16))) return FP8BLK_ERR_ALIGNMENT;
+  const int64_t fb = F / kBlock;
+  const int64_t groups = M * fb;
+  const int64_t blocks = (groups + 63) / 64;  // 4 waves x 16 groups
+  if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(silu_mul_quant_act_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(gu), reinterpret_cast<u32x2*>(q), s, reinterpret_cast<u32x4*>(y),
+                     groups, fb, pow2);
   return launch_status();
 }
 

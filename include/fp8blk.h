@@ -119,6 +119,51 @@ fp8blk_status fp8blk_grouped_gemm(const uint8_t* qa, const float* sa,
                                   int64_t N, int64_t K,
                                   uint16_t* y, hipStream_t stream);
 
+/*
+ * Fused producers: the bf16 input of a linear layer is computed and quantised
+ * in one pass, so it is never written to and read back from HBM. Both pages
+ * count the quantisation kernels as overhead and name kernel fusion as the
+ * remedy (upppp.jp, «重要度サンプリングで精度を保つ»; greentreeone.com,
+ * «Реальные прирост производительности»), and keep normalisation and the
+ * nonlinearities in bf16 (greentreeone.com, «Технический прорыв»).
+ *
+ * Each call computes the producer in fp32, rounds every value once to bf16
+ * (nearest, ties to even), and quantises exactly those bf16 values as
+ * fp8blk_quant_act does: (q, s) equal fp8blk_quant_act applied to the bf16
+ * values, bit for bit. If y is not NULL the bf16 values are also written
+ * there (for a consumer that needs them unquantised); y may be NULL.
+ * Results that overflow bf16 are undefined, like non-finite inputs.
+ */
+
+/*
+ * RMSNorm + 1x128 quantisation, the input of the qkv and gate_up linears:
+ *   v[m][k] = bf16( x[m][k] * r[m] * gamma[k] ),
+ *   r[m]    = 1 / sqrt( (sum_k x[m][k]^2) / K + eps )   (fp32)
+ *   x     [M][K] bf16 in (16-byte aligned)
+ *   gamma [K]    bf16 in (16-byte aligned)
+ *   eps   finite, >= 0 (with eps == 0 an all-zero row has no defined result)
+ *   q [M][K] codes, s [M][K/128] scales out: as fp8blk_quant_act of v
+ *   y [M][K] bf16 out (v itself), or NULL (16-byte aligned if not NULL)
+ *   M >= 0 (M == 0: no-op), K > 0 and K % 128 == 0, pow2 in {0, 1}.
+ */
+fp8blk_status fp8blk_rmsnorm_quant_act(const uint16_t* x, const uint16_t* gamma, float eps,
+                                       int64_t M, int64_t K, uint8_t* q, float* s,
+                                       uint16_t* y, int pow2, hipStream_t stream);
+
+/*
+ * SiLU(gate) * up + 1x128 quantisation, the input of the down linear:
+ *   h[m][f] = bf16( g / (1 + exp(-g)) * u ),  g = gu[m][f], u = gu[m][F + f]
+ *   gu [M][2F] bf16 in: each row is [gate (F) | up (F)], the gate_up
+ *      linear's output with gate and up weights stacked in that order
+ *      (16-byte aligned)
+ *   q [M][F] codes, s [M][F/128] scales out: as fp8blk_quant_act of h
+ *   y [M][F] bf16 out (h itself), or NULL (16-byte aligned if not NULL)
+ *   M >= 0 (M == 0: no-op), F > 0 and F % 128 == 0, pow2 in {0, 1}.
+ */
+fp8blk_status fp8blk_silu_mul_quant_act(const uint16_t* gu, int64_t M, int64_t F,
+                                        uint8_t* q, float* s, uint16_t* y, int pow2,
+                                        hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (host memory). */
 const char* fp8blk_status_string(fp8blk_status status);
 

@@ -163,6 +163,38 @@ def small_moe_inputs(seed, tokens, hidden, experts, topk, n):
     return x_tok[tok], w, offsets
 
 
+def rmsnorm_inputs(m, k, gen, outlier_frac=0.005, outlier_scale=30.0):
+    """(x [m, k], gamma [k]) bf16: residual-stream rows ~ N(0, 1) with
+    outliers as in ``activation``, and norm weights gamma ~ N(1, 0.25^2)."""
+    x = activation(m, k, gen, outlier_frac, outlier_scale)
+    gamma = (1.0 + 0.25 * torch.randn(k, generator=gen, dtype=torch.float32)).to(torch.bfloat16)
+    return x, gamma
+
+
+def gate_up_output(m, f, gen, gate_std=2.0, up_std=1.0):
+    """gu [m, 2f] bf16, the gate_up linear's output laid out [gate | up]:
+    gate ~ N(0, gate_std^2), up ~ N(0, up_std^2)."""
+    g = torch.randn(m, f, generator=gen, dtype=torch.float32) * gate_std
+    u = torch.randn(m, f, generator=gen, dtype=torch.float32) * up_std
+    return torch.cat([g, u], dim=1).to(torch.bfloat16)
+
+
+def producer_inputs(workload, which, seed=0, m=None):
+    """Full-size inputs of one fused producer of a dense workload:
+    ``which`` = "rmsnorm": (x [M, hidden], gamma [hidden]), the RMSNorm in
+    front of qkv / gate_up (hidden = the qkv linear's K);
+    ``which`` = "silu_mul": gu [M, 2F], the gate_up output in front of down
+    (F = the down linear's K)."""
+    wl = WORKLOADS[workload]
+    dims = {nm: k for nm, k, _ in wl.linears}
+    rows = wl.m if m is None else m
+    if which == "rmsnorm":
+        return rmsnorm_inputs(rows, dims["qkv"], _gen(workload, 0x40, seed), wl.outlier_frac, wl.outlier_scale)
+    if which == "silu_mul":
+        return gate_up_output(rows, dims["down"], _gen(workload, 0x41, seed))
+    raise ValueError(which)
+
+
 def generator(tag, seed=0):
     """A seeded generator for ad-hoc test inputs (``tag`` < 256)."""
     g = torch.Generator(device="cpu")

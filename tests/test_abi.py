@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
-        "fp8blk_status_string"])
+        "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -109,6 +109,43 @@ def test_grouped_gemm_validation(lib):
     assert f(P, P, P, P, P + 2, 2, 4, 128, 128, P, NULL) == ALIGN
     assert f(P, P, P4, P, P, 2, 4, 128, 128, P, NULL) == ALIGN
     assert f(NULL, NULL, NULL, NULL, NULL, 3, 0, 128, 128, NULL, NULL) == OK
+
+
+def test_rmsnorm_quant_act_validation(lib):
+    f = lib.fp8blk_rmsnorm_quant_act
+    assert f(P, P, 1e-5, -1, 128, P, P, P, 0, NULL) == INVALID
+    assert f(P, P, 1e-5, 4, 0, P, P, P, 0, NULL) == INVALID
+    assert f(P, P, 1e-5, 4, 128, P, P, P, 2, NULL) == INVALID          # pow2 flag
+    assert f(P, P, -1e-5, 4, 128, P, P, P, 0, NULL) == INVALID         # eps < 0
+    assert f(P, P, float("nan"), 4, 128, P, P, P, 0, NULL) == INVALID
+    assert f(P, P, float("inf"), 4, 128, P, P, P, 0, NULL) == INVALID
+    assert f(P, P, 1e-5, 4, 100, P, P, P, 0, NULL) == SHAPE
+    for i in range(4):
+        ptrs = [P, P, P, P]
+        ptrs[i] = NULL
+        assert f(ptrs[0], ptrs[1], 1e-5, 4, 128, ptrs[2], ptrs[3], P, 0, NULL) == INVALID
+    assert f(P4, P, 1e-5, 4, 128, P, P, P, 0, NULL) == ALIGN
+    assert f(P, P4, 1e-5, 4, 128, P, P, P, 0, NULL) == ALIGN           # gamma
+    assert f(P, P, 1e-5, 4, 128, P4, P, P, 0, NULL) == ALIGN
+    assert f(P, P, 1e-5, 4, 128, P, P + 2, P, 0, NULL) == ALIGN
+    assert f(P, P, 1e-5, 4, 128, P, P, P4, 0, NULL) == ALIGN           # y, when given
+    assert f(NULL, NULL, 0.0, 0, 128, NULL, NULL, NULL, 1, NULL) == OK  # M == 0 is a no-op
+
+
+def test_silu_mul_quant_act_validation(lib):
+    f = lib.fp8blk_silu_mul_quant_act
+    assert f(P, -1, 128, P, P, P, 0, NULL) == INVALID
+    assert f(P, 4, 0, P, P, P, 0, NULL) == INVALID
+    assert f(P, 4, 128, P, P, P, 3, NULL) == INVALID
+    assert f(P, 4, 192, P, P, P, 0, NULL) == SHAPE
+    assert f(NULL, 4, 128, P, P, P, 0, NULL) == INVALID
+    assert f(P, 4, 128, NULL, P, P, 0, NULL) == INVALID
+    assert f(P, 4, 128, P, NULL, P, 0, NULL) == INVALID
+    assert f(P4, 4, 128, P, P, P, 0, NULL) == ALIGN
+    assert f(P, 4, 128, P4, P, P, 0, NULL) == ALIGN
+    assert f(P, 4, 128, P, P + 1, P, 0, NULL) == ALIGN
+    assert f(P, 4, 128, P, P, P4, 0, NULL) == ALIGN
+    assert f(NULL, 0, 128, NULL, NULL, NULL, 0, NULL) == OK
 
 
 def test_python_entry_points_raise(lib):
