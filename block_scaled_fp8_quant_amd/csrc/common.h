@@ -1,5 +1,5 @@
 // Shared helpers of libfp8blk.so: host-side argument checks and small
-// device utilities (bf16 unpacking, 16-lane DPP reductions, packing).
+// device utilities (bf16 unpacking and packing, buffer resources).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,15 +28,14 @@ inline fp8blk_status launch_status() {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Maximum over the 16 lanes of a DPP row (lanes 16r .. 16r+15). Every lane
-// of the row must be active. quad_perm swaps lanes 1<->0 and 2<->3, then
-// pairs of lanes; row_half_mirror and row_mirror fold 8 and 16 lanes.
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
-  return v;
+// Buffer resource over `bytes` bytes from `base` (raw, stride 0): loads at
+// byte offsets past the end return zeros instead of faulting, which lets
+// ragged edges be read without branches.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
 }
 
 // bf16 bits of an fp32 value, round to nearest even (finite inputs).

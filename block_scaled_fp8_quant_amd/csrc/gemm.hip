@@ -154,16 +154,10 @@ __device__ __forceinline__ void wait_vm() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Direct global->LDS loads through buffer resources. A resource covers the
-// tile's rows from its first row to the end of the operand (at most 4 GB);
-// the hardware range check returns zeros for rows past the end, so partial
-// tiles need no clamping. Lane offsets are 32-bit: BM * K < 2^32.
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr int kRsrcFlags = 0x00020000;  // raw (stride 0) dword-addressed resource
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcFlags);
-}
+// Direct global->LDS loads through buffer resources (make_rsrc). A resource
+// covers the tile's rows from its first row to the end of the operand (at
+// most 4 GB); the hardware range check returns zeros for rows past the end,
+// so partial tiles need no clamping. Lane offsets are 32-bit: BM * K < 2^32.
 __device__ __forceinline__ void dma16(rsrc_t r, uint32_t voff, uint32_t soff, lds_u8* lds_window) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_window, 16, voff, soff, 0, 0);
 }

@@ -35,9 +35,18 @@ constexpr float kFastMinScale = 0x1p-90f;
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// RN32(amax / 448) without a division: q0 = amax * RN32(1/448), then one
+// fma-corrected step. Equal to the IEEE quotient for every positive finite
+// bf16 amax, subnormal results included (checked exhaustively on the CPU);
+// amax is always a bf16 value here, the largest magnitude of its group.
+constexpr float kInv448 = 0x1.24924ap-9f;  // RN32(1/448)
+
 __device__ __forceinline__ float group_scale(float amax, int pow2) {
   if (amax == 0.0f) return 0.0f;
-  if (!pow2) return amax / kE4M3Max;  // correctly rounded fp32 division
+  if (!pow2) {
+    const float q0 = amax * kInv448;
+    return __builtin_fmaf(-__builtin_fmaf(kE4M3Max, q0, -amax), kInv448, q0);
+  }
   // amax = m * 2**e with m in [0.5, 1); 448 * 2**k = 0.875 * 2**(k+9).
   // k = e-9 suffices iff m <= 0.875 (k = e-10 never does), else k = e-8.
   int e;
@@ -54,6 +63,11 @@ __device__ __forceinline__ u32x2 encode8(const uint32_t w[4], float s) {
     a[2 * i] = fabsf(bf16_lo(w[i]));
     a[2 * i + 1] = fabsf(bf16_hi(w[i]));
   }
+  // v_cvt_pk_fp8_f32 rounds to nearest even and gives the NaN code only
+  // above 464 (the midpoint between 448 and 480). With a normal scale every
+  // quotient is at most RN32(amax / s) <= 448 (1 + 2^-23), so the fast path
+  // needs no clamp; a subnormal scale can be rounded far below amax / 448,
+  // so the division path clamps at 448.
   float q[8];
   if (s >= kFastMinScale) {
     const float r = 1.0f / s;
@@ -65,10 +79,8 @@ __device__ __forceinline__ u32x2 encode8(const uint32_t w[4], float s) {
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = (s == 0.0f) ? 0.0f : a[j] / s;
+    for (int j = 0; j < 8; ++j) q[j] = (s == 0.0f) ? 0.0f : fminf(a[j] / s, kE4M3Max);
   }
-#pragma unroll
-  for (int j = 0; j < 8; ++j) q[j] = fminf(q[j], kE4M3Max);  // saturate
 
   uint32_t c0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
   c0 = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], c0, true);
@@ -78,6 +90,34 @@ __device__ __forceinline__ u32x2 encode8(const uint32_t w[4], float s) {
   c0 |= __builtin_amdgcn_perm(w[1], w[0], 0x07050301u) & 0x80808080u;
   c1 |= __builtin_amdgcn_perm(w[3], w[2], 0x07050301u) & 0x80808080u;
   return u32x2{c0, c1};
+}
+
+// Largest magnitude of the 8 bf16 values in w[0..3], as fp32 bits. For
+// finite non-negative floats the order of the bit patterns is the numeric
+// order, so the maximum is taken on the packed 16-bit magnitudes (one
+// v_pk_max_u16 per two values) and widened once.
+__device__ __forceinline__ uint32_t amax8_bits(const uint32_t w[4]) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+  const uint32_t p = __builtin_bit_cast(uint32_t, m);
+  return max(p << 16, p & 0xFFFF0000u);
+}
+
+// Maximum of non-negative fp32 bit patterns over a 16-lane DPP row (lanes
+// 16r .. 16r+15): quad_perm swaps lanes 1<->0 and 2<->3, then pairs of
+// lanes; row_half_mirror and row_mirror fold 8 and 16 lanes. Every lane of
+// the row must be active.
+// No lane of these patterns reads outside its row, so the 0 supplied for
+// out-of-row sources (bound_ctrl) never takes part; with it the compiler
+// fuses each exchange into one v_max_u32_dpp.
+__device__ __forceinline__ uint32_t row16_max_bits(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, true));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, true));
+  return v;
 }
 
 // x, q viewed as 16-byte / 8-byte units: group g occupies units 16g .. 16g+15.
@@ -97,11 +137,8 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const u32x4* __restrict_
   for (int u = 0; u < 4; ++u) {
     const int64_t g = g_wave + u * 4 + (lane >> 4);
     const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
-    m = row16_max(m);  // all 64 lanes take part
-    const float sc = group_scale(m, pow2);
+    // all 64 lanes take part in the row maximum
+    const float sc = group_scale(__uint_as_float(row16_max_bits(amax8_bits(w))), pow2);
     const u32x2 codes = encode8(w, sc);
     if (g < groups) {
       __builtin_nontemporal_store(codes, &q[g * 16 + (lane & 15)]);
@@ -127,14 +164,13 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const u32x4* __restri
 #pragma unroll
   for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load(&w[base + (int64_t)i * 16 * row_units]);
 
-  float m = 0.0f;
+  uint32_t mb = 0;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t ww[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(ww[j])), fabsf(bf16_hi(ww[j]))));
+    mb = max(mb, amax8_bits(ww));
   }
-  m = row16_max(m);
+  float m = __uint_as_float(row16_max_bits(mb));
   if ((t & 15) == 0) red[t >> 4] = m;
   __syncthreads();
   m = red[0];
@@ -173,8 +209,12 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Two fp32 values to a packed bf16 pair (lo in the low half), round to
+// nearest even: one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return (uint32_t)to_bf16_bits(lo) | ((uint32_t)to_bf16_bits(hi) << 16);
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Quantize one lane's 8 bf16 values w[0..3] as part of the 128-wide group
@@ -183,11 +223,7 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 // must call this (DPP).
 __device__ __forceinline__ void quant_store8(const uint32_t w[4], int pow2, bool live, u32x2* q_unit,
                                              float* s_group, bool first_lane, u32x4* y_unit) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
-  m = row16_max(m);
-  const float sc = group_scale(m, pow2);
+  const float sc = group_scale(__uint_as_float(row16_max_bits(amax8_bits(w))), pow2);
   const u32x2 codes = encode8(w, sc);
   if (live) {
     __builtin_nontemporal_store(codes, q_unit);
@@ -196,85 +232,204 @@ __device__ __forceinline__ void quant_store8(const uint32_t w[4], int pow2, bool
   }
 }
 
-// RMSNorm + quantization: one wave per row of K (K % 128 == 0) elements.
-// The row is walked in 512-element chunks (lane l holds elements 8l..8l+7
-// of a chunk, so each 16-lane row holds one 128-wide group); the first
-// kCachedChunks stay in registers between the two passes, later ones are
-// read again (from L2).
-constexpr int kCachedChunks = 8;  // K <= 4096 kept in registers
-
-// Second pass over one chunk: y = bf16(x * r * gamma), then quantize. Every
-// lane of the wave calls it (DPP inside); lanes past the row end store nothing.
-__device__ __forceinline__ void rmsnorm_quant_chunk(u32x4 v, const u32x4* __restrict__ gamma, float r, int64_t u,
-                                                    int64_t units, int64_t row, int64_t kb, int lane,
-                                                    u32x2* __restrict__ q, float* __restrict__ s,
-                                                    u32x4* __restrict__ y, int pow2) {
-  const bool live = u < units;  // whole 16-lane rows (K % 128 == 0)
-  const u32x4 gv = live ? gamma[u] : u32x4{0, 0, 0, 0};
-  const uint32_t xw[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
-  uint32_t w[4];
+// Sum of squares of the 8 bf16 values of a 16-byte unit added to acc, one
+// v_dot2_f32_bf16 per pair (exact bf16 products, fp32 accumulation).
+__device__ __forceinline__ float sum_sq8(u32x4 v, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = pack_bf16(bf16_lo(xw[i]) * r * bf16_lo(gw[i]), bf16_hi(xw[i]) * r * bf16_hi(gw[i]));
-  quant_store8(w, pow2, live, &q[row * units + u], &s[row * kb + u / 16], (lane & 15) == 0,
-               y ? &y[row * units + u] : nullptr);
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 p = __builtin_bit_cast(bf16x2, w[i]);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(p, p, acc, false);
+  }
+  return acc;
 }
 
-__global__ __launch_bounds__(256) void rmsnorm_quant_act_kernel(const u32x4* __restrict__ x,
-                                                                const u32x4* __restrict__ gamma, float eps,
-                                                                int64_t M, int64_t K, u32x2* __restrict__ q,
-                                                                float* __restrict__ s, u32x4* __restrict__ y,
-                                                                int pow2) {
+// ---------------------------------------------------------------- RMSNorm
+// Workgroups of four waves, each taking kRmsIters consecutive slices of
+// rows. Each row is handled by WPR waves (T = 64*WPR threads; thread t
+// holds 16-byte units t, t+T, .. of the row, at most CU of them, so a
+// 16-lane DPP row holds whole 128-wide groups). gamma is loaded once per
+// workgroup and kept in registers; the next row's x is loaded while the
+// current one is normalised and quantized. With WPR > 1 the waves of a row
+// add their partial sums through LDS, in a fixed order (the result does not
+// depend on timing).
+constexpr int kRmsIters = 4;
+constexpr int kNontemporal = 2;  // cache-policy bits of a buffer load: nt (streamed once)
+
+template <int WPR, int CU>
+__global__ __launch_bounds__(256) void rmsnorm_quant_act_rows_kernel(
+    const u32x4* __restrict__ x, const u32x4* __restrict__ gamma, float eps, int64_t M, int64_t K,
+    u32x2* __restrict__ q, float* __restrict__ s, u32x4* __restrict__ y, int pow2) {
+  constexpr int T = 64 * WPR;
+  constexpr int RPW = 4 / WPR;  // rows per workgroup and iteration
+  // gamma as fp32 when it fits, else packed and widened at each use
+  constexpr bool kGammaF32 = CU <= 2;
+  __shared__ float red[2][4];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int sub = wave / WPR, t = (wave % WPR) * 64 + lane;
+  const int64_t units = K / 8, kb = K / kBlock;
+
+  u32x4 gp[CU];
+  float gf[kGammaF32 ? CU : 1][8];
+#pragma unroll
+  for (int c = 0; c < CU; ++c) {
+    const int64_t u = t + (int64_t)c * T;
+    gp[c] = u < units ? gamma[u] : u32x4{0, 0, 0, 0};
+    if constexpr (kGammaF32) {
+      const uint32_t g[4] = {gp[c].x, gp[c].y, gp[c].z, gp[c].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        gf[c][2 * i] = bf16_lo(g[i]);
+        gf[c][2 * i + 1] = bf16_hi(g[i]);
+      }
+    }
+  }
+
+  // Branch-free row loads: the resource covers the wave's row (nothing
+  // past the last row), so units past the row end, and rows past M, read
+  // as zeros. K <= 8192 here: offsets stay far below 2^32.
+  const int64_t first = (int64_t)blockIdx.x * RPW * kRmsIters;
+  auto load_row = [&](u32x4 (&v)[CU], int64_t row) {
+    const bool in = row < M;
+    const rsrc_t rs = make_rsrc(x + (in ? row : 0) * units, in ? (uint32_t)(K * 2) : 0u);
+#pragma unroll
+    for (int c = 0; c < CU; ++c)
+      v[c] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(t + c * T) * 16u, 0,
+                                                                           kNontemporal));
+  };
+  u32x4 cur[CU];
+  load_row(cur, first + sub);
+#pragma unroll
+  for (int it = 0; it < kRmsIters; ++it) {
+    const int64_t base = first + it * RPW;
+    if (base >= M) break;  // uniform over the workgroup
+    const int64_t row = base + sub;
+    const int buf = it & 1;
+
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CU; ++c) ss = sum_sq8(cur[c], ss);
+    // Issue the next row's loads only after this row's data has been
+    // consumed: the wait the compiler places before the first use of
+    // `cur` then does not also wait for the prefetch.
+    asm volatile("" : "+v"(ss) : : "memory");
+    u32x4 nxt[CU];
+    if (it + 1 < kRmsIters) load_row(nxt, row + RPW);
+
+    ss = wave_sum(ss);
+    if constexpr (WPR > 1) {
+      // double-buffered: a wave can only overwrite red[buf] two iterations
+      // later, after every wave has passed the barrier of the next one
+      if (lane == 0) red[buf][wave] = ss;
+      __syncthreads();
+      ss = red[buf][sub * WPR];
+#pragma unroll
+      for (int j = 1; j < WPR; ++j) ss += red[buf][sub * WPR + j];
+    }
+    // r = 1 / sqrt(mean + eps): correctly rounded fp32 division and square root
+    const float r = 1.0f / sqrtf(ss / (float)K + eps);
+
+#pragma unroll
+    for (int c = 0; c < CU; ++c) {
+      const int64_t u = t + (int64_t)c * T;
+      const bool live = row < M && u < units;  // uniform over each 16-lane row
+      const uint32_t xw[4] = {cur[c].x, cur[c].y, cur[c].z, cur[c].w};
+      uint32_t w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float g0, g1;
+        if constexpr (kGammaF32) {
+          g0 = gf[c][2 * i];
+          g1 = gf[c][2 * i + 1];
+        } else {
+          const uint32_t g[4] = {gp[c].x, gp[c].y, gp[c].z, gp[c].w};
+          g0 = bf16_lo(g[i]);
+          g1 = bf16_hi(g[i]);
+        }
+        w[i] = pack_bf16(bf16_lo(xw[i]) * r * g0, bf16_hi(xw[i]) * r * g1);
+      }
+      const int64_t e = live ? row * units + u : 0;
+      quant_store8(w, pow2, live, &q[e], &s[live ? row * kb + u / 16 : 0], (lane & 15) == 0,
+                   y ? &y[e] : nullptr);
+    }
+    if (it + 1 < kRmsIters) {
+#pragma unroll
+      for (int c = 0; c < CU; ++c) cur[c] = nxt[c];
+    }
+  }
+}
+
+// Rows too long for the register cache of the kernel above (K > 8192): one
+// wave per row, the row read twice (the second time mostly from L2).
+__global__ __launch_bounds__(256) void rmsnorm_quant_act_long_kernel(const u32x4* __restrict__ x,
+                                                                     const u32x4* __restrict__ gamma, float eps,
+                                                                     int64_t M, int64_t K, u32x2* __restrict__ q,
+                                                                     float* __restrict__ s, u32x4* __restrict__ y,
+                                                                     int pow2) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= M) return;  // uniform over the wave
-  const int64_t units = K / 8;                     // 16-byte units per row
-  const int64_t chunks = (units + 63) / 64;
+  const int64_t units = K / 8, kb = K / kBlock;
   const u32x4* xr = x + row * units;
-
-  u32x4 cache[kCachedChunks];
   float ss = 0.0f;
-#pragma unroll
-  for (int c = 0; c < kCachedChunks; ++c) {
-    const int64_t u = (int64_t)c * 64 + lane;
-    cache[c] = (c < chunks && u < units) ? __builtin_nontemporal_load(&xr[u]) : u32x4{0, 0, 0, 0};
-    const uint32_t w[4] = {cache[c].x, cache[c].y, cache[c].z, cache[c].w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
-      ss = __builtin_fmaf(a, a, ss);
-      ss = __builtin_fmaf(b, b, ss);
-    }
-  }
-  for (int64_t c = kCachedChunks; c < chunks; ++c) {
-    const int64_t u = c * 64 + lane;
-    const u32x4 v = u < units ? xr[u] : u32x4{0, 0, 0, 0};
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = bf16_lo(w[i]), b = bf16_hi(w[i]);
-      ss = __builtin_fmaf(a, a, ss);
-      ss = __builtin_fmaf(b, b, ss);
-    }
-  }
-  ss = wave_sum(ss);
-  // r = 1 / sqrt(mean + eps): correctly rounded fp32 division and square root
+  for (int64_t u = lane; u < units; u += 64) ss = sum_sq8(xr[u], ss);
+  ss = wave_sum(ss);  // the lanes reconverge after the loop
   const float r = 1.0f / sqrtf(ss / (float)K + eps);
-
-  const int64_t kb = K / kBlock;
+  for (int64_t u0 = 0; u0 < units; u0 += 64) {  // uniform
+    const int64_t u = u0 + lane;
+    const bool live = u < units;
+    const u32x4 v = live ? xr[u] : u32x4{0, 0, 0, 0};
+    const u32x4 gv = live ? gamma[u] : u32x4{0, 0, 0, 0};
+    const uint32_t xw[4] = {v.x, v.y, v.z, v.w}, gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t w[4];
 #pragma unroll
-  for (int c = 0; c < kCachedChunks; ++c)
-    if (c < chunks)  // uniform
-      rmsnorm_quant_chunk(cache[c], gamma, r, c * 64 + lane, units, row, kb, lane, q, s, y, pow2);
-  for (int64_t c = kCachedChunks; c < chunks; ++c) {
-    const int64_t u = c * 64 + lane;
-    rmsnorm_quant_chunk(u < units ? xr[u] : u32x4{0, 0, 0, 0}, gamma, r, u, units, row, kb, lane, q, s, y, pow2);
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack_bf16(bf16_lo(xw[i]) * r * bf16_lo(gw[i]), bf16_hi(xw[i]) * r * bf16_hi(gw[i]));
+    const int64_t e = live ? row * units + u : 0;
+    quant_store8(w, pow2, live, &q[e], &s[live ? row * kb + u / 16 : 0], (lane & 15) == 0,
+                 y ? &y[e] : nullptr);
   }
 }
 
-// SiLU(gate) * up + quantization. gu is [M][2F] = [gate | up] per row; the
-// output groups are the M * F/128 groups of h = silu(g) * u, laid out like
-// quant_act_kernel's (a 16-lane row per group, 16 groups per wave).
+// ---------------------------------------------------------------- SiLU * up
+// silu(g) * u = g * u / (1 + 2^a), a = -g log2(e), with the hardware exp2
+// and reciprocal (each within 1 ulp). The reciprocal does not return
+// subnormals, so 1 + 2^a must stay below 2^126: silu_mul_near serves
+// g > -64 (a < 92.4). For g <= -64, silu_mul_far takes the denominator
+// scaled by 2^-64 (2^-64 + 2^(a-64)) and scales the result back by an exact
+// 2^-64 at the end; exp2 then overflows only where the exact result is far
+// below the smallest bf16 subnormal. Relative error before the bf16
+// rounding: below 2^-16 (dominated by the rounding of a, at most
+// 2^-24 * |a| with |a| <= 192 where the result is not negligible); for
+// g > 0 large, sigma is 1 to fp32 precision.
+constexpr float kLog2e = 1.44269504088896341f;
+
+__device__ __forceinline__ float silu_mul_near(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * kLog2e)) * u;
+}
+
+__device__ __forceinline__ float silu_mul_far(float g, float u) {
+  const bool far = g <= -64.0f;
+  const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(-g, kLog2e, far ? -64.0f : 0.0f));
+  const float h = g * __builtin_amdgcn_rcpf((far ? 0x1p-64f : 1.0f) + e) * u;
+  return far ? h * 0x1p-64f : h;
+}
+
+// Whether any of the 8 packed bf16 gates is <= -64: the bit patterns of
+// negative values grow with their magnitude, and -64 is 0xC280.
+__device__ __forceinline__ bool any_gate_far(const uint32_t gw[4]) {
+  typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+  u16x2 m = __builtin_bit_cast(u16x2, gw[0]);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, gw[i]));
+  return max((uint32_t)m.x, (uint32_t)m.y) >= 0xC280u;
+}
+
+// gu is [M][2F] = [gate | up] per row; the output groups are the M * F/128
+// groups of h = silu(g) * u, laid out like quant_act_kernel's (a 16-lane
+// row per group, 16 groups per wave).
 __global__ __launch_bounds__(256) void silu_mul_quant_act_kernel(const u32x4* __restrict__ gu,
                                                                  u32x2* __restrict__ q, float* __restrict__ s,
                                                                  u32x4* __restrict__ y, int64_t groups,
@@ -296,14 +451,18 @@ __global__ __launch_bounds__(256) void silu_mul_quant_act_kernel(const u32x4* __
     const uint32_t gw[4] = {gv[k].x, gv[k].y, gv[k].z, gv[k].w}, uw[4] = {uv[k].x, uv[k].y, uv[k].z, uv[k].w};
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float g0 = bf16_lo(gw[i]), g1 = bf16_hi(gw[i]);
-      const float h0 = g0 / (1.0f + expf(-g0)) * bf16_lo(uw[i]);
-      const float h1 = g1 / (1.0f + expf(-g1)) * bf16_hi(uw[i]);
-      w[i] = pack_bf16(h0, h1);
+    for (int i = 0; i < 4; ++i)
+      w[i] = pack_bf16(silu_mul_near(bf16_lo(gw[i]), bf16_lo(uw[i])),
+                       silu_mul_near(bf16_hi(gw[i]), bf16_hi(uw[i])));
+    if (__builtin_amdgcn_ballot_w64(any_gate_far(gw)) != 0) {  // uniform; gates <= -64 are rare
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = pack_bf16(silu_mul_far(bf16_lo(gw[i]), bf16_lo(uw[i])),
+                         silu_mul_far(bf16_hi(gw[i]), bf16_hi(uw[i])));
     }
-    const int64_t unit = gi * 16 + (lane & 15);
-    quant_store8(w, pow2, gi < groups, &q[unit], &s[gi], (lane & 15) == 0, y ? &y[unit] : nullptr);
+    const int64_t unit = gi < groups ? gi * 16 + (lane & 15) : 0;
+    quant_store8(w, pow2, gi < groups, &q[unit], &s[gi < groups ? gi : 0], (lane & 15) == 0,
+                 y ? &y[unit] : nullptr);
   }
 }
 
@@ -353,11 +512,32 @@ extern "C" fp8blk_status fp8blk_rmsnorm_quant_act(const uint16_t* x, const uint1
   if (!x || !gamma || !q || !s) return FP8BLK_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(gamma, 16) || !aligned(q, 16) || !aligned(s, 4) || (y && !aligned(y, 16)))
     return FP8BLK_ERR_ALIGNMENT;
-  const int64_t blocks = (M + 3) / 4;  // one wave per row
-  if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(rmsnorm_quant_act_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4*>(x), reinterpret_cast<const u32x4*>(gamma), eps, M, K,
-                     reinterpret_cast<u32x2*>(q), s, reinterpret_cast<u32x4*>(y), pow2);
+  if ((M + 3) / 4 > INT32_MAX) return FP8BLK_ERR_SHAPE;  // the largest grid below: 4 rows per workgroup
+  const int64_t units = K / 8;
+  const u32x4* xv = reinterpret_cast<const u32x4*>(x);
+  const u32x4* gv = reinterpret_cast<const u32x4*>(gamma);
+  u32x2* qv = reinterpret_cast<u32x2*>(q);
+  u32x4* yv = reinterpret_cast<u32x4*>(y);
+  // waves per row and cached units per lane: 8 to 16 values per lane in
+  // registers for K <= 4096, 32 for K <= 8192
+  auto launch = [&](auto kernel, int64_t rows_per_iter) {
+    const int64_t rows_per_wg = rows_per_iter * kRmsIters;
+    const int64_t wgs = (M + rows_per_wg - 1) / rows_per_wg;
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)wgs), dim3(256), 0, stream, xv, gv, eps, M, K, qv, s, yv, pow2);
+  };
+  if (units <= 128) {
+    launch(rmsnorm_quant_act_rows_kernel<1, 2>, 4);
+  } else if (units <= 256) {
+    launch(rmsnorm_quant_act_rows_kernel<2, 2>, 2);
+  } else if (units <= 512) {
+    launch(rmsnorm_quant_act_rows_kernel<4, 2>, 1);
+  } else if (units <= 1024) {
+    launch(rmsnorm_quant_act_rows_kernel<4, 4>, 1);
+  } else {
+    const int64_t blocks = (M + 3) / 4;  // one wave per row
+    hipLaunchKernelGGL(rmsnorm_quant_act_long_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, xv, gv, eps,
+                       M, K, qv, s, yv, pow2);
+  }
   return launch_status();
 }
 

@@ -30,10 +30,9 @@ DEV = "cuda:0"
 # two products. 2^-14 leaves a wide margin while still being 64x finer than
 # a bf16 ulp.
 MID_WINDOW = 2.0 ** -14
-# Below 2^-120 the fp32 producer underflows (exp(-g) overflows for
-# g < -88.7, so silu(g) becomes -0 where the exact value is ~1e-38);
-# such values are compared as zero.
-TINY = 2.0 ** -120
+# Below the smallest normal number the kernel's fp32 arithmetic may flush
+# to zero; exact values there are compared as zero.
+TINY = 2.0 ** -126
 
 
 def bits_of(t):
@@ -107,12 +106,16 @@ def check_silu(gu, pow2, what="silu_mul"):
 
 # ------------------------------------------------------------------ RMSNorm
 
-# K = 128: one group; 384: a partial 512-element chunk; 4096: every chunk
-# held in registers; 4736 and 8192: chunks past the register cache read
-# again, the last one partial for 4736. M not a multiple of the 4 rows a
-# workgroup takes.
+# Shapes over every kernel variant (16-byte units per row U = K/8):
+# U <= 128: one wave per row (K = 128, 384, 1024); U <= 256: two waves per
+# row (1152, 2048); U <= 512: four waves, two units per lane (2176, 4096);
+# U <= 1024: four waves, four units per lane (4224, 8192); longer rows: the
+# one-wave kernel that reads the row twice (8832, 16384). The row counts
+# leave ragged last workgroups (a workgroup takes 16, 8 or 4 rows) and
+# lanes past the row end.
 @pytest.mark.parametrize("pow2", [False, True])
-@pytest.mark.parametrize("m,k", [(1, 128), (5, 384), (13, 4096), (7, 4736), (6, 8192)])
+@pytest.mark.parametrize("m,k", [(1, 128), (37, 128), (5, 384), (37, 1024), (19, 1152), (11, 2048), (9, 2176),
+                                 (13, 4096), (6, 4224), (6, 8192), (3, 8832), (2, 16384)])
 def test_rmsnorm_shapes(fp8blk_lib, m, k, pow2):
     x, gamma = synth.rmsnorm_inputs(m, k, synth.generator(40, k + m))
     print("rmsnorm m=%d k=%d pow2=%d" % (m, k, pow2), flush=True)
@@ -185,8 +188,8 @@ def test_silu_mul_shapes(fp8blk_lib, m, f, pow2):
 
 def test_silu_mul_special_values(fp8blk_lib):
     """Gate values across the whole sigmoid: zero (h = 0), large positive
-    (h = g * u), large negative (h -> 0, underflowing below -88.7), a zero
-    up half, and every finite bf16 gate value in [-128, 128]."""
+    (h = g * u), large negative (h -> 0 through the bf16 subnormals), a
+    zero up half, and every finite bf16 gate value in [-128, 128]."""
     f = 1024
     gen = synth.generator(44)
     g = torch.randn(6, f, generator=gen) * 3

@@ -110,9 +110,26 @@ def _special_rows():
     return torch.tensor(x, dtype=torch.float32).to(torch.bfloat16)
 
 
+def _scale_rounded_down_rows():
+    """Groups whose fp32 scale amax/448 rounds down, so the largest
+    elements' quotients land just above 448 (they must still encode to
+    +-448): every such bf16 amax with exponent in [-80, 100), 512 of them
+    evenly spaced, each with -amax and its lower bf16 neighbour."""
+    b = np.arange(0x0001, 0x7F80, dtype=np.uint32)
+    amax = (b << 16).view(np.float32).astype(np.float64)
+    s32 = (amax / 448.0).astype(np.float32).astype(np.float64)
+    pick = amax[(s32 * 448.0 < amax) & (amax >= 2.0 ** -80) & (amax < 2.0 ** 100)]
+    pick = pick[np.linspace(0, len(pick) - 1, 512).astype(np.int64)]
+    g = np.zeros((len(pick), 128))
+    g[:, 0] = pick
+    g[:, 1] = -pick
+    g[:, 2] = pick * (1 - 2.0 ** -8)
+    return torch.tensor(g, dtype=torch.float32).to(torch.bfloat16)
+
+
 @pytest.mark.parametrize("pow2", [False, True])
 def test_adversarial_groups(fp8blk_lib, pow2):
-    x = torch.cat([_tie_rows(), _divide_vs_reciprocal_rows(), _special_rows()])
+    x = torch.cat([_tie_rows(), _divide_vs_reciprocal_rows(), _special_rows(), _scale_rounded_down_rows()])
     x = x.reshape(-1, 128)
     pad = (-x.shape[0]) % 4
     x = torch.cat([x, torch.zeros(pad, 128, dtype=torch.bfloat16)]).reshape(-1, 512)

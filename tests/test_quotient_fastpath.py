@@ -1,9 +1,10 @@
 """The corrected-reciprocal quotient of the quantisation kernels equals IEEE
-fp32 division wherever it decides a code (exhaustive over bf16, CPU only).
+fp32 division wherever it decides a code, and their division-free scale
+amax/448 equals the IEEE quotient (both exhaustive over bf16, CPU only).
 
-The kernels use it for scales s >= 2**-90; the same check with the bound
-lowered to 2**-126 finds disagreeing codes, which is why smaller scales
-take a true division."""
+The kernels use the quotient shortcut for scales s >= 2**-90; the same
+check with the bound lowered to 2**-126 finds disagreeing codes, which is
+why smaller scales take a true division."""
 
 import os
 import shutil
@@ -13,6 +14,7 @@ import pytest
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "quotient_fastpath_check.c")
+SCALE_SRC = os.path.join(HERE, "csrc", "scale_fastpath_check.c")
 
 
 @pytest.fixture(scope="module")
@@ -37,3 +39,13 @@ def test_lower_bound_is_needed(checker):
     """With subnormal-range scales allowed, the shortcut does change codes."""
     out = subprocess.run([checker, "0", "-126"], capture_output=True, text=True, timeout=600).stdout
     assert "code_mismatches=0" not in out
+
+
+def test_division_free_scale_is_exact(tmp_path):
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    exe = str(tmp_path / "scheck")
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-o", exe, SCALE_SRC, "-lm"], check=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout
+    assert "checked=32639 mismatches=0" in out.stdout
