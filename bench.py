@@ -10,7 +10,10 @@ the measured step time (quantisation included), in TFLOP/s. ``roofline``
 covers the dominant kernel (the GEMM) with its average launch duration
 measured by HIP events on the launch stream inside the timed region.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload.
+workload. ``producers`` (after the timed region) times the two fused
+producer kernels at the workload's shapes -- RMSNorm -> 1x128 quantisation
+of the qkv / gate_up input and SiLU(gate)*up -> quantisation of the down
+input -- each against the HBM roofline.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -20,8 +23,9 @@ device copy run in the same process (--copy-yardstick):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d F -o f -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-yardstick
   rocprofv3 --pmc WRITE_SIZE --output-format csv -d W -o w -- python bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-yardstick
   python bench.py --summarize-traffic F/f_counter_collection.csv W/w_counter_collection.csv
-which writes profiles/traffic.json (keyed by a hash of the kernel sources,
-so a later kernel change turns the reported traffic back into null).
+which writes profiles/traffic.json (each kernel's record keyed by a hash of
+its sources, so a later change to them turns the reported traffic back into
+null).
 """
 
 import argparse
@@ -39,6 +43,9 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 GEMM_KERNELS = ("gemm_kernel", "grouped_gemm_kernel")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# kernels whose counter traffic is recorded (substrings of the kernel names)
+TRAFFIC_KERNELS = ("gemm_kernel", "quant_act_kernel", "quant_weight_kernel", "rmsnorm_quant_act_rows_kernel",
+                   "silu_mul_quant_act_kernel")
 
 
 def parse():
@@ -49,6 +56,8 @@ def parse():
     p.add_argument("--workload", default="llama8b_prefill",
                    choices=["llama8b_prefill", "llama8b_decode", "qwen8b_pow2", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-producers", action="store_true", help="skip timing the fused producer kernels")
+    p.add_argument("--producer-reps", type=int, default=20)
     p.add_argument("--cpu-sample-rows", type=int, default=8192)
     p.add_argument("--cpu-sample-wrows", type=int, default=1536)
     p.add_argument("--copy-yardstick", action="store_true",
@@ -58,9 +67,15 @@ def parse():
     return p.parse_args()
 
 
-def source_hash():
+# the sources each recorded kernel is built from: a counter record stays
+# valid while these files are unchanged
+KERNEL_SOURCES = {"gemm_kernel": ("gemm.hip", "common.h")}
+QUANT_SOURCES = ("quant.hip", "common.h")
+
+
+def source_hash(kernel="gemm_kernel"):
     h = hashlib.sha256()
-    for name in ("gemm.hip", "quant.hip", "common.h"):
+    for name in KERNEL_SOURCES.get(kernel, QUANT_SOURCES):
         with open(os.path.join(ROOT, "block_scaled_fp8_quant_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -126,6 +141,75 @@ def step(fb, layers, events=None):
             timed("gemm", lambda: fb.grouped_gemm(L["qa"], L["sa"], L["qw"], L["sw"], L["off"], y=L["y"]))
         else:
             timed("gemm", lambda: fb.gemm(L["qa"], L["sa"], L["qw"], L["sw"], y=L["y"]))
+
+
+RMS_EPS = 1e-5
+
+
+def build_producers(workload, dev):
+    """Full-size inputs of the two fused producers, resident on the GPU,
+    with preallocated outputs."""
+    import torch
+    import synth
+    x, gamma = synth.producer_inputs(workload, "rmsnorm")
+    gu = synth.producer_inputs(workload, "silu_mul")
+    pow2 = False if workload == "moe" else synth.WORKLOADS[workload].pow2
+    m, k = x.shape
+    mg, f = gu.shape[0], gu.shape[1] // 2
+    P = dict(x=x.to(dev), gamma=gamma.to(dev), gu=gu.to(dev), pow2=pow2, m=m, k=k, mg=mg, f=f,
+             q1=torch.empty(m, k, dtype=torch.uint8, device=dev),
+             s1=torch.empty(m, k // 128, dtype=torch.float32, device=dev),
+             q2=torch.empty(mg, f, dtype=torch.uint8, device=dev),
+             s2=torch.empty(mg, f // 128, dtype=torch.float32, device=dev))
+    del x, gamma, gu
+    return P
+
+
+def time_producers(fb, P, reps):
+    """Average launch time of each fused producer (``reps`` launches replayed
+    from a HIP graph between two HIP events on the launch stream) against
+    the HBM roofline. Algorithmic
+    bytes: bf16 input read once, E4M3 codes and fp32 scales written (plus
+    gamma for RMSNorm). ``bf16_roundtrip_bytes_saved``: the bytes an unfused
+    pipeline moves in addition (the producer's bf16 output written, then
+    read back by the quantisation)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    m, k, mg, f = P["m"], P["k"], P["mg"], P["f"]
+    kernels = (
+        ("rmsnorm_quant_act", [m, k],
+         lambda: fb.rmsnorm_quant_act(P["x"], P["gamma"], RMS_EPS, P["pow2"], q=P["q1"], s=P["s1"]),
+         2 * m * k + 2 * k + m * k + 4 * m * k // 128, 4 * m * k),
+        ("silu_mul_quant_act", [mg, 2 * f],
+         lambda: fb.silu_mul_quant_act(P["gu"], P["pow2"], q=P["q2"], s=P["s2"]),
+         4 * mg * f + mg * f + 4 * mg * f // 128, 4 * mg * f),
+    )
+    out = {}
+    for name, shape, fn, nbytes, saved in kernels:
+        fn()
+        torch.cuda.synchronize()
+        # captured back to back in a HIP graph: at decode sizes a launch from
+        # Python takes longer than the kernel, and the events would time that
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(reps):
+                fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        del graph
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"input_shape": shape, "avg_launch_us": round(ms * 1e3, 2), "bound": "hbm",
+                     "algorithmic_bytes_per_launch": nbytes, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "bf16_roundtrip_bytes_saved": saved}
+    return out
 
 
 def kernel_bytes(layers):
@@ -232,20 +316,30 @@ def summarize_traffic(fetch_csv, write_csv):
                 return v
         raise KeyError(key)
 
-    gemm_key = "gemm_kernel"
     copy_key = "copyBuffer"
-    g_f, g_w = pick(fetch, gemm_key), pick(write, gemm_key)
     c_f, c_w = max(pick(fetch, copy_key)), max(pick(write, copy_key))
     f_scale = COPY_BYTES / (c_f * 1024.0)
     w_scale = COPY_BYTES / (c_w * 1024.0)
+    kernels = {}
+    for key in TRAFFIC_KERNELS:
+        try:
+            kf, kw = pick(fetch, key), pick(write, key)
+        except KeyError:
+            continue
+        kernels[key] = {"source_hash": source_hash(key), "fetch_kib_per_dispatch": statistics.mean(kf),
+                        "write_kib_per_dispatch": statistics.mean(kw), "dispatches": len(kf),
+                        "bytes_per_launch": statistics.mean(kf) * 1024 * f_scale
+                        + statistics.mean(kw) * 1024 * w_scale}
+    g = kernels["gemm_kernel"]
     rec = {
         "source_hash": source_hash(),
-        "gemm_fetch_kib_per_dispatch": statistics.mean(g_f),
-        "gemm_write_kib_per_dispatch": statistics.mean(g_w),
-        "gemm_dispatches": len(g_f),
+        "gemm_fetch_kib_per_dispatch": g["fetch_kib_per_dispatch"],
+        "gemm_write_kib_per_dispatch": g["write_kib_per_dispatch"],
+        "gemm_dispatches": g["dispatches"],
         "copy_fetch_kib": c_f, "copy_write_kib": c_w, "copy_bytes": COPY_BYTES,
         "fetch_scale": f_scale, "write_scale": w_scale,
-        "gemm_bytes_per_launch": statistics.mean(g_f) * 1024 * f_scale + statistics.mean(g_w) * 1024 * w_scale,
+        "gemm_bytes_per_launch": g["bytes_per_launch"],
+        "kernels": kernels,
     }
     return rec
 
@@ -298,12 +392,15 @@ def main():
     gemm_avg_ms = sum(per_kind["gemm"]) / len(per_kind["gemm"])
     gemm_flops_launch = flops_step / len(layers)
     achieved = gemm_flops_launch / (gemm_avg_ms * 1e-3) / 1e12
-    traffic = None
+    traffic, traffic_rec = None, {}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(args.workload)
         if rec and rec.get("source_hash") == source_hash():
             traffic = rec.get("gemm_bytes_per_launch")
+        if rec:
+            traffic_rec = {k: v for k, v in rec.get("kernels", {}).items()
+                           if v.get("source_hash") == source_hash(k)}
     kb = kernel_bytes(layers)
     gemm_alg_bytes = sum(L["m"] * L["k"] + L["n"] * L["k"] * max(L["e"], 1) + 4 * L["m"] * L["k"] // 128
                          + 4 * L["n"] * L["k"] * max(L["e"], 1) // 16384 + 2 * L["m"] * L["n"]
@@ -342,6 +439,16 @@ def main():
         "roofline": roofline(gemm_flops_launch, gemm_alg_bytes, gemm_avg_ms, traffic),
         "breakdown": breakdown,
     }
+    if not args.no_producers:
+        print("bench: timing the fused producers", file=sys.stderr, flush=True)
+        for L in layers:                      # free the step's buffers first
+            L.clear()
+        torch.cuda.empty_cache()
+        out["producers"] = time_producers(fb, build_producers(args.workload, dev), args.producer_reps)
+        for name, key in (("rmsnorm_quant_act", "rmsnorm_quant_act_rows_kernel"),
+                          ("silu_mul_quant_act", "silu_mul_quant_act_kernel")):
+            t = traffic_rec.get(key, {}).get("bytes_per_launch")
+            out["producers"][name]["traffic"] = None if t is None else round(t)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows)

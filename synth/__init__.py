@@ -180,18 +180,29 @@ def gate_up_output(m, f, gen, gate_std=2.0, up_std=1.0):
 
 
 def producer_inputs(workload, which, seed=0, m=None):
-    """Full-size inputs of one fused producer of a dense workload:
+    """Full-size inputs of one fused producer of a workload:
     ``which`` = "rmsnorm": (x [M, hidden], gamma [hidden]), the RMSNorm in
-    front of qkv / gate_up (hidden = the qkv linear's K);
+    front of qkv / gate_up (hidden = the qkv linear's K; for "moe" the
+    token rows [MOE_TOKENS, MOE_HIDDEN] before routing);
     ``which`` = "silu_mul": gu [M, 2F], the gate_up output in front of down
-    (F = the down linear's K)."""
-    wl = WORKLOADS[workload]
-    dims = {nm: k for nm, k, _ in wl.linears}
-    rows = wl.m if m is None else m
+    (F = the down linear's K; for "moe" one row per routed (token, expert)
+    pair, F = MOE_FFN)."""
+    if workload == "moe":
+        hidden, f = MOE_HIDDEN, MOE_FFN
+        rows_x, rows_gu = MOE_TOKENS, MOE_TOKENS * MOE_TOPK
+        frac, scale = 0.0, 1.0
+    else:
+        wl = WORKLOADS[workload]
+        dims = {nm: k for nm, k, _ in wl.linears}
+        hidden, f = dims["qkv"], dims["down"]
+        rows_x = rows_gu = wl.m
+        frac, scale = wl.outlier_frac, wl.outlier_scale
+    if m is not None:
+        rows_x = rows_gu = m
     if which == "rmsnorm":
-        return rmsnorm_inputs(rows, dims["qkv"], _gen(workload, 0x40, seed), wl.outlier_frac, wl.outlier_scale)
+        return rmsnorm_inputs(rows_x, hidden, _gen(workload, 0x40, seed), frac, scale)
     if which == "silu_mul":
-        return gate_up_output(rows, dims["down"], _gen(workload, 0x41, seed))
+        return gate_up_output(rows_gu, f, _gen(workload, 0x41, seed))
     raise ValueError(which)
 
 
