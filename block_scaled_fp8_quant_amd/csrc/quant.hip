@@ -25,6 +25,8 @@
 // either way. Groups with s < 2**-90 use a true division per element. The
 // sign never passes through this arithmetic: magnitudes are encoded and the
 // bf16 sign bits are OR-ed into the codes, which keeps -0 as 0x80.
+#include <algorithm>
+
 #include "common.h"
 
 namespace fp8blk {
@@ -246,21 +248,23 @@ __device__ __forceinline__ float sum_sq8(u32x4 v, float acc) {
 }
 
 // ---------------------------------------------------------------- RMSNorm
-// Workgroups of four waves, each taking kRmsIters consecutive slices of
-// rows. Each row is handled by WPR waves (T = 64*WPR threads; thread t
+// Workgroups of four waves, each taking `iters` (1 to 4) consecutive slices
+// of rows: more rows per workgroup amortise gamma, fewer keep the grid
+// large enough to fill the chip when M is small. Each row is handled by WPR waves (T = 64*WPR threads; thread t
 // holds 16-byte units t, t+T, .. of the row, at most CU of them, so a
 // 16-lane DPP row holds whole 128-wide groups). gamma is loaded once per
 // workgroup and kept in registers; the next row's x is loaded while the
 // current one is normalised and quantized. With WPR > 1 the waves of a row
 // add their partial sums through LDS, in a fixed order (the result does not
 // depend on timing).
-constexpr int kRmsIters = 4;
+constexpr int kRmsMaxIters = 4;
+constexpr int64_t kRmsTargetWGs = 2048;  // 256 CUs x 8 resident four-wave workgroups
 constexpr int kNontemporal = 2;  // cache-policy bits of a buffer load: nt (streamed once)
 
 template <int WPR, int CU>
 __global__ __launch_bounds__(256) void rmsnorm_quant_act_rows_kernel(
     const u32x4* __restrict__ x, const u32x4* __restrict__ gamma, float eps, int64_t M, int64_t K,
-    u32x2* __restrict__ q, float* __restrict__ s, u32x4* __restrict__ y, int pow2) {
+    u32x2* __restrict__ q, float* __restrict__ s, u32x4* __restrict__ y, int pow2, int iters) {
   constexpr int T = 64 * WPR;
   constexpr int RPW = 4 / WPR;  // rows per workgroup and iteration
   // gamma as fp32 when it fits, else packed and widened at each use
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_act_rows_kernel(
   // Branch-free row loads: the resource covers the wave's row (nothing
   // past the last row), so units past the row end, and rows past M, read
   // as zeros. K <= 8192 here: offsets stay far below 2^32.
-  const int64_t first = (int64_t)blockIdx.x * RPW * kRmsIters;
+  const int64_t first = (int64_t)blockIdx.x * RPW * iters;
   auto load_row = [&](u32x4 (&v)[CU], int64_t row) {
     const bool in = row < M;
     const rsrc_t rs = make_rsrc(x + (in ? row : 0) * units, in ? (uint32_t)(K * 2) : 0u);
@@ -301,8 +305,7 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_act_rows_kernel(
   };
   u32x4 cur[CU];
   load_row(cur, first + sub);
-#pragma unroll
-  for (int it = 0; it < kRmsIters; ++it) {
+  for (int it = 0; it < iters; ++it) {
     const int64_t base = first + it * RPW;
     if (base >= M) break;  // uniform over the workgroup
     const int64_t row = base + sub;
@@ -315,8 +318,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_act_rows_kernel(
     // consumed: the wait the compiler places before the first use of
     // `cur` then does not also wait for the prefetch.
     asm volatile("" : "+v"(ss) : : "memory");
-    u32x4 nxt[CU];
-    if (it + 1 < kRmsIters) load_row(nxt, row + RPW);
+    u32x4 nxt[CU] = {};
+    if (it + 1 < iters) load_row(nxt, row + RPW);  // uniform
 
     ss = wave_sum(ss);
     if constexpr (WPR > 1) {
@@ -354,10 +357,8 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_act_rows_kernel(
       quant_store8(w, pow2, live, &q[e], &s[live ? row * kb + u / 16 : 0], (lane & 15) == 0,
                    y ? &y[e] : nullptr);
     }
-    if (it + 1 < kRmsIters) {
 #pragma unroll
-      for (int c = 0; c < CU; ++c) cur[c] = nxt[c];
-    }
+    for (int c = 0; c < CU; ++c) cur[c] = nxt[c];
   }
 }
 
@@ -521,9 +522,11 @@ extern "C" fp8blk_status fp8blk_rmsnorm_quant_act(const uint16_t* x, const uint1
   // waves per row and cached units per lane: 8 to 16 values per lane in
   // registers for K <= 4096, 32 for K <= 8192
   auto launch = [&](auto kernel, int64_t rows_per_iter) {
-    const int64_t rows_per_wg = rows_per_iter * kRmsIters;
+    const int iters = (int)std::max<int64_t>(1, std::min<int64_t>(kRmsMaxIters, M / (rows_per_iter * kRmsTargetWGs)));
+    const int64_t rows_per_wg = rows_per_iter * iters;
     const int64_t wgs = (M + rows_per_wg - 1) / rows_per_wg;
-    hipLaunchKernelGGL(kernel, dim3((uint32_t)wgs), dim3(256), 0, stream, xv, gv, eps, M, K, qv, s, yv, pow2);
+    hipLaunchKernelGGL(kernel, dim3((uint32_t)wgs), dim3(256), 0, stream, xv, gv, eps, M, K, qv, s, yv, pow2,
+                       iters);
   };
   if (units <= 128) {
     launch(rmsnorm_quant_act_rows_kernel<1, 2>, 4);
