@@ -23,6 +23,10 @@ What it computes (sources are web pages about NVIDIA NeMo RL's FP8 recipe):
   «Реальные прирост производительности»): the quantization kernels are
   overhead and their fusion is the way past it; ``producers`` holds the two
   producers fused with the activation quantization (RMSNorm, SiLU * up).
+* Both pages (upppp.jp «KVキャッシュとAttentionにも拡張», greentreeone.com
+  «Реальные прирост производительности»): the KV cache in FP8, with the
+  Q/K/V scales recalibrated after every training step; ``kv_cache`` holds the
+  per-tensor recalibration and the quantize-and-write of K and V.
 
 The pages give no scale formula, no E4M3 variant, no rounding mode and no
 accumulation scheme. The readings taken where they are silent are written
@@ -57,6 +61,12 @@ from .producers import (
     silu_mul_ref,
     round_bf16,
 )
+from .kv_cache import (
+    qkv_amax_ref,
+    kv_scales_ref,
+    kv_quantize_ref,
+    kv_cache_write_ref,
+)
 from .gemm import (
     dequant_act,
     dequant_weight,
@@ -74,4 +84,5 @@ __all__ = [
     "dequant_act", "dequant_weight", "gemm_ref", "gemm_ref_blas",
     "grouped_gemm_ref", "gemm_rows_ref", "tolerance_ok",
     "rmsnorm_ref", "silu_mul_ref", "round_bf16",
+    "qkv_amax_ref", "kv_scales_ref", "kv_quantize_ref", "kv_cache_write_ref",
 ]
