@@ -13,7 +13,9 @@ measured by HIP events on the launch stream inside the timed region.
 workload. ``producers`` (after the timed region) times the two fused
 producer kernels at the workload's shapes -- RMSNorm -> 1x128 quantisation
 of the qkv / gate_up input and SiLU(gate)*up -> quantisation of the down
-input -- each against the HBM roofline.
+input -- each against the HBM roofline; ``kv_cache`` does the same for the
+FP8 KV-cache path (Q/K/V recalibration maxima, quantize-and-write of K and V
+into the cache) at the workload's attention shapes.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -45,7 +47,7 @@ GEMM_KERNELS = ("gemm_kernel", "grouped_gemm_kernel")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # kernels whose counter traffic is recorded (substrings of the kernel names)
 TRAFFIC_KERNELS = ("gemm_kernel", "quant_act_kernel", "quant_weight_kernel", "rmsnorm_quant_act_rows_kernel",
-                   "silu_mul_quant_act_kernel")
+                   "silu_mul_quant_act_kernel", "qkv_amax_kernel", "kv_cache_write_kernel")
 
 
 def parse():
@@ -57,6 +59,7 @@ def parse():
                    choices=["llama8b_prefill", "llama8b_decode", "qwen8b_pow2", "moe"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-producers", action="store_true", help="skip timing the fused producer kernels")
+    p.add_argument("--no-kv", action="store_true", help="skip timing the FP8 KV-cache path")
     p.add_argument("--producer-reps", type=int, default=20)
     p.add_argument("--cpu-sample-rows", type=int, default=8192)
     p.add_argument("--cpu-sample-wrows", type=int, default=1536)
@@ -69,8 +72,10 @@ def parse():
 
 # the sources each recorded kernel is built from: a counter record stays
 # valid while these files are unchanged
-KERNEL_SOURCES = {"gemm_kernel": ("gemm.hip", "common.h")}
-QUANT_SOURCES = ("quant.hip", "common.h")
+KERNEL_SOURCES = {"gemm_kernel": ("gemm.hip", "common.h"),
+                  "qkv_amax_kernel": ("kv_cache.hip", "quant_common.h", "common.h"),
+                  "kv_cache_write_kernel": ("kv_cache.hip", "quant_common.h", "common.h")}
+QUANT_SOURCES = ("quant.hip", "quant_common.h", "common.h")
 
 
 def source_hash(kernel="gemm_kernel"):
@@ -173,8 +178,6 @@ def time_producers(fb, P, reps):
     gamma for RMSNorm). ``bf16_roundtrip_bytes_saved``: the bytes an unfused
     pipeline moves in addition (the producer's bf16 output written, then
     read back by the quantisation)."""
-    import torch
-    stream = torch.cuda.current_stream()
     m, k, mg, f = P["m"], P["k"], P["mg"], P["f"]
     kernels = (
         ("rmsnorm_quant_act", [m, k],
@@ -186,29 +189,77 @@ def time_producers(fb, P, reps):
     )
     out = {}
     for name, shape, fn, nbytes, saved in kernels:
-        fn()
-        torch.cuda.synchronize()
-        # captured back to back in a HIP graph: at decode sizes a launch from
-        # Python takes longer than the kernel, and the events would time that
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for _ in range(reps):
-                fn()
-        graph.replay()
-        torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        graph.replay()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / reps
-        del graph
-        gbs = nbytes / (ms * 1e-3) / 1e9
-        out[name] = {"input_shape": shape, "avg_launch_us": round(ms * 1e3, 2), "bound": "hbm",
-                     "algorithmic_bytes_per_launch": nbytes, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "bf16_roundtrip_bytes_saved": saved}
+        # replayed from a HIP graph: at decode sizes a launch from Python
+        # takes longer than the kernel, and the events would time that
+        out[name] = hbm_entry(shape, graph_time_ms(fn, reps), nbytes)
+        out[name]["bf16_roundtrip_bytes_saved"] = saved
+    return out
+
+
+def build_kv(workload, dev):
+    """The workload's qkv projection output (one layer) and a KV cache of
+    2T slots, resident on the GPU, plus the scales and a slot permutation."""
+    import torch
+    import synth
+    qkv, (hq, hkv, d) = synth.kv_inputs(workload)
+    t = qkv.shape[0]
+    dq = qkv.to(dev)
+    del qkv
+    slot = torch.randperm(2 * t, generator=synth.generator(0x70))[:t].to(dev)
+    return dict(qkv=dq, hq=hq, hkv=hkv, d=d, t=t, slot=slot,
+                amax=torch.empty(3, dtype=torch.float32, device=dev),
+                scale=torch.empty(3, dtype=torch.float32, device=dev),
+                kc=torch.zeros(2 * t, hkv * d, dtype=torch.uint8, device=dev),
+                vc=torch.zeros(2 * t, hkv * d, dtype=torch.uint8, device=dev))
+
+
+def graph_time_ms(fn, reps):
+    """Average time of fn over ``reps`` calls captured in a HIP graph and
+    replayed between two HIP events (fn run once first, outside)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    del graph
+    return a.elapsed_time(b) / reps
+
+
+def hbm_entry(shape, ms, nbytes):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"input_shape": shape, "avg_launch_us": round(ms * 1e3, 2), "bound": "hbm",
+            "algorithmic_bytes_per_launch": nbytes, "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def time_kv(fb, K, reps):
+    """The FP8 KV-cache path at the workload's attention shapes: the Q/K/V
+    recalibration maxima (reset + reduction over the qkv output, read once)
+    and the quantize-and-write of every token's K and V rows (bf16 read,
+    codes written, slot read)."""
+    qkv, hq, hkv, d, t = K["qkv"], K["hq"], K["hkv"], K["d"], K["t"]
+    k = qkv[:, hq * d:(hq + hkv) * d]
+    v = qkv[:, (hq + hkv) * d:]
+    fb.qkv_amax(qkv, hq, hkv, d, amax=K["amax"], reset=True)
+    fb.kv_scales(K["amax"], scale=K["scale"])
+    ms_amax = graph_time_ms(lambda: fb.qkv_amax(qkv, hq, hkv, d, amax=K["amax"], reset=True), reps)
+    ms_write = graph_time_ms(lambda: fb.kv_cache_write(k, v, K["slot"], K["scale"][1:2], K["scale"][2:3],
+                                                        K["kc"], K["vc"]), reps)
+    w = hkv * d
+    out = {"heads": [hq, hkv, d],
+           "qkv_amax": hbm_entry([t, (hq + 2 * hkv) * d], ms_amax, 2 * t * (hq + 2 * hkv) * d + 12),
+           "kv_cache_write": hbm_entry([t, 2, w], ms_write, 2 * t * w * 2 + 2 * t * w + 8 * t + 8)}
     return out
 
 
@@ -449,6 +500,13 @@ def main():
                           ("silu_mul_quant_act", "silu_mul_quant_act_kernel")):
             t = traffic_rec.get(key, {}).get("bytes_per_launch")
             out["producers"][name]["traffic"] = None if t is None else round(t)
+    if not args.no_kv:
+        print("bench: timing the FP8 KV-cache path", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        out["kv_cache"] = time_kv(fb, build_kv(args.workload, dev), args.producer_reps)
+        for name, key in (("qkv_amax", "qkv_amax_kernel"), ("kv_cache_write", "kv_cache_write_kernel")):
+            t = traffic_rec.get(key, {}).get("bytes_per_launch")
+            out["kv_cache"][name]["traffic"] = None if t is None else round(t)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows)

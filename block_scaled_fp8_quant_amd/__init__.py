@@ -9,12 +9,14 @@ CPU fallback: if the library is missing, every call raises.
 Two layers:
   * ``fp8blk_quant_act``, ``fp8blk_quant_weight``, ``fp8blk_gemm``,
     ``fp8blk_grouped_gemm``, ``fp8blk_rmsnorm_quant_act``,
-    ``fp8blk_silu_mul_quant_act``: the C entry points under their own names
+    ``fp8blk_silu_mul_quant_act``, ``fp8blk_qkv_amax``, ``fp8blk_kv_scales``,
+    ``fp8blk_kv_cache_write``: the C entry points under their own names
     (integer device pointers, sizes, stream handle); they raise
     ``Fp8BlkError`` on a non-OK status;
   * ``quant_act``, ``quant_weight``, ``gemm``, ``grouped_gemm``,
-    ``rmsnorm_quant_act``, ``silu_mul_quant_act``: tensor versions that
-    validate shapes and allocate outputs.
+    ``rmsnorm_quant_act``, ``silu_mul_quant_act``, ``qkv_amax``,
+    ``kv_scales``, ``kv_cache_write``: tensor versions that validate shapes
+    and allocate outputs.
 """
 
 import ctypes
@@ -52,6 +54,9 @@ def load():
         "fp8blk_grouped_gemm": [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp],
         "fp8blk_rmsnorm_quant_act": [vp, vp, f32, i64, i64, vp, vp, vp, i32, vp],
         "fp8blk_silu_mul_quant_act": [vp, i64, i64, vp, vp, vp, i32, vp],
+        "fp8blk_qkv_amax": [vp, i64, i64, i64, i64, vp, i32, vp],
+        "fp8blk_kv_scales": [vp, i64, vp, i32, vp],
+        "fp8blk_kv_cache_write": [vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -95,6 +100,19 @@ def fp8blk_rmsnorm_quant_act(x, gamma, eps, M, K, q, s, y, pow2, stream):
 
 def fp8blk_silu_mul_quant_act(gu, M, F, q, s, y, pow2, stream):
     return _call("fp8blk_silu_mul_quant_act", gu, M, F, q, s, y, int(pow2), stream)
+
+
+def fp8blk_qkv_amax(qkv, T, Hq, Hkv, D, amax, reset, stream):
+    return _call("fp8blk_qkv_amax", qkv, T, Hq, Hkv, D, amax, int(reset), stream)
+
+
+def fp8blk_kv_scales(amax, n, scale, pow2, stream):
+    return _call("fp8blk_kv_scales", amax, n, scale, int(pow2), stream)
+
+
+def fp8blk_kv_cache_write(k, v, ld, T, Hkv, D, slot, num_slots, k_scale, v_scale, k_cache, v_cache, stream):
+    return _call("fp8blk_kv_cache_write", k, v, ld, T, Hkv, D, slot, num_slots, k_scale, v_scale,
+                 k_cache, v_cache, stream)
 
 
 # ------------------------------------------------------------ tensor API
@@ -257,6 +275,72 @@ def silu_mul_quant_act(gu, pow2=False, want_y=False, q=None, s=None, y=None):
     return q, s, y
 
 
+def qkv_amax(qkv, hq, hkv, d, amax=None, reset=True):
+    """Running maxima of |Q|, |K|, |V| of a qkv projection output [T,
+    (hq + 2*hkv)*d] (bf16, rows [Q | K | V]) into amax (fp32 [3] on the
+    device; allocated when None). reset=False folds this chunk into the
+    existing maxima. Returns amax."""
+    torch = _torch()
+    if qkv.dim() != 2:
+        raise ValueError("qkv must be 2-D [T, (Hq + 2*Hkv) * D]")
+    t, c = qkv.shape
+    if c != (hq + 2 * hkv) * d:
+        raise ValueError("qkv has %d columns, expected (Hq + 2*Hkv) * D = %d" % (c, (hq + 2 * hkv) * d))
+    _check(qkv, "qkv", torch.bfloat16, (t, c))
+    if amax is None:
+        amax = torch.empty(3, dtype=torch.float32, device=qkv.device)
+        reset = True
+    _check(amax, "amax", torch.float32, (3,), qkv.device)
+    fp8blk_qkv_amax(qkv.data_ptr(), t, hq, hkv, d, amax.data_ptr(), reset, _stream(qkv.device))
+    return amax
+
+
+def kv_scales(amax, pow2=False, scale=None):
+    """Per-tensor scales from maxima (fp32 [n] on the device)."""
+    torch = _torch()
+    if amax.dim() != 1:
+        raise ValueError("amax must be 1-D")
+    n = amax.shape[0]
+    _check(amax, "amax", torch.float32, (n,))
+    scale = torch.empty(n, dtype=torch.float32, device=amax.device) if scale is None else scale
+    _check(scale, "scale", torch.float32, (n,), amax.device)
+    fp8blk_kv_scales(amax.data_ptr(), n, scale.data_ptr(), pow2, _stream(amax.device))
+    return scale
+
+
+def kv_cache_write(k, v, slot, k_scale, v_scale, k_cache, v_cache):
+    """Quantize the K and V rows of T tokens ([T, Hkv*D] bf16, or column
+    slices of a qkv output whose rows are contiguous) with the per-tensor
+    scales (fp32 tensors of one element on the device) and write them to
+    k_cache / v_cache ([num_slots, Hkv, D] or [num_slots, Hkv*D] uint8) at
+    rows slot[t] (int64 [T] on the device; negative = skip)."""
+    torch = _torch()
+    if k.dim() != 2 or v.shape != k.shape:
+        raise ValueError("k and v must be 2-D and of the same shape")
+    t, width = k.shape
+    dev = k.device
+    for name, x in (("k", k), ("v", v)):
+        if x.dtype != torch.bfloat16 or x.device != dev or x.device.type != "cuda":
+            raise TypeError("%s must be bf16 on the same HIP device" % name)
+        if x.stride(1) != 1 or (t > 1 and x.stride(0) != k.stride(0)):
+            raise ValueError("%s rows must be contiguous with a common row stride" % name)
+    ld = k.stride(0) if t > 1 else width
+    num_slots = k_cache.shape[0]
+    hkv_d = k_cache[0].numel() if num_slots else width
+    if hkv_d != width:
+        raise ValueError("cache rows hold %d values, k rows %d" % (hkv_d, width))
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if c.dtype != torch.uint8 or c.device != dev or not c.is_contiguous() or c.shape != k_cache.shape:
+            raise ValueError("%s must be a contiguous uint8 cache like k_cache on the same device" % name)
+    _check(slot, "slot", torch.int64, (t,), dev)
+    _check(k_scale.reshape(-1), "k_scale", torch.float32, (1,), dev)
+    _check(v_scale.reshape(-1), "v_scale", torch.float32, (1,), dev)
+    d = width  # passed as Hkv = 1, D = Hkv*D: the kernel only needs the row width
+    fp8blk_kv_cache_write(k.data_ptr(), v.data_ptr(), ld, t, 1, d, slot.data_ptr(), num_slots,
+                          k_scale.data_ptr(), v_scale.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                          _stream(dev))
+
+
 def linear(x, qw, sw, pow2=False):
     """One W8A8 linear layer: quantise X per 1x128 group, then the
     block-scaled GEMM against pre-quantised weights. Returns Y bf16."""
@@ -268,6 +352,7 @@ __all__ = [
     "BLOCK", "Fp8BlkError", "LIB_PATH", "load",
     "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
     "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act",
+    "fp8blk_qkv_amax", "fp8blk_kv_scales", "fp8blk_kv_cache_write",
     "quant_act", "quant_weight", "gemm", "grouped_gemm", "rmsnorm_quant_act", "silu_mul_quant_act",
-    "linear",
+    "qkv_amax", "kv_scales", "kv_cache_write", "linear",
 ]

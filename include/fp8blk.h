@@ -32,7 +32,8 @@
  * never allocates, frees, copies to or from the host, or synchronises. The
  * library keeps no state: concurrent calls on different streams are safe.
  * Inputs and outputs must not overlap. Identical inputs give bitwise
- * identical outputs (no atomics, fixed reduction order).
+ * identical outputs (sums in a fixed order; the only atomics are the
+ * order-independent maxima of fp8blk_qkv_amax).
  *
  * Errors: every argument check happens before any HIP call, so a rejected
  * call has no effect. Device-side faults surface at the caller's next
@@ -163,6 +164,58 @@ fp8blk_status fp8blk_rmsnorm_quant_act(const uint16_t* x, const uint16_t* gamma,
 fp8blk_status fp8blk_silu_mul_quant_act(const uint16_t* gu, int64_t M, int64_t F,
                                         uint8_t* q, float* s, uint16_t* y, int pow2,
                                         hipStream_t stream);
+
+/*
+ * FP8 KV cache (upppp.jp, «KVキャッシュとAttentionにも拡張»; greentreeone.com,
+ * «Реальные прирост производительности»): the KV cache is stored in FP8, and
+ * because the policy's weights change every training step, the Q, K and V
+ * scales are recomputed from BF16 activations at the end of each step for
+ * the next rollout. The pages give no granularity; this library keeps one
+ * scale per tensor (Q, K, V of one attention layer) with the linear layers'
+ * rule (s = amax/448 in fp32, or the power-of-two option).
+ *
+ * Recalibration, step 1: running maxima of |Q|, |K|, |V| over the chunks of
+ * a calibration batch.
+ *   qkv  [T][(Hq + 2*Hkv)*D] bf16 in: the qkv projection's output, each row
+ *        laid out [Q heads (Hq*D) | K heads (Hkv*D) | V heads (Hkv*D)]
+ *        (16-byte aligned)
+ *   amax [3] fp32 in/out (device): |Q|, |K|, |V| maxima; reset = 1 sets them
+ *        to 0 first (the batch's first chunk), reset = 0 folds this chunk
+ *        into them. The result does not depend on the order of the work
+ *        (max is exact and order-independent).
+ *   T >= 0 (T == 0 only applies reset), Hq, Hkv >= 1, D >= 1 and D % 8 == 0.
+ */
+fp8blk_status fp8blk_qkv_amax(const uint16_t* qkv, int64_t T, int64_t Hq, int64_t Hkv,
+                              int64_t D, float* amax, int reset, hipStream_t stream);
+
+/*
+ * Recalibration, step 2: scale[i] = the scale rule applied to amax[i]
+ * (device arrays of n fp32; amax 0 gives scale 0), pow2 in {0, 1}.
+ */
+fp8blk_status fp8blk_kv_scales(const float* amax, int64_t n, float* scale, int pow2,
+                               hipStream_t stream);
+
+/*
+ * KV-cache quantize-and-write: for each token t with 0 <= slot[t] <
+ * num_slots, k_cache[slot[t]][j] = E4M3(RN_fp32(k[t][j] / k_scale[0])) for
+ * j < Hkv*D, and likewise v into v_cache with v_scale[0]. Codes saturate at
+ * +-448 (tokens may exceed the calibrated range); a zero scale writes +-0.
+ * Tokens with a negative slot (padding) or one past the cache write nothing.
+ *   k, v    [T][ld] bf16 in, the first Hkv*D columns of each row used (so
+ *           they may point into a qkv projection output: ld = (Hq+2Hkv)*D)
+ *           (16-byte aligned, ld % 8 == 0, ld >= Hkv*D)
+ *   slot    [T] int64 (device)
+ *   k_scale, v_scale: one fp32 each (device), e.g. from fp8blk_kv_scales
+ *   k_cache, v_cache [num_slots][Hkv*D] E4M3 codes (16-byte aligned); a
+ *           paged cache whose blocks are [block_size][Hkv][D] is this layout
+ *           with slot = block * block_size + offset
+ *   The slots of one call must be distinct (else which token lands is
+ *   unspecified). T >= 0 (0: no-op), Hkv >= 1, D >= 1 and D % 8 == 0.
+ */
+fp8blk_status fp8blk_kv_cache_write(const uint16_t* k, const uint16_t* v, int64_t ld, int64_t T,
+                                    int64_t Hkv, int64_t D, const int64_t* slot, int64_t num_slots,
+                                    const float* k_scale, const float* v_scale,
+                                    uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code (host memory). */
 const char* fp8blk_status_string(fp8blk_status status);

@@ -206,6 +206,32 @@ def producer_inputs(workload, which, seed=0, m=None):
     raise ValueError(which)
 
 
+# attention heads (query, key/value) and head size of each workload's model
+ATTENTION = {
+    "llama8b_decode": (32, 8, 128),
+    "llama8b_prefill": (32, 8, 128),
+    "qwen8b_pow2": (32, 8, 128),
+    "moe": (32, 4, 128),              # Qwen3-30B-A3B
+}
+
+
+def kv_inputs(workload, seed=0, t=None):
+    """A qkv projection output for the KV-cache path: [T, (Hq + 2*Hkv)*D]
+    bf16, each row [Q | K | V], with Q ~ N(0, 1), K ~ N(0, 2^2) and
+    V ~ N(0, 0.5^2), and 0.5% of the entries x30 (the workload's outlier
+    recipe). T = the workload's token count. Returns (qkv, (Hq, Hkv, D))."""
+    hq, hkv, d = ATTENTION[workload]
+    rows = (MOE_TOKENS if workload == "moe" else WORKLOADS[workload].m) if t is None else t
+    g = _gen(workload, 0x50, seed)
+    parts = [torch.randn(rows, hq * d, generator=g, dtype=torch.float32),
+             torch.randn(rows, hkv * d, generator=g, dtype=torch.float32) * 2.0,
+             torch.randn(rows, hkv * d, generator=g, dtype=torch.float32) * 0.5]
+    x = torch.cat(parts, dim=1)
+    mask = torch.rand(x.shape, generator=g) < 0.005
+    x = torch.where(mask, x * 30.0, x)
+    return x.to(torch.bfloat16), (hq, hkv, d)
+
+
 def generator(tag, seed=0):
     """A seeded generator for ad-hoc test inputs (``tag`` < 256)."""
     g = torch.Generator(device="cpu")

@@ -35,7 +35,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
-        "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_status_string"])
+        "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_qkv_amax", "fp8blk_kv_scales",
+        "fp8blk_kv_cache_write", "fp8blk_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -146,6 +147,55 @@ def test_silu_mul_quant_act_validation(lib):
     assert f(P, 4, 128, P, P + 1, P, 0, NULL) == ALIGN
     assert f(P, 4, 128, P, P, P4, 0, NULL) == ALIGN
     assert f(NULL, 0, 128, NULL, NULL, NULL, 0, NULL) == OK
+
+
+def test_qkv_amax_validation(lib):
+    f = lib.fp8blk_qkv_amax
+    assert f(P, -1, 32, 8, 128, P, 1, NULL) == INVALID
+    assert f(P, 4, 0, 8, 128, P, 1, NULL) == INVALID
+    assert f(P, 4, 32, 0, 128, P, 1, NULL) == INVALID
+    assert f(P, 4, 32, 8, 0, P, 1, NULL) == INVALID
+    assert f(P, 4, 32, 8, 128, P, 2, NULL) == INVALID       # reset flag
+    assert f(P, 4, 32, 8, 100, P, 1, NULL) == SHAPE          # D % 8
+    assert f(NULL, 4, 32, 8, 128, P, 1, NULL) == INVALID
+    assert f(P, 4, 32, 8, 128, NULL, 1, NULL) == INVALID
+    assert f(P4, 4, 32, 8, 128, P, 1, NULL) == ALIGN
+    assert f(P, 4, 32, 8, 128, P + 2, 1, NULL) == ALIGN
+    assert f(NULL, 0, 32, 8, 128, P, 0, NULL) == OK          # T == 0 without reset: nothing to do
+
+
+def test_kv_scales_validation(lib):
+    f = lib.fp8blk_kv_scales
+    assert f(P, -1, P, 0, NULL) == INVALID
+    assert f(P, 3, P, 5, NULL) == INVALID
+    assert f(NULL, 3, P, 0, NULL) == INVALID
+    assert f(P, 3, NULL, 0, NULL) == INVALID
+    assert f(P + 1, 3, P, 0, NULL) == ALIGN
+    assert f(NULL, 0, NULL, 0, NULL) == OK
+
+
+def test_kv_cache_write_validation(lib):
+    f = lib.fp8blk_kv_cache_write
+    ok = [P, P, 1024, 4, 8, 128, P, 16, P, P, P, P, NULL]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["k", "v", "ld", "T", "Hkv", "D", "slot", "slots", "ks", "vs", "kc", "vc", "stream"]
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+    assert call(T=-1) == INVALID
+    assert call(Hkv=0) == INVALID
+    assert call(D=0) == INVALID
+    assert call(slots=-1) == INVALID
+    assert call(ld=1000) == INVALID                           # ld < Hkv*D
+    assert call(D=100, ld=800) == SHAPE                       # D % 8
+    assert call(ld=1028) == SHAPE                             # ld % 8
+    for name in ("k", "v", "slot", "ks", "vs", "kc", "vc"):
+        assert call(**{name: NULL}) == INVALID, name
+    for name, bad in (("k", P4), ("v", P4), ("slot", P4), ("ks", P + 2), ("kc", P4), ("vc", P4)):
+        assert call(**{name: bad}) == ALIGN, name
+    assert call(T=0, k=NULL, v=NULL, slot=NULL) == OK
 
 
 def test_python_entry_points_raise(lib):

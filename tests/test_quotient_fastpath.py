@@ -15,6 +15,7 @@ import pytest
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "csrc", "quotient_fastpath_check.c")
 SCALE_SRC = os.path.join(HERE, "csrc", "scale_fastpath_check.c")
+KV_SRC = os.path.join(HERE, "csrc", "kv_quotient_check.c")
 
 
 @pytest.fixture(scope="module")
@@ -49,3 +50,26 @@ def test_division_free_scale_is_exact(tmp_path):
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stdout
     assert "checked=32639 mismatches=0" in out.stdout
+
+
+@pytest.fixture(scope="module")
+def kv_checker(tmp_path_factory):
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    exe = str(tmp_path_factory.mktemp("kvcheck") / "kvcheck")
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-march=native", "-o", exe, KV_SRC, "-lm"], check=True)
+    return exe
+
+
+def test_calibrated_scale_quotient_codes_are_exact(kv_checker):
+    """The KV-cache write's quotient under arbitrary scales in
+    [2^-90, 2^126]: every bf16 magnitude, the linear rule's scales and
+    2000 random ones, codes equal to the clamped IEEE quotient's."""
+    out = subprocess.run([kv_checker, "2000", "1", "-90"], capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stdout
+    assert "code_mismatches=0" in out.stdout
+
+
+def test_calibrated_scale_lower_bound_is_needed(kv_checker):
+    out = subprocess.run([kv_checker, "100", "2", "-126"], capture_output=True, text=True, timeout=300).stdout
+    assert "code_mismatches=0" not in out
