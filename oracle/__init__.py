@@ -27,6 +27,9 @@ What it computes (sources are web pages about NVIDIA NeMo RL's FP8 recipe):
   «Реальные прирост производительности»): the KV cache in FP8, with the
   Q/K/V scales recalibrated after every training step; ``kv_cache`` holds the
   per-tensor recalibration and the quantize-and-write of K and V.
+* FP8 training (upppp.jp «FP8適用の難所：数値のズレ問題», greentreeone.com
+  «Технический прорыв»): ``backward`` holds the dgrad and wgrad GEMMs under
+  the same quantization rule along each GEMM's contraction dimension.
 
 The pages give no scale formula, no E4M3 variant, no rounding mode and no
 accumulation scheme. The readings taken where they are silent are written
@@ -67,6 +70,13 @@ from .kv_cache import (
     kv_quantize_ref,
     kv_cache_write_ref,
 )
+from .backward import (
+    quant_act_t_ref,
+    quant_weight_t_ref,
+    gemm_rowscaled_ref,
+    dgrad_ref,
+    wgrad_ref,
+)
 from .gemm import (
     dequant_act,
     dequant_weight,
@@ -85,4 +95,5 @@ __all__ = [
     "grouped_gemm_ref", "gemm_rows_ref", "tolerance_ok",
     "rmsnorm_ref", "silu_mul_ref", "round_bf16",
     "qkv_amax_ref", "kv_scales_ref", "kv_quantize_ref", "kv_cache_write_ref",
+    "quant_act_t_ref", "quant_weight_t_ref", "gemm_rowscaled_ref", "dgrad_ref", "wgrad_ref",
 ]
