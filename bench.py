@@ -15,7 +15,9 @@ producer kernels at the workload's shapes -- RMSNorm -> 1x128 quantisation
 of the qkv / gate_up input and SiLU(gate)*up -> quantisation of the down
 input -- each against the HBM roofline; ``kv_cache`` does the same for the
 FP8 KV-cache path (Q/K/V recalibration maxima, quantize-and-write of K and V
-into the cache) at the workload's attention shapes.
+into the cache) at the workload's attention shapes; ``backward`` times the
+dgrad and wgrad GEMMs of every linear (and their transposing quantizers)
+against the same rooflines.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -60,6 +62,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-producers", action="store_true", help="skip timing the fused producer kernels")
     p.add_argument("--no-kv", action="store_true", help="skip timing the FP8 KV-cache path")
+    p.add_argument("--no-backward", action="store_true", help="skip timing the backward GEMMs")
+    p.add_argument("--backward-reps", type=int, default=3)
     p.add_argument("--producer-reps", type=int, default=20)
     p.add_argument("--cpu-sample-rows", type=int, default=8192)
     p.add_argument("--cpu-sample-wrows", type=int, default=1536)
@@ -260,6 +264,62 @@ def time_kv(fb, K, reps):
     out = {"heads": [hq, hkv, d],
            "qkv_amax": hbm_entry([t, (hq + 2 * hkv) * d], ms_amax, 2 * t * (hq + 2 * hkv) * d + 12),
            "kv_cache_write": hbm_entry([t, 2, w], ms_write, 2 * t * w * 2 + 2 * t * w + 8 * t + 8)}
+    return out
+
+
+def time_backward(fb, workload, dev, reps):
+    """The backward GEMMs of each linear of a dense workload at its shapes:
+    dgrad dX = dY W (quant_act of dY, quant_weight_t of W, gemm) and wgrad
+    dW = dY^T X (quant_act_t of dY and X, gemm_rowscaled). Each kernel is
+    timed from HIP-graph replays; the two GEMMs get roofline entries like
+    the forward GEMM's (FLOPs per launch averaged over the linears), the
+    transposing quantizers HBM entries."""
+    import torch
+    import synth
+    wl = synth.WORKLOADS[workload]
+    pow2 = wl.pow2
+    sums = {"dgrad": [0.0, 0.0, 0.0], "wgrad": [0.0, 0.0, 0.0], "quant_act_t": [0.0, 0.0], "quant_weight_t": [0.0, 0.0]}
+    per_layer = {}
+    for li, (name, k, n) in enumerate(wl.linears):
+        dy, x, w = synth.backward_inputs(workload, li)
+        m = x.shape[0]
+        dy, x, w = dy.to(dev), x.to(dev), w.to(dev)
+        qa, sa = fb.quant_act(dy, pow2)
+        qwt, swt = fb.quant_weight_t(w, pow2)
+        dx = torch.empty(m, k, dtype=torch.bfloat16, device=dev)
+        qat, sat = fb.quant_act_t(dy, pow2)
+        qbt, sbt = fb.quant_act_t(x, pow2)
+        dw = torch.empty(n, k, dtype=torch.bfloat16, device=dev)
+        t_dgrad = graph_time_ms(lambda: fb.gemm(qa, sa, qwt, swt, y=dx), reps)
+        t_wgrad = graph_time_ms(lambda: fb.gemm_rowscaled(qat, sat, qbt, sbt, y=dw), reps)
+        t_qat = graph_time_ms(lambda: (fb.quant_act_t(dy, pow2, qt=qat, st=sat),
+                                       fb.quant_act_t(x, pow2, qt=qbt, st=sbt)), reps)
+        t_qwt = graph_time_ms(lambda: fb.quant_weight_t(w, pow2, qt=qwt, st=swt), reps)
+        flops = 2.0 * m * n * k
+        sums["dgrad"][0] += t_dgrad
+        sums["dgrad"][1] += flops
+        sums["dgrad"][2] += m * n + n * k + 4 * m * n // 128 + 4 * n * k // 16384 + 2 * m * k
+        sums["wgrad"][0] += t_wgrad
+        sums["wgrad"][1] += flops
+        sums["wgrad"][2] += n * m + k * m + 4 * (n + k) * m // 128 + 2 * n * k
+        sums["quant_act_t"][0] += t_qat
+        sums["quant_act_t"][1] += (m * n + m * k) * (3 + 4 / 128)
+        sums["quant_weight_t"][0] += t_qwt
+        sums["quant_weight_t"][1] += 3 * n * k + 4 * n * k // 16384
+        per_layer[name] = {"dgrad_us": round(t_dgrad * 1e3, 1), "wgrad_us": round(t_wgrad * 1e3, 1)}
+        del dy, x, w, qa, sa, qwt, swt, dx, qat, sat, qbt, sbt, dw
+        torch.cuda.empty_cache()
+    L = len(wl.linears)
+    out = {}
+    for kind in ("dgrad", "wgrad"):
+        ms, flops, nbytes = sums[kind]
+        out[kind] = roofline(flops / L, nbytes / L, ms / L, None)
+        out[kind]["tflops_all_linears"] = round(flops / (ms * 1e-3) / 1e12, 1)
+    for kind in ("quant_act_t", "quant_weight_t"):
+        ms, nbytes = sums[kind]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[kind] = {"gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4), "ms_all_linears": round(ms, 4)}
+    out["per_layer"] = per_layer
     return out
 
 
@@ -500,6 +560,10 @@ def main():
                           ("silu_mul_quant_act", "silu_mul_quant_act_kernel")):
             t = traffic_rec.get(key, {}).get("bytes_per_launch")
             out["producers"][name]["traffic"] = None if t is None else round(t)
+    if not args.no_backward and args.workload != "moe":
+        print("bench: timing the backward GEMMs", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        out["backward"] = time_backward(fb, args.workload, dev, args.backward_reps)
     if not args.no_kv:
         print("bench: timing the FP8 KV-cache path", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()

@@ -10,13 +10,16 @@ Two layers:
   * ``fp8blk_quant_act``, ``fp8blk_quant_weight``, ``fp8blk_gemm``,
     ``fp8blk_grouped_gemm``, ``fp8blk_rmsnorm_quant_act``,
     ``fp8blk_silu_mul_quant_act``, ``fp8blk_qkv_amax``, ``fp8blk_kv_scales``,
-    ``fp8blk_kv_cache_write``: the C entry points under their own names
+    ``fp8blk_kv_cache_write``, ``fp8blk_quant_act_t``,
+    ``fp8blk_quant_weight_t``, ``fp8blk_gemm_rowscaled``: the C entry points
+    under their own names
     (integer device pointers, sizes, stream handle); they raise
     ``Fp8BlkError`` on a non-OK status;
   * ``quant_act``, ``quant_weight``, ``gemm``, ``grouped_gemm``,
     ``rmsnorm_quant_act``, ``silu_mul_quant_act``, ``qkv_amax``,
-    ``kv_scales``, ``kv_cache_write``: tensor versions that validate shapes
-    and allocate outputs.
+    ``kv_scales``, ``kv_cache_write``, ``quant_act_t``, ``quant_weight_t``,
+    ``gemm_rowscaled`` (and ``dgrad``, ``wgrad`` built from them): tensor
+    versions that validate shapes and allocate outputs.
 """
 
 import ctypes
@@ -55,6 +58,9 @@ def load():
         "fp8blk_rmsnorm_quant_act": [vp, vp, f32, i64, i64, vp, vp, vp, i32, vp],
         "fp8blk_silu_mul_quant_act": [vp, i64, i64, vp, vp, vp, i32, vp],
         "fp8blk_qkv_amax": [vp, i64, i64, i64, i64, vp, i32, vp],
+        "fp8blk_quant_act_t": [vp, i64, i64, vp, vp, i32, vp],
+        "fp8blk_quant_weight_t": [vp, i64, i64, vp, vp, i32, vp],
+        "fp8blk_gemm_rowscaled": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8blk_kv_scales": [vp, i64, vp, i32, vp],
         "fp8blk_kv_cache_write": [vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp],
     }
@@ -100,6 +106,18 @@ def fp8blk_rmsnorm_quant_act(x, gamma, eps, M, K, q, s, y, pow2, stream):
 
 def fp8blk_silu_mul_quant_act(gu, M, F, q, s, y, pow2, stream):
     return _call("fp8blk_silu_mul_quant_act", gu, M, F, q, s, y, int(pow2), stream)
+
+
+def fp8blk_quant_act_t(x, M, K, qt, st, pow2, stream):
+    return _call("fp8blk_quant_act_t", x, M, K, qt, st, int(pow2), stream)
+
+
+def fp8blk_quant_weight_t(w, N, K, qt, st, pow2, stream):
+    return _call("fp8blk_quant_weight_t", w, N, K, qt, st, int(pow2), stream)
+
+
+def fp8blk_gemm_rowscaled(qa, sa, qb, sb, M, N, K, y, stream):
+    return _call("fp8blk_gemm_rowscaled", qa, sa, qb, sb, M, N, K, y, stream)
 
 
 def fp8blk_qkv_amax(qkv, T, Hq, Hkv, D, amax, reset, stream):
@@ -275,6 +293,80 @@ def silu_mul_quant_act(gu, pow2=False, want_y=False, q=None, s=None, y=None):
     return q, s, y
 
 
+def quant_act_t(x, pow2=False, qt=None, st=None):
+    """128x1 groups of bf16 X[M, K] (M % 128 == 0), written transposed ->
+    (Q^T uint8 [K, M], S^T fp32 [K, M/128])."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    m, k = x.shape
+    _check(x, "x", torch.bfloat16, (m, k))
+    if m % BLOCK or k % 64:
+        raise ValueError("M must be a multiple of 128 and K of 64")
+    qt = torch.empty((k, m), dtype=torch.uint8, device=x.device) if qt is None else qt
+    st = torch.empty((k, m // BLOCK), dtype=torch.float32, device=x.device) if st is None else st
+    _check(qt, "qt", torch.uint8, (k, m), x.device)
+    _check(st, "st", torch.float32, (k, m // BLOCK), x.device)
+    fp8blk_quant_act_t(x.data_ptr(), m, k, qt.data_ptr(), st.data_ptr(), pow2, _stream(x.device))
+    return qt, st
+
+
+def quant_weight_t(w, pow2=False, qt=None, st=None):
+    """128x128 block quantisation of bf16 W[N, K], written transposed ->
+    (QW^T uint8 [K, N], SW^T fp32 [K/128, N/128])."""
+    torch = _torch()
+    if w.dim() != 2:
+        raise ValueError("w must be 2-D [N, K]")
+    n, k = w.shape
+    _check(w, "w", torch.bfloat16, (n, k))
+    if n % BLOCK or k % BLOCK:
+        raise ValueError("N and K must be multiples of 128")
+    qt = torch.empty((k, n), dtype=torch.uint8, device=w.device) if qt is None else qt
+    st = torch.empty((k // BLOCK, n // BLOCK), dtype=torch.float32, device=w.device) if st is None else st
+    _check(qt, "qt", torch.uint8, (k, n), w.device)
+    _check(st, "st", torch.float32, (k // BLOCK, n // BLOCK), w.device)
+    fp8blk_quant_weight_t(w.data_ptr(), n, k, qt.data_ptr(), st.data_ptr(), pow2, _stream(w.device))
+    return qt, st
+
+
+def gemm_rowscaled(qa, sa, qb, sb, y=None):
+    """Y[M, N] bf16 = sum_b SA[m, b] SB[n, b] (QA QB^T over K block b):
+    per-row scales on both operands."""
+    torch = _torch()
+    if qa.dim() != 2 or qb.dim() != 2:
+        raise ValueError("qa must be [M, K] and qb [N, K]")
+    m, k = qa.shape
+    n = qb.shape[0]
+    if k % BLOCK or n % BLOCK:
+        raise ValueError("N and K must be multiples of 128")
+    dev = qa.device
+    _check(qa, "qa", torch.uint8, (m, k))
+    _check(sa, "sa", torch.float32, (m, k // BLOCK), dev)
+    _check(qb, "qb", torch.uint8, (n, k), dev)
+    _check(sb, "sb", torch.float32, (n, k // BLOCK), dev)
+    y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if y is None else y
+    _check(y, "y", torch.bfloat16, (m, n), dev)
+    fp8blk_gemm_rowscaled(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(), m, n, k, y.data_ptr(),
+                          _stream(dev))
+    return y
+
+
+def dgrad(dy, qwt, swt, pow2=False):
+    """dX = dY W for Y = X W^T: dY [M, N] bf16 quantised in 1x128 groups,
+    times the transposed weight codes (qwt [K, N], swt [K/128, N/128] from
+    quant_weight_t). Returns dX bf16 [M, K]."""
+    qa, sa = quant_act(dy, pow2)
+    return gemm(qa, sa, qwt, swt)
+
+
+def wgrad(dy, x, pow2=False):
+    """dW = dY^T X for Y = X W^T: dY [M, N] and X [M, K] (bf16, M % 128 ==
+    0) quantised in 128x1 groups. Returns dW bf16 [N, K]."""
+    qa, sa = quant_act_t(dy, pow2)
+    qb, sb = quant_act_t(x, pow2)
+    return gemm_rowscaled(qa, sa, qb, sb)
+
+
 def qkv_amax(qkv, hq, hkv, d, amax=None, reset=True):
     """Running maxima of |Q|, |K|, |V| of a qkv projection output [T,
     (hq + 2*hkv)*d] (bf16, rows [Q | K | V]) into amax (fp32 [3] on the
@@ -353,6 +445,8 @@ __all__ = [
     "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
     "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act",
     "fp8blk_qkv_amax", "fp8blk_kv_scales", "fp8blk_kv_cache_write",
+    "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
     "quant_act", "quant_weight", "gemm", "grouped_gemm", "rmsnorm_quant_act", "silu_mul_quant_act",
-    "qkv_amax", "kv_scales", "kv_cache_write", "linear",
+    "qkv_amax", "kv_scales", "kv_cache_write", "quant_act_t", "quant_weight_t", "gemm_rowscaled",
+    "dgrad", "wgrad", "linear",
 ]

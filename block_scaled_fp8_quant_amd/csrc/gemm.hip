@@ -56,9 +56,14 @@ constexpr int BK = kBlock;  // K step = one scale block
 // 32-bit lane offsets into a tile's rows: 256 * K must stay below 2^32
 constexpr int64_t kMaxK = int64_t(1) << 24;
 
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 2>
+// RB_ = false: B carries one scale per 128x128 block (weights), SW[N/128][KB].
+// RB_ = true: B carries one scale per row and K block, SB[N][KB] (the wgrad
+// operands: 128x1 groups on both sides), so the fold needs a scale per
+// output column.
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 2, bool RB_ = false>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_;
+  static constexpr bool RB = RB_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
@@ -67,11 +72,13 @@ struct Tile {
   static constexpr int A_WIN = BM / 8 / WAVES, B_WIN = BN / 8 / WAVES;
   static_assert(A_WIN * 8 * WAVES == BM && B_WIN * 8 * WAVES == BN, "rows per wave");
   static_assert(BM % 64 == 0 && BM / 64 < WAVES, "row scales: one dword window per wave, one wave left for the weight scales");
+  static_assert(!RB || (BN % 64 == 0 && BM / 64 + BN / 64 <= WAVES), "RB: one dword window per wave for A and B rows");
   static_assert(kBlock % WN == 0, "a wave's columns lie in one weight block");
   static_assert(WM % 16 == 0 && WN % 16 == 0, "16x16 MFMA tiles");
   static constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK;
   // A tile, B tile, BM row scales, then a 256-byte window of weight scales
-  static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4 + 256;
+  // (RB: BN row scales of B)
+  static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4 + (RB ? BN * 4 : 256);
   static constexpr int LDS = STAGES * STAGE + 4 * WAVES;  // stages, then one scale verdict per wave
   // direct loads one wave issues per stage: its A and B windows and one scale window
   static constexpr int LOADS_PER_STAGE = A_WIN + B_WIN + 1;
@@ -96,7 +103,11 @@ struct Tile {
 using Big = Tile<256, 256, 2, 4>;
 using Mid = Tile<128, 128, 2, 2, FP8BLK_MID_STAGES>;
 using Small = Tile<64, 64, 1, 4, FP8BLK_SMALL_STAGES>;
+using BigRB = Tile<256, 256, 2, 4, 2, true>;
+using MidRB = Tile<128, 128, 2, 2, FP8BLK_MID_STAGES, true>;
+using SmallRB = Tile<64, 64, 1, 4, FP8BLK_SMALL_STAGES, true>;
 static_assert(Big::LDS <= 160 * 1024 && Mid::LDS <= 160 * 1024 && Small::LDS <= 160 * 1024, "LDS budget");
+static_assert(BigRB::LDS <= 160 * 1024 && MidRB::LDS <= 160 * 1024 && SmallRB::LDS <= 160 * 1024, "LDS budget");
 
 // 16-byte chunk c of LDS row r is stored at chunk c ^ key(r), so the 16
 // rows that one operand read touches (same logical chunk) are spread over
@@ -196,7 +207,10 @@ __device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp
 #pragma unroll
   for (int i = 0; i < C::B_WIN; ++i)
     dma16(b, lp.b_off[i], koff, stage + C::A_BYTES + (wave * C::B_WIN + i) * 1024);
-  const int window = wave < C::BM / 64 ? wave : C::BM / 64;
+  // RB: waves past the B windows repeat the last one (same rows, same data)
+  const int window = wave < C::BM / 64 ? wave
+                     : C::RB ? C::BM / 64 + (wave - C::BM / 64 < C::BN / 64 ? wave - C::BM / 64 : C::BN / 64 - 1)
+                             : C::BM / 64;
   dma4(s, lp.s_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + window * 256);
 }
 
@@ -207,6 +221,16 @@ __device__ __forceinline__ void fold_row(v4f (&acc)[C::TN], const v4f (&p)[C::TN
   for (int j = 0; j < C::TN; ++j)
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[j][r], sc, acc[j][r]);
+}
+
+// RB: acc[j][r] += p[j][r] * sa * sb[j][r], sb = the scales of the lane's
+// output columns 16j + 4g + r.
+template <class C>
+__device__ __forceinline__ void fold_row_rb(v4f (&acc)[C::TN], const v4f (&p)[C::TN], float sa, const v4f (&sb)[C::TN]) {
+#pragma unroll
+  for (int j = 0; j < C::TN; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[j][r] = __builtin_fmaf(p[j][r] * sa, sb[j][r], acc[j][r]);
 }
 
 template <class C>
@@ -323,6 +347,12 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
   v8i wfr[C::TN], afr[2];
   v4f srow[C::TM / 4];
   float swv = 0.f;
+  // RB: B-row scales of the lane's output columns. They are replaced by the
+  // new block's right after row 0's fold, the last fold of the previous
+  // block (its last two rows fold in (1) and at row 0).
+  v4f sbn[C::RB ? C::TN : 1];
+#pragma unroll
+  for (int j = 0; j < (C::RB ? C::TN : 1); ++j) sbn[j] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int j = 0; j < C::TN; ++j) wfr[j] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
   afr[0] = afr[1] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
@@ -345,7 +375,7 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
       const float* sc = reinterpret_cast<const float*>(sA + C::A_BYTES + C::B_BYTES);
 #pragma unroll
       for (int q = 0; q < C::TM / 4; ++q) srow[q] = *reinterpret_cast<const v4f*>(sc + wm + c16 * C::TM + 4 * q);
-      const float swv_new = sc[C::BM + wn / kBlock];
+      const float swv_new = C::RB ? 0.f : sc[C::BM + wn / kBlock];
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         if constexpr (POW2)
@@ -357,7 +387,10 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
         wfr[j] = read_frag(sA + C::A_BYTES, wn + 16 * j + c16, g);
       }
       if constexpr (!POW2) {
-        fold_row<C>(acc[C::TM - 2], pp, sc_prev);
+        if constexpr (C::RB)
+          fold_row_rb<C>(acc[C::TM - 2], pp, sc_prev, sbn);
+        else
+          fold_row<C>(acc[C::TM - 2], pp, sc_prev);
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
         sc_prev = sc_last;
@@ -365,8 +398,7 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
       swv = swv_new;
       ew = e8m0_of(swv);
       // first activation fragment and the scales (TM / 4 + 3 reads)
-      if (C::TM == 8) __builtin_amdgcn_sched_group_barrier(0x100, 5, 0);
-      if (C::TM == 4) __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, C::TM / 4 + 2 + (C::RB ? 0 : 1), 0);
 #pragma unroll
       for (int j = 0; j < C::TN; ++j) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // tail MFMA j
@@ -387,15 +419,27 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
       } else {
         v4f p[C::TN];
         mfma_row<C>(p, wfr, afr[i & 1]);
-        fold_row<C>(acc[i == 0 ? C::TM - 1 : i - 1], pp, sc_prev);
+        if constexpr (C::RB) {
+          fold_row_rb<C>(acc[i == 0 ? C::TM - 1 : i - 1], pp, sc_prev, sbn);
+          if (i == 0) {  // the previous block's folds are done: this block's B scales
+            const float* sc = reinterpret_cast<const float*>(sA + C::A_BYTES + C::B_BYTES);
+#pragma unroll
+            for (int j = 0; j < C::TN; ++j) sbn[j] = *reinterpret_cast<const v4f*>(sc + C::BM + wn + 16 * j + 4 * g);
+          }
+        } else {
+          fold_row<C>(acc[i == 0 ? C::TM - 1 : i - 1], pp, sc_prev);
+        }
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) pp[j] = p[j];
-        sc_prev = srow[i / 4][i % 4] * swv;
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next fragment reads
+        sc_prev = C::RB ? srow[i / 4][i % 4] : srow[i / 4][i % 4] * swv;  // RB: the A scale alone
+        if (C::RB && i == 0)
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 + C::TN, 0);  // next fragment and the B scales
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // next fragment reads
 #pragma unroll
         for (int j = 0; j < C::TN; ++j) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // four fold FMAs
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, C::RB ? 8 : 4, 0);   // its quad's fold
         }
       }
       sched_fence();
@@ -403,7 +447,7 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
     if constexpr (POW2)
       ea_last = e8m0_of(srow[(C::TM - 1) / 4][(C::TM - 1) % 4]);
     else
-      sc_last = srow[(C::TM - 1) / 4][(C::TM - 1) % 4] * swv;
+      sc_last = C::RB ? srow[(C::TM - 1) / 4][(C::TM - 1) % 4] : srow[(C::TM - 1) / 4][(C::TM - 1) % 4] * swv;
     wait_vm<LPS * (S - 2)>();  // (3) block kb+1 has landed
     lds_barrier();
     issue_stage<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
@@ -418,8 +462,13 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
   } else {
     v4f p[C::TN];
     mfma_row<C>(p, wfr, afr[(C::TM - 1) & 1]);
-    fold_row<C>(acc[C::TM - 2], pp, sc_prev);
-    fold_row<C>(acc[C::TM - 1], p, sc_last);
+    if constexpr (C::RB) {
+      fold_row_rb<C>(acc[C::TM - 2], pp, sc_prev, sbn);
+      fold_row_rb<C>(acc[C::TM - 1], p, sc_last, sbn);
+    } else {
+      fold_row<C>(acc[C::TM - 2], pp, sc_prev);
+      fold_row<C>(acc[C::TM - 1], p, sc_last);
+    }
   }
   wait_vm0();  // no load may still be writing LDS when the workgroup ends
 }
@@ -472,6 +521,12 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     lp.s = sa + m0 * KB;
     lp.s_len = clamp_len((M - m0) * KB * 4);
     lp.s_off = (uint32_t)row * (uint32_t)(KB * 4);
+  } else if constexpr (C::RB) {
+    // B-row scales of tile rows bw*64 + lane, in natural order (sw is SB[N][KB])
+    const int bw = wave - C::BM / 64 < C::BN / 64 ? wave - C::BM / 64 : C::BN / 64 - 1;
+    lp.s = sw + n0 * KB;
+    lp.s_len = clamp_len((N - n0) * KB * 4);
+    lp.s_off = (uint32_t)(bw * 64 + lane) * (uint32_t)(KB * 4);
   } else {  // weight scales of column blocks n0/128 + lane (lanes past the tile's blocks repeat)
     constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;  // a 64-wide tile lies in one block
     lp.s = sw + (n0 / kBlock) * KB;
@@ -492,22 +547,31 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
   // flight while one is computed. The loop body is branch-free: past the
   // last block the refill uses resources of length zero (out-of-range loads
   // fetch nothing) and the fragments read ahead are not used.
-  ScaleScan<C> scan;
-  scan_begin<C>(scan, sa, sw, M, N, m0, n0, wave, KB, lane);
+  if constexpr (C::RB) {
+    // per-row scales on both operands: always the fold path
 #pragma unroll
-  for (int b = 0; b < C::STAGES; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
-  uint32_t* verdict = reinterpret_cast<uint32_t*>(smem_generic + C::STAGES * C::STAGE);
-  const bool ok = scan_end<C>(scan, lane);
-  if (lane == 0) verdict[wave] = ok ? 1u : 0u;
-  wait_vm<C::LOADS_PER_STAGE * (C::STAGES - 1)>();  // block 0 has landed (the scan's later loads too)
-  lds_barrier();
-  bool pow2 = true;
-#pragma unroll
-  for (int w = 0; w < C::WAVES; ++w) pow2 = pow2 & (verdict[w] != 0u);
-  if (pow2)
-    k_loop<C, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
-  else
+    for (int b = 0; b < C::STAGES; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
+    wait_vm<C::LOADS_PER_STAGE * (C::STAGES - 1)>();  // block 0 has landed
+    lds_barrier();
     k_loop<C, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+  } else {
+    ScaleScan<C> scan;
+    scan_begin<C>(scan, sa, sw, M, N, m0, n0, wave, KB, lane);
+#pragma unroll
+    for (int b = 0; b < C::STAGES; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
+    uint32_t* verdict = reinterpret_cast<uint32_t*>(smem_generic + C::STAGES * C::STAGE);
+    const bool ok = scan_end<C>(scan, lane);
+    if (lane == 0) verdict[wave] = ok ? 1u : 0u;
+    wait_vm<C::LOADS_PER_STAGE * (C::STAGES - 1)>();  // block 0 has landed (the scan's later loads too)
+    lds_barrier();
+    bool pow2 = true;
+#pragma unroll
+    for (int w = 0; w < C::WAVES; ++w) pow2 = pow2 & (verdict[w] != 0u);
+    if (pow2)
+      k_loop<C, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+    else
+      k_loop<C, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+  }
 
   if (!cols_valid) return;
   // lane holds Y[m0 + wm + 16i + l%16][n0 + wn + 16j + 4*(l/16) + r], r < 4
@@ -670,6 +734,16 @@ extern "C" fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa, const u
 
 // Expert groups: 128-row tiles when the average expert has at least 128
 // rows, else 64-row tiles (less padding in partly filled tiles).
+extern "C" fp8blk_status fp8blk_gemm_rowscaled(const uint8_t* qa, const float* sa, const uint8_t* qb,
+                                               const float* sb, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                                               hipStream_t stream) {
+  const fp8blk_status st = check_gemm_args(qa, sa, qb, sb, M, N, K, y);
+  if (st != FP8BLK_OK || M == 0) return st;
+  if (tiles_of<BigRB>(M, N) >= kCUs) return launch_gemm<BigRB>(qa, sa, qb, sb, M, N, K, y, stream);
+  if (tiles_of<MidRB>(M, N) >= 2 * kCUs) return launch_gemm<MidRB>(qa, sa, qb, sb, M, N, K, y, stream);
+  return launch_gemm<SmallRB>(qa, sa, qb, sb, M, N, K, y, stream);
+}
+
 extern "C" fp8blk_status fp8blk_grouped_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw,
                                              const float* sw, const int32_t* offsets, int64_t E,
                                              int64_t total_M, int64_t N, int64_t K, uint16_t* y,

@@ -93,6 +93,149 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const u32x4* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Transposed quantization for the backward GEMMs (FP8 training: upppp.jp
+// «FP8適用の難所：数値のズレ問題», greentreeone.com «Технический прорыв»).
+// Each backward GEMM reads its operands along its contraction dimension:
+// wgrad contracts over the tokens, so dY and X are quantized in 128x1 groups
+// (128 consecutive rows of one column) and written transposed; dgrad reads W
+// along N, so the weight's 128x128 blocks are written transposed.
+
+// X [M][K] -> Q^T [K][M], S^T [K][M/128]: one workgroup per 128 x 64 tile
+// (rows m0.., columns k0..). Thread t loads rows 2q, 2q+1 (q = t/8, +32)
+// of 16-byte column chunk t%8 and stores each column's two values as one
+// dword of LDS row k (a column of the tile) at dword q: 64 LDS rows of 128
+// values, row stride 65 dwords, so both these writes and the reads below
+// hit 64 distinct banks. Then thread t = 4k + p takes rows 32p..32p+31 of
+// column k: the four lanes of a quad hold one 128-row group, reduced by
+// two DPP steps, and store its 128 codes as one contiguous 128-byte run.
+constexpr int kTStride = 65;  // dwords per LDS row
+
+__global__ __launch_bounds__(256) void quant_act_t_kernel(const u32x4* __restrict__ x, int64_t M, int64_t K,
+                                                          u32x4* __restrict__ qt, float* __restrict__ st,
+                                                          int pow2) {
+  __shared__ uint32_t lds[64 * kTStride];
+  const int t = threadIdx.x;
+  const int64_t k_tiles = K / 64;
+  const int64_t m0 = (int64_t)(blockIdx.x / k_tiles) * 128, k0 = (int64_t)(blockIdx.x % k_tiles) * 64;
+  const int c = t & 7, q = t >> 3;
+  const int64_t row_units = K / 8;
+  u32x4 v[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      v[2 * i + h] = __builtin_nontemporal_load(&x[(m0 + 2 * (q + 32 * i) + h) * row_units + k0 / 8 + c]);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t e0[4] = {v[2 * i].x, v[2 * i].y, v[2 * i].z, v[2 * i].w};      // row 2q'
+    const uint32_t e1[4] = {v[2 * i + 1].x, v[2 * i + 1].y, v[2 * i + 1].z, v[2 * i + 1].w};  // row 2q'+1
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      // column 8c + 2j (low halves) and 8c + 2j + 1 (high halves)
+      lds[(8 * c + 2 * j) * kTStride + q + 32 * i] = __builtin_amdgcn_perm(e1[j], e0[j], 0x05040100u);
+      lds[(8 * c + 2 * j + 1) * kTStride + q + 32 * i] = __builtin_amdgcn_perm(e1[j], e0[j], 0x07060302u);
+    }
+  }
+  __syncthreads();
+  const int k = t >> 2, p = t & 3;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) w[i] = lds[k * kTStride + 16 * p + i];  // rows 32p + 2i, +1
+  uint32_t mb = 0;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) mb = max(mb, amax8_bits(&w[4 * g]));
+  mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF, true));
+  mb = max(mb, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0x4E, 0xF, 0xF, true));
+  const float sc = group_scale(__uint_as_float(mb), pow2);
+  u32x2 code[4];
+#pragma unroll
+  for (int g = 0; g < 4; ++g) code[g] = encode8(&w[4 * g], sc);
+  u32x4* dst = qt + (k0 + k) * (M / 16) + (m0 + 32 * p) / 16;
+  __builtin_nontemporal_store(u32x4{code[0].x, code[0].y, code[1].x, code[1].y}, dst);
+  __builtin_nontemporal_store(u32x4{code[2].x, code[2].y, code[3].x, code[3].y}, dst + 1);
+  if (p == 0) st[(k0 + k) * (M / 128) + m0 / 128] = sc;
+}
+
+// 4x4 byte transpose: a[i] holds row i (byte j = column j); returns column j
+// in b[j] (byte i = row i).
+__device__ __forceinline__ void transpose4x4(const uint32_t a[4], uint32_t b[4]) {
+  const uint32_t p01l = __builtin_amdgcn_perm(a[1], a[0], 0x05010400u);  // a0.0 a1.0 a0.1 a1.1
+  const uint32_t p01h = __builtin_amdgcn_perm(a[1], a[0], 0x07030602u);  // a0.2 a1.2 a0.3 a1.3
+  const uint32_t p23l = __builtin_amdgcn_perm(a[3], a[2], 0x05010400u);
+  const uint32_t p23h = __builtin_amdgcn_perm(a[3], a[2], 0x07030602u);
+  b[0] = __builtin_amdgcn_perm(p23l, p01l, 0x05040100u);
+  b[1] = __builtin_amdgcn_perm(p23l, p01l, 0x07060302u);
+  b[2] = __builtin_amdgcn_perm(p23h, p01h, 0x05040100u);
+  b[3] = __builtin_amdgcn_perm(p23h, p01h, 0x07060302u);
+}
+
+// W [N][K] -> QW^T [K][N], SW^T [K/128][N/128]: one workgroup per 128x128
+// block. Thread t holds the 8x8 sub-block rows 8(t/16).., columns 8(t%16)..
+// (eight 16-byte loads; the 16 threads of a row group read 256 contiguous
+// bytes), the block maximum goes through DPP and LDS, the codes are
+// transposed in registers (v_perm) and staged through LDS so that the
+// transposed rows leave as 16-byte coalesced stores.
+__global__ __launch_bounds__(256) void quant_weight_t_kernel(const u32x4* __restrict__ w, int64_t N, int64_t K,
+                                                             u32x4* __restrict__ qt, float* __restrict__ st,
+                                                             int pow2) {
+  __shared__ float red[16];
+  __shared__ __attribute__((aligned(16))) uint32_t tile[128 * 32];  // transposed codes, 128 rows of 128 bytes
+  const int t = threadIdx.x;
+  const int64_t kblocks = K / kBlock;
+  const int64_t bi = blockIdx.x / kblocks, bj = blockIdx.x % kblocks;
+  const int R = t >> 4, C = t & 15;
+  const int64_t row_units = K / 8;
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    v[i] = __builtin_nontemporal_load(&w[(bi * kBlock + 8 * R + i) * row_units + bj * 16 + C]);
+  uint32_t mb = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t ww[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    mb = max(mb, amax8_bits(ww));
+  }
+  float m = __uint_as_float(row16_max_bits(mb));
+  if ((t & 15) == 0) red[t >> 4] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) m = fmaxf(m, red[i]);
+  const float sc = group_scale(m, pow2);
+  // codes of rows 8R+i, columns 8C..8C+7: lo word = columns 0-3, hi = 4-7
+  uint32_t lo[8], hi[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t ww[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    const u32x2 c = encode8(ww, sc);
+    lo[i] = c.x;
+    hi[i] = c.y;
+  }
+  // transposed: column 8C + j of W is row 8C + j of W^T, bytes = rows 8R..8R+7
+  uint32_t c_lo[4], c_hi[4], d_lo[4], d_hi[4];
+  transpose4x4(&lo[0], c_lo);  // rows 0-3, columns 0-3
+  transpose4x4(&lo[4], c_hi);  // rows 4-7, columns 0-3
+  transpose4x4(&hi[0], d_lo);  // rows 0-3, columns 4-7
+  transpose4x4(&hi[4], d_hi);  // rows 4-7, columns 4-7
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    tile[(8 * C + j) * 32 + 2 * R] = c_lo[j];
+    tile[(8 * C + j) * 32 + 2 * R + 1] = c_hi[j];
+    tile[(8 * C + 4 + j) * 32 + 2 * R] = d_lo[j];
+    tile[(8 * C + 4 + j) * 32 + 2 * R + 1] = d_hi[j];
+  }
+  __syncthreads();
+  const int64_t out_units = N / 16;  // 16-byte units per W^T row
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int id = t + 256 * i, r = id >> 3, u = id & 7;  // 128 rows x 8 units
+    const u32x4 val = *reinterpret_cast<const u32x4*>(&tile[r * 32 + 4 * u]);
+    __builtin_nontemporal_store(val, &qt[(bj * kBlock + r) * out_units + bi * 8 + u]);
+  }
+  if (t == 0) st[bj * (N / kBlock) + bi] = sc;
+}
+
+// ---------------------------------------------------------------------------
 // Producers fused with the activation quantization (the pages name the
 // quantization kernels as overhead and their fusion as the way past it:
 // upppp.jp «重要度サンプリングで精度を保つ», greentreeone.com «Реальные
@@ -402,6 +545,34 @@ extern "C" fp8blk_status fp8blk_quant_weight(const uint16_t* w, int64_t N, int64
   hipLaunchKernelGGL(quant_weight_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
                      reinterpret_cast<const u32x4*>(w), reinterpret_cast<u32x2*>(q), s, kblocks, K,
                      pow2);
+  return launch_status();
+}
+
+extern "C" fp8blk_status fp8blk_quant_act_t(const uint16_t* x, int64_t M, int64_t K, uint8_t* qt, float* st,
+                                            int pow2, hipStream_t stream) {
+  if (M < 0 || K <= 0 || (pow2 != 0 && pow2 != 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (M % kBlock || K % 64) return FP8BLK_ERR_SHAPE;
+  if (M == 0) return FP8BLK_OK;
+  if (!x || !qt || !st) return FP8BLK_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(qt, 16) || !aligned(st, 4)) return FP8BLK_ERR_ALIGNMENT;
+  const int64_t blocks = (M / kBlock) * (K / 64);
+  if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(quant_act_t_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2);
+  return launch_status();
+}
+
+extern "C" fp8blk_status fp8blk_quant_weight_t(const uint16_t* w, int64_t N, int64_t K, uint8_t* qt, float* st,
+                                               int pow2, hipStream_t stream) {
+  if (N < 0 || K <= 0 || (pow2 != 0 && pow2 != 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (N % kBlock || K % kBlock) return FP8BLK_ERR_SHAPE;
+  if (N == 0) return FP8BLK_OK;
+  if (!w || !qt || !st) return FP8BLK_ERR_INVALID_ARG;
+  if (!aligned(w, 16) || !aligned(qt, 16) || !aligned(st, 4)) return FP8BLK_ERR_ALIGNMENT;
+  const int64_t blocks = (N / kBlock) * (K / kBlock);
+  if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(quant_weight_t_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(w), N, K, reinterpret_cast<u32x4*>(qt), st, pow2);
   return launch_status();
 }
 

@@ -121,6 +121,57 @@ fp8blk_status fp8blk_grouped_gemm(const uint8_t* qa, const float* sa,
                                   uint16_t* y, hipStream_t stream);
 
 /*
+ * Backward GEMMs of a linear layer Y = X W^T (FP8 training in Megatron Core:
+ * upppp.jp, «FP8適用の難所：数値のズレ問題»; greentreeone.com, «Технический
+ * прорыв»). The pages describe the forward recipe only; here each backward
+ * GEMM quantizes its operands along its own contraction dimension:
+ *   dgrad  dX = dY W:   fp8blk_quant_act(dY) (1x128 groups along N) and
+ *          fp8blk_quant_weight_t(W) (the 128x128 blocks, transposed), then
+ *          fp8blk_gemm(Q(dY), S(dY), QW^T, SW^T, M, K, N, dX);
+ *   wgrad  dW = dY^T X: fp8blk_quant_act_t of dY and of X (128x1 groups: 128
+ *          consecutive tokens of one column), then
+ *          fp8blk_gemm_rowscaled(Q(dY^T), S, Q(X^T), S, N, K, M, dW).
+ */
+
+/*
+ * 128x1 quantisation, written transposed: the 1x128 group quantisation of
+ * X^T. For each column k and token block b, the 128 values
+ * x[128b .. 128b+127][k] form one group (scale rule as fp8blk_quant_act).
+ *   x  [M][K] bf16 in (16-byte aligned)
+ *   qt [K][M] E4M3 codes out (16-byte aligned): qt[k][m] codes x[m][k]
+ *   st [K][M/128] fp32 scales out
+ *   M >= 0 (0: no-op), M % 128 == 0, K > 0 and K % 64 == 0, pow2 in {0, 1}.
+ */
+fp8blk_status fp8blk_quant_act_t(const uint16_t* x, int64_t M, int64_t K,
+                                 uint8_t* qt, float* st, int pow2, hipStream_t stream);
+
+/*
+ * 128x128 weight quantisation written transposed: the same blocks, codes and
+ * scales as fp8blk_quant_weight, in the layout the dgrad GEMM reads.
+ *   w  [N][K] bf16 in (16-byte aligned)
+ *   qt [K][N] E4M3 codes out: qt[k][n] codes w[n][k] (16-byte aligned)
+ *   st [K/128][N/128] fp32 scales out: st[j][i] is the scale of block (i, j)
+ *   N >= 0 (0: no-op), N % 128 == 0, K > 0 and K % 128 == 0, pow2 in {0, 1}.
+ */
+fp8blk_status fp8blk_quant_weight_t(const uint16_t* w, int64_t N, int64_t K,
+                                    uint8_t* qt, float* st, int pow2, hipStream_t stream);
+
+/*
+ * GEMM with per-row scales on both operands (the wgrad GEMM):
+ *   y[m][n] = bf16( sum_b sa[m][b] * sb[n][b] *
+ *                   sum_{k in block b} E4M3(qa[m][k]) * E4M3(qb[n][k]) )
+ *   qa [M][K] codes, sa [M][K/128]; qb [N][K] codes, sb [N][K/128] (one
+ *   scale per row and K block, e.g. from fp8blk_quant_act_t)
+ *   y  [M][N] bf16 out (16-byte aligned)
+ *   M >= 0 (M == 0: no-op), N > 0, K > 0, N % 128 == 0, K % 128 == 0,
+ *   K <= 2^24.
+ */
+fp8blk_status fp8blk_gemm_rowscaled(const uint8_t* qa, const float* sa,
+                                    const uint8_t* qb, const float* sb,
+                                    int64_t M, int64_t N, int64_t K,
+                                    uint16_t* y, hipStream_t stream);
+
+/*
  * Fused producers: the bf16 input of a linear layer is computed and quantised
  * in one pass, so it is never written to and read back from HBM. Both pages
  * count the quantisation kernels as overhead and name kernel fusion as the

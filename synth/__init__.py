@@ -206,6 +206,19 @@ def producer_inputs(workload, which, seed=0, m=None):
     raise ValueError(which)
 
 
+def backward_inputs(workload, layer, seed=0, m=None):
+    """(dY [M, N], X [M, K], W [N, K]) bf16 for the backward GEMMs of one
+    linear of a dense workload: X and W as in ``linear_inputs``, the output
+    gradient dY ~ N(0, 1) * 2^-10 with the workload's outlier recipe."""
+    wl = WORKLOADS[workload]
+    if isinstance(layer, str):
+        layer = [nm for nm, _, _ in wl.linears].index(layer)
+    x, w = linear_inputs(workload, layer, seed, m)
+    g = _gen(workload, 0x60 + layer, seed)
+    dy = activation(x.shape[0], w.shape[0], g, wl.outlier_frac, wl.outlier_scale).float() * 2.0 ** -10
+    return dy.to(torch.bfloat16), x, w
+
+
 # attention heads (query, key/value) and head size of each workload's model
 ATTENTION = {
     "llama8b_decode": (32, 8, 128),

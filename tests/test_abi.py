@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
         "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_qkv_amax", "fp8blk_kv_scales",
-        "fp8blk_kv_cache_write", "fp8blk_status_string"])
+        "fp8blk_kv_cache_write", "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
+        "fp8blk_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -196,6 +197,36 @@ def test_kv_cache_write_validation(lib):
     for name, bad in (("k", P4), ("v", P4), ("slot", P4), ("ks", P + 2), ("kc", P4), ("vc", P4)):
         assert call(**{name: bad}) == ALIGN, name
     assert call(T=0, k=NULL, v=NULL, slot=NULL) == OK
+
+
+def test_transposed_quant_validation(lib):
+    f = lib.fp8blk_quant_act_t
+    assert f(P, -128, 128, P, P, 0, NULL) == INVALID
+    assert f(P, 128, 0, P, P, 0, NULL) == INVALID
+    assert f(P, 128, 128, P, P, 2, NULL) == INVALID
+    assert f(P, 100, 128, P, P, 0, NULL) == SHAPE          # M % 128
+    assert f(P, 128, 96, P, P, 0, NULL) == SHAPE           # K % 64
+    assert f(NULL, 128, 128, P, P, 0, NULL) == INVALID
+    assert f(P, 128, 128, P4, P, 0, NULL) == ALIGN
+    assert f(P, 128, 128, P, P + 2, 0, NULL) == ALIGN
+    assert f(NULL, 0, 128, NULL, NULL, 0, NULL) == OK
+    g = lib.fp8blk_quant_weight_t
+    assert g(P, 100, 128, P, P, 0, NULL) == SHAPE
+    assert g(P, 128, 200, P, P, 0, NULL) == SHAPE
+    assert g(P, 128, 128, P, P, -1, NULL) == INVALID
+    assert g(P, 128, 128, NULL, P, 0, NULL) == INVALID
+    assert g(P4, 128, 128, P, P, 0, NULL) == ALIGN
+    assert g(NULL, 0, 128, NULL, NULL, 0, NULL) == OK
+
+
+def test_gemm_rowscaled_validation(lib):
+    f = lib.fp8blk_gemm_rowscaled
+    assert f(P, P, P, P, -1, 128, 128, P, NULL) == INVALID
+    assert f(P, P, P, P, 4, 130, 128, P, NULL) == SHAPE
+    assert f(P, P, P, P, 4, 128, (1 << 24) + 128, P, NULL) == SHAPE
+    assert f(P, P, NULL, P, 4, 128, 128, P, NULL) == INVALID
+    assert f(P, P, P, P + 1, 4, 128, 128, P, NULL) == ALIGN
+    assert f(NULL, NULL, NULL, NULL, 0, 128, 128, NULL, NULL) == OK
 
 
 def test_python_entry_points_raise(lib):
