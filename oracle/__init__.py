@@ -30,6 +30,9 @@ What it computes (sources are web pages about NVIDIA NeMo RL's FP8 recipe):
 * FP8 training (upppp.jp «FP8適用の難所：数値のズレ問題», greentreeone.com
   «Технический прорыв»): ``backward`` holds the dgrad and wgrad GEMMs under
   the same quantization rule along each GEMM's contraction dimension.
+* Both pages (upppp.jp «KVキャッシュとAttentionにも拡張», greentreeone.com
+  «Реальные прирост производительности»): attention in FP8 over the FP8 KV
+  cache; ``attention`` holds the decode step's attention over the paged cache.
 
 The pages give no scale formula, no E4M3 variant, no rounding mode and no
 accumulation scheme. The readings taken where they are silent are written
@@ -77,6 +80,7 @@ from .backward import (
     dgrad_ref,
     wgrad_ref,
 )
+from .attention import decode_attention_ref
 from .gemm import (
     dequant_act,
     dequant_weight,
@@ -96,4 +100,5 @@ __all__ = [
     "rmsnorm_ref", "silu_mul_ref", "round_bf16",
     "qkv_amax_ref", "kv_scales_ref", "kv_quantize_ref", "kv_cache_write_ref",
     "quant_act_t_ref", "quant_weight_t_ref", "gemm_rowscaled_ref", "dgrad_ref", "wgrad_ref",
+    "decode_attention_ref",
 ]

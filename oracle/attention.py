@@ -1,0 +1,74 @@
+"""FP8 decode attention over the paged FP8 KV cache (test infrastructure
+only, see the package docstring).
+
+Sources: the upppp.jp NeMo RL FP8 article, section «KVキャッシュとAttention
+にも拡張»: the longer the outputs, the more the KV cache and attention
+dominate rollout time, so the KV cache and attention also run in FP8 with
+the recalibrated Q/K/V scales; the greentreeone.com article, section
+«Реальные прирост производительности»: FP8 for the KV cache and the
+attention operations.
+
+Readings taken where the pages are silent (each listed in the design doc):
+
+* the decode step: each sequence's new query token attends over every token
+  cached for it (context_len tokens, the new one included once written);
+* Q is quantized like K and V, per tensor with the calibrated Q scale
+  (``kv_quantize_ref``); scores are the exact products of the FP8 values,
+      s[h, t] = (sum_d dec(q8[h, d]) dec(k8[t, g, d])) * q_scale * k_scale * sm_scale
+  with g = h // (Hq / Hkv) (grouped-query attention) and sm_scale given
+  (1 / sqrt(D) by default);
+* softmax over t in exact arithmetic, the probabilities kept unquantized,
+      out[h, d] = sum_t softmax(s[h])_t dec(v8[t, g, d]) * v_scale
+  rounded once to bf16 by the caller's comparison; a sequence with no
+  cached tokens gives 0;
+* paged cache: token t of sequence b is in slot
+  block_table[b, t // block_size] * block_size + t % block_size of the
+  [slots, Hkv, D] caches written by the cache write.
+
+Pins (tests/test_oracle_attention.py): one cached token returns its value
+row exactly; equal scores give the plain mean of the value rows; a dominant
+score selects its token; the softmax weights equal a Python loop with
+math.exp; permuting the pages (block table) leaves the output unchanged;
+grouped heads read their own KV head.
+"""
+
+import numpy as np
+
+from .e4m3 import decode
+from .kv_cache import kv_quantize_ref
+from .quant import bf16_values
+
+
+def decode_attention_ref(q, k_cache, v_cache, block_table, block_size, context_lens, q_scale, k_scale, v_scale,
+                         sm_scale=None):
+    """q [B, Hq, D] bf16; caches [slots, Hkv, D] E4M3 codes (uint8);
+    block_table [B, max_blocks] int; context_lens [B] int. Returns float64
+    [B, Hq, D]."""
+    qv = bf16_values(q)
+    b_, hq, d = qv.shape
+    k_cache = np.asarray(k_cache, np.uint8)
+    v_cache = np.asarray(v_cache, np.uint8)
+    hkv = k_cache.shape[1]
+    if hq % hkv or k_cache.shape[2] != d or v_cache.shape != k_cache.shape:
+        raise ValueError("shapes: q [B, Hq, D], caches [slots, Hkv, D], Hq % Hkv == 0")
+    group = hq // hkv
+    sm = 1.0 / np.sqrt(d) if sm_scale is None else float(np.float32(sm_scale))
+    qs, ks, vs = (float(np.float32(s)) for s in (q_scale, k_scale, v_scale))
+    q8 = decode(kv_quantize_ref(q, qs).reshape(b_, hq, d))
+    kd = decode(k_cache)
+    vd = decode(v_cache)
+    out = np.zeros((b_, hq, d))
+    table = np.asarray(block_table, np.int64)
+    for b in range(b_):
+        n = int(context_lens[b])
+        if n == 0:
+            continue
+        t = np.arange(n)
+        slots = table[b, t // block_size] * block_size + t % block_size
+        for h in range(hq):
+            g = h // group
+            s = (kd[slots, g, :] @ q8[b, h]) * qs * ks * sm
+            w = np.exp(s - s.max())
+            w /= w.sum()
+            out[b, h] = (w @ vd[slots, g, :]) * vs
+    return out
