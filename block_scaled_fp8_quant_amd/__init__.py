@@ -11,15 +11,16 @@ Two layers:
     ``fp8blk_grouped_gemm``, ``fp8blk_rmsnorm_quant_act``,
     ``fp8blk_silu_mul_quant_act``, ``fp8blk_qkv_amax``, ``fp8blk_kv_scales``,
     ``fp8blk_kv_cache_write``, ``fp8blk_quant_act_t``,
-    ``fp8blk_quant_weight_t``, ``fp8blk_gemm_rowscaled``: the C entry points
-    under their own names
+    ``fp8blk_quant_weight_t``, ``fp8blk_gemm_rowscaled``,
+    ``fp8blk_decode_attention``: the C entry points under their own names
     (integer device pointers, sizes, stream handle); they raise
     ``Fp8BlkError`` on a non-OK status;
   * ``quant_act``, ``quant_weight``, ``gemm``, ``grouped_gemm``,
     ``rmsnorm_quant_act``, ``silu_mul_quant_act``, ``qkv_amax``,
     ``kv_scales``, ``kv_cache_write``, ``quant_act_t``, ``quant_weight_t``,
-    ``gemm_rowscaled`` (and ``dgrad``, ``wgrad`` built from them): tensor
-    versions that validate shapes and allocate outputs.
+    ``gemm_rowscaled`` (and ``dgrad``, ``wgrad`` built from them),
+    ``decode_attention``: tensor versions that validate shapes and allocate
+    outputs.
 """
 
 import ctypes
@@ -59,6 +60,8 @@ def load():
         "fp8blk_silu_mul_quant_act": [vp, i64, i64, vp, vp, vp, i32, vp],
         "fp8blk_qkv_amax": [vp, i64, i64, i64, i64, vp, i32, vp],
         "fp8blk_quant_act_t": [vp, i64, i64, vp, vp, i32, vp],
+        "fp8blk_decode_attention": [vp, i64, i64, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp, vp, f32,
+                                    vp, i64, vp],
         "fp8blk_quant_weight_t": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_gemm_rowscaled": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8blk_kv_scales": [vp, i64, vp, i32, vp],
@@ -106,6 +109,12 @@ def fp8blk_rmsnorm_quant_act(x, gamma, eps, M, K, q, s, y, pow2, stream):
 
 def fp8blk_silu_mul_quant_act(gu, M, F, q, s, y, pow2, stream):
     return _call("fp8blk_silu_mul_quant_act", gu, M, F, q, s, y, int(pow2), stream)
+
+
+def fp8blk_decode_attention(q, ldq, B, Hq, Hkv, D, k_cache, v_cache, num_slots, block_table, max_blocks,
+                            block_size, context_lens, q_scale, k_scale, v_scale, sm_scale, out, ldo, stream):
+    return _call("fp8blk_decode_attention", q, ldq, B, Hq, Hkv, D, k_cache, v_cache, num_slots, block_table,
+                 max_blocks, block_size, context_lens, q_scale, k_scale, v_scale, sm_scale, out, ldo, stream)
 
 
 def fp8blk_quant_act_t(x, M, K, qt, st, pow2, stream):
@@ -367,6 +376,43 @@ def wgrad(dy, x, pow2=False):
     return gemm_rowscaled(qa, sa, qb, sb)
 
 
+def decode_attention(q, k_cache, v_cache, block_table, block_size, context_lens, q_scale, k_scale, v_scale,
+                     sm_scale=None, out=None):
+    """FP8 decode attention: q [B, Hq, D] bf16 (or [B, Hq*D] rows with a row
+    stride, e.g. a view into a qkv output), caches [slots, Hkv, D] uint8,
+    block_table [B, max_blocks] int32, context_lens [B] int32, one-element
+    fp32 scale tensors, all on the device. Returns out [B, Hq, D] bf16."""
+    torch = _torch()
+    if k_cache.dim() != 3 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [slots, Hkv, D] and alike")
+    slots, hkv, d = k_cache.shape
+    b = q.shape[0]
+    hq = (q.shape[1] * q.shape[2] if q.dim() == 3 else q.shape[1]) // d
+    dev = q.device
+    if q.dtype != torch.bfloat16 or dev.type != "cuda":
+        raise TypeError("q must be bf16 on a HIP device")
+    if q.stride(-1) != 1 or (q.dim() == 3 and q.stride(1) != d):
+        raise ValueError("each row of q must hold its Hq heads contiguously")
+    ldq = q.stride(0) if b > 1 else hq * d
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if c.dtype != torch.uint8 or c.device != dev or not c.is_contiguous():
+            raise ValueError("%s must be a contiguous uint8 tensor on the device of q" % name)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _check(block_table, "block_table", torch.int32, (b, block_table.shape[1]), dev)
+    _check(context_lens, "context_lens", torch.int32, (b,), dev)
+    for name, sc in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check(sc.reshape(-1), name, torch.float32, (1,), dev)
+    out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    _check(out, "out", torch.bfloat16, (b, hq, d), dev)
+    sm = 1.0 / d ** 0.5 if sm_scale is None else float(sm_scale)
+    fp8blk_decode_attention(q.data_ptr(), ldq, b, hq, hkv, d, k_cache.data_ptr(), v_cache.data_ptr(), slots,
+                            block_table.data_ptr(), block_table.shape[1], block_size, context_lens.data_ptr(),
+                            q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), sm, out.data_ptr(), hq * d,
+                            _stream(dev))
+    return out
+
+
 def qkv_amax(qkv, hq, hkv, d, amax=None, reset=True):
     """Running maxima of |Q|, |K|, |V| of a qkv projection output [T,
     (hq + 2*hkv)*d] (bf16, rows [Q | K | V]) into amax (fp32 [3] on the
@@ -445,8 +491,8 @@ __all__ = [
     "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
     "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act",
     "fp8blk_qkv_amax", "fp8blk_kv_scales", "fp8blk_kv_cache_write",
-    "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
+    "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled", "fp8blk_decode_attention",
     "quant_act", "quant_weight", "gemm", "grouped_gemm", "rmsnorm_quant_act", "silu_mul_quant_act",
     "qkv_amax", "kv_scales", "kv_cache_write", "quant_act_t", "quant_weight_t", "gemm_rowscaled",
-    "dgrad", "wgrad", "linear",
+    "dgrad", "wgrad", "decode_attention", "linear",
 ]

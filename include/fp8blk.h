@@ -268,6 +268,41 @@ fp8blk_status fp8blk_kv_cache_write(const uint16_t* k, const uint16_t* v, int64_
                                     const float* k_scale, const float* v_scale,
                                     uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream);
 
+/*
+ * FP8 decode attention over the paged FP8 KV cache (upppp.jp,
+ * «KVキャッシュとAttentionにも拡張»: with long outputs the KV cache and
+ * attention dominate rollout time, and both run in FP8; greentreeone.com,
+ * «Реальные прирост производительности»). Each sequence's new query token
+ * attends over its cached tokens:
+ *   q8 = E4M3(RN_fp32(q / q_scale)) (as the cache write quantizes K and V)
+ *   s[h][t] = (sum_d q8[h][d] * k8[t][g][d]) * q_scale * k_scale * sm_scale,
+ *             g = h / (Hq / Hkv)
+ *   out[h][d] = bf16( sum_t softmax_t(s[h])[t] * v8[t][g][d] * v_scale )
+ * with the softmax and the weighted sum in fp32.
+ *   q            [B][ldq] bf16: the first Hq*D values of row b are sequence b's
+ *                query heads (so q may point into a qkv projection output)
+ *   k_cache, v_cache [num_slots][Hkv][D] E4M3 codes (fp8blk_kv_cache_write)
+ *   block_table  [B][max_blocks] int32 (device): token t of sequence b is in
+ *                slot block_table[b][t / block_size] * block_size + t % block_size
+ *   context_lens [B] int32 (device): cached tokens per sequence
+ *   q_scale, k_scale, v_scale: one fp32 each (device)
+ *   sm_scale     softmax scale (1/sqrt(D) for standard attention)
+ *   out          [B][ldo] bf16 out: Hq heads x D per row (16-byte aligned)
+ *   D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}; ldq and ldo
+ *   multiples of 8 and >= Hq*D; B >= 0 (0: no-op); block_size, max_blocks >= 1.
+ * Tokens whose block index is past max_blocks, whose block id is negative or
+ * whose slot is past num_slots are skipped; a sequence without tokens gives
+ * zeros.
+ */
+fp8blk_status fp8blk_decode_attention(const uint16_t* q, int64_t ldq, int64_t B, int64_t Hq,
+                                      int64_t Hkv, int64_t D, const uint8_t* k_cache,
+                                      const uint8_t* v_cache, int64_t num_slots,
+                                      const int32_t* block_table, int64_t max_blocks,
+                                      int64_t block_size, const int32_t* context_lens,
+                                      const float* q_scale, const float* k_scale,
+                                      const float* v_scale, float sm_scale,
+                                      uint16_t* out, int64_t ldo, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (host memory). */
 const char* fp8blk_status_string(fp8blk_status status);
 

@@ -245,6 +245,46 @@ def kv_inputs(workload, seed=0, t=None):
     return x.to(torch.bfloat16), (hq, hkv, d)
 
 
+def attention_inputs(context_lens, hq, hkv, d=128, block_size=16, seed=0, spare_blocks=3):
+    """A decode step over a paged KV cache: q [B, Hq, D] ~ N(0, 1) and, for
+    every cached token, K ~ N(0, 2^2) and V ~ N(0, 0.5^2) rows [T, Hkv*D]
+    (bf16), with the pages of all sequences shuffled over a pool that has
+    ``spare_blocks`` unused pages. Returns a dict: q, k, v, slot [T] (the
+    cache slot of each token row), block_table [B, max_blocks] int32 (-1
+    past a sequence's pages), context_lens [B] int32, num_slots, block_size."""
+    g = generator(0xA0, seed)
+    lens = [int(n) for n in context_lens]
+    b = len(lens)
+    blocks = [(n + block_size - 1) // block_size for n in lens]
+    max_blocks = max(1, max(blocks))
+    pool = sum(blocks) + spare_blocks
+    perm = torch.randperm(pool, generator=g)
+    table = torch.full((b, max_blocks), -1, dtype=torch.int32)
+    slots, used = [], 0
+    for i, n in enumerate(lens):
+        table[i, :blocks[i]] = perm[used:used + blocks[i]].to(torch.int32)
+        used += blocks[i]
+        for t in range(n):
+            slots.append(int(table[i, t // block_size]) * block_size + t % block_size)
+    tot = len(slots)
+    q = torch.randn(b, hq, d, generator=g).to(torch.bfloat16)
+    k = (torch.randn(tot, hkv * d, generator=g) * 2.0).to(torch.bfloat16)
+    v = (torch.randn(tot, hkv * d, generator=g) * 0.5).to(torch.bfloat16)
+    return dict(q=q, k=k, v=v, slot=torch.tensor(slots, dtype=torch.int64), block_table=table,
+                context_lens=torch.tensor(lens, dtype=torch.int32), num_slots=pool * block_size,
+                block_size=block_size)
+
+
+def random_cache_codes(shape, seed, device):
+    """E4M3 codes drawn on ``device``: magnitude codes 0..126 (finite values)
+    with random signs, for caches too large to draw on the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed((int(seed) << 16) + 0xB0)
+    mag = torch.randint(0, 127, shape, generator=g, device=device, dtype=torch.int32)
+    sign = torch.randint(0, 2, shape, generator=g, device=device, dtype=torch.int32) * 128
+    return (mag + sign).to(torch.uint8)
+
+
 def generator(tag, seed=0):
     """A seeded generator for ad-hoc test inputs (``tag`` < 256)."""
     g = torch.Generator(device="cpu")

@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
         "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
         "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_qkv_amax", "fp8blk_kv_scales",
         "fp8blk_kv_cache_write", "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
-        "fp8blk_status_string"])
+        "fp8blk_decode_attention", "fp8blk_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -227,6 +227,34 @@ def test_gemm_rowscaled_validation(lib):
     assert f(P, P, NULL, P, 4, 128, 128, P, NULL) == INVALID
     assert f(P, P, P, P + 1, 4, 128, 128, P, NULL) == ALIGN
     assert f(NULL, NULL, NULL, NULL, 0, 128, 128, NULL, NULL) == OK
+
+
+def test_decode_attention_validation(lib):
+    f = lib.fp8blk_decode_attention
+    names = ["q", "ldq", "B", "Hq", "Hkv", "D", "kc", "vc", "slots", "table", "max_blocks", "bs", "lens",
+             "qs", "ks", "vs", "sm", "out", "ldo", "stream"]
+    ok = [P, 4096, 4, 32, 8, 128, P, P, 1024, P, 16, 16, P, P, P, P, 0.088, P, 4096, NULL]
+
+    def call(**kw):
+        a = list(ok)
+        for key, val in kw.items():
+            a[names.index(key)] = val
+        return f(*a)
+    assert call(B=-1) == INVALID
+    assert call(Hq=0) == INVALID
+    assert call(max_blocks=0) == INVALID
+    assert call(bs=0) == INVALID
+    assert call(sm=float("nan")) == INVALID
+    assert call(ldq=1024) == INVALID                      # ldq < Hq*D
+    assert call(D=64, ldq=2048, ldo=2048) == SHAPE        # D != 128
+    assert call(Hq=12) == SHAPE                           # Hq % Hkv
+    assert call(Hq=128, ldq=16384, ldo=16384) == SHAPE    # Hq / Hkv = 16
+    assert call(ldq=4100) == SHAPE
+    for name in ("q", "kc", "vc", "table", "lens", "qs", "ks", "vs", "out"):
+        assert call(**{name: NULL}) == INVALID, name
+    for name, bad in (("q", P4), ("kc", P4), ("out", P4), ("table", P + 2), ("qs", P + 1)):
+        assert call(**{name: bad}) == ALIGN, name
+    assert call(B=0, q=NULL, out=NULL) == OK
 
 
 def test_python_entry_points_raise(lib):

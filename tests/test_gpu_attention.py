@@ -1,0 +1,168 @@
+"""GPU parity of the FP8 decode attention over the paged FP8 KV cache
+against the oracle, through the C ABI. The caches are written by the
+library's own cache write from seeded bf16 K and V; the oracle reads the same
+cache bytes. Outputs within |y - y_ref| <= 2^-7 |y_ref| + 1e-3 rms(y_ref)."""
+
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_fp8_quant_amd as fb
+import oracle
+import synth
+from tests.gpu_util import assert_within_tolerance, guarded
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+D = 128
+
+
+def build(lens, hq, hkv, seed=0, bs=16):
+    """Inputs on the device, caches filled by the cache write with scales
+    calibrated on the data."""
+    a = synth.attention_inputs(lens, hq, hkv, D, bs, seed)
+    k, v = a["k"].to(DEV), a["v"].to(DEV)
+    num_slots = a["num_slots"]
+    kc = torch.zeros(num_slots, hkv, D, dtype=torch.uint8, device=DEV)
+    vc = torch.zeros(num_slots, hkv, D, dtype=torch.uint8, device=DEV)
+    amax = torch.stack([a["q"].float().abs().max(), a["k"].float().abs().max(), a["v"].float().abs().max()])
+    scales = fb.kv_scales(amax.to(DEV))
+    if k.shape[0]:
+        fb.kv_cache_write(k, v, a["slot"].to(DEV), scales[1:2], scales[2:3], kc, vc)
+    torch.cuda.synchronize()
+    return a, kc, vc, scales
+
+
+def run(a, kc, vc, scales, sm=None):
+    b, hq = a["q"].shape[0], a["q"].shape[1]
+    out, check = guarded((b, hq, D), torch.bfloat16, DEV)
+    fb.decode_attention(a["q"].to(DEV), kc, vc, a["block_table"].to(DEV), a["block_size"],
+                        a["context_lens"].to(DEV), scales[0:1], scales[1:2], scales[2:3], sm_scale=sm, out=out)
+    check()
+    return out
+
+
+def reference(a, kc, vc, scales, sm=None):
+    s = scales.cpu().numpy()
+    return oracle.decode_attention_ref(a["q"], kc.cpu().numpy(), vc.cpu().numpy(), a["block_table"].numpy(),
+                                       a["block_size"], a["context_lens"].numpy(), s[0], s[1], s[2], sm)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (32, 8), (32, 4)])
+def test_context_lengths_and_groups(fp8blk_lib, hq, hkv):
+    """Context lengths 0, 1, a partial 16-token subtile, one and two 64-token
+    tiles, more tiles than waves, ragged tails; every head-group size."""
+    lens = [0, 1, 15, 64, 65, 300, 1000, 257]
+    a, kc, vc, sc = build(lens, hq, hkv, seed=hq + hkv)
+    out = run(a, kc, vc, sc)
+    ref = reference(a, kc, vc, sc)
+    assert torch.all(out[0].float() == 0)
+    assert_within_tolerance(out.float().cpu().numpy().reshape(len(lens), -1), ref.reshape(len(lens), -1),
+                            what="decode attention")
+
+
+def test_softmax_scale_and_block_size(fp8blk_lib):
+    a, kc, vc, sc = build([33, 130, 7], 16, 4, seed=5, bs=8)
+    for sm in (0.01, 0.3):
+        out = run(a, kc, vc, sc, sm)
+        assert_within_tolerance(out.float().cpu().numpy().reshape(3, -1), reference(a, kc, vc, sc, sm).reshape(3, -1),
+                                what="sm_scale %g" % sm)
+
+
+def test_single_token_is_its_value_row(fp8blk_lib):
+    """One cached token: softmax weight 1, out = v8 * v_scale to a bf16 ulp."""
+    a, kc, vc, sc = build([1, 1, 1], 8, 2, seed=6)
+    out = run(a, kc, vc, sc).float().cpu().numpy()
+    ref = reference(a, kc, vc, sc)
+    assert np.all(np.abs(out - ref) <= 2.0 ** -8 * np.abs(ref))
+
+
+def test_masked_tokens_are_skipped(fp8blk_lib):
+    """A negative block id, a block past the cache and a context longer than
+    the block table: those tokens are left out, as if never cached."""
+    a, kc, vc, sc = build([40, 50, 20], 8, 4, seed=7)
+    table = a["block_table"].clone()
+    table[0, 1] = -1                                   # tokens 16..31 of sequence 0
+    table[1, 2] = a["num_slots"] // 16 + 5             # tokens 32..47 of sequence 1
+    lens = a["context_lens"].clone()
+    lens[2] = 20 + 16 * table.shape[1]                 # past max_blocks * block_size
+    b2 = dict(a, block_table=table, context_lens=lens)
+    out = run(b2, kc, vc, sc).float().cpu().numpy()
+    # the same attention on a cache holding only the kept tokens, repacked
+    keep = {0: [t for t in range(40) if not 16 <= t < 32], 1: [t for t in range(50) if not 32 <= t < 48],
+            2: list(range(16 * table.shape[1]))}
+    kcn, vcn = kc.cpu().numpy(), vc.cpu().numpy()
+    rows_k, rows_v, new_table, new_lens, nxt = [], [], [], [], 0
+    width = max(len(v) for v in keep.values())
+    for bi in range(3):
+        ids = []
+        for t in keep[bi]:
+            blk = int(a["block_table"][bi, t // 16]) if t // 16 < table.shape[1] else -1
+            if blk < 0:
+                continue
+            slot = blk * 16 + t % 16
+            rows_k.append(kcn[slot])
+            rows_v.append(vcn[slot])
+            ids.append(nxt)
+            nxt += 1
+        new_lens.append(len(ids))
+        new_table.append(ids + [0] * (width - len(ids)))
+    ref = oracle.decode_attention_ref(a["q"], np.stack(rows_k), np.stack(rows_v), np.array(new_table), 1,
+                                      np.array(new_lens), *sc.cpu().numpy())
+    assert_within_tolerance(out.reshape(3, -1), ref.reshape(3, -1), what="masked tokens")
+
+
+def test_end_to_end_recalibrate_write_attend(fp8blk_lib):
+    """A qkv projection output for the cached tokens: maxima -> scales ->
+    cache write -> attention of each sequence's last token, all on the
+    device; the oracle reads the caches the device wrote."""
+    hq, hkv = 32, 8
+    lens = [100, 37, 256, 1]
+    qkv, _ = synth.kv_inputs("llama8b_decode", t=sum(lens))
+    dq = qkv.to(DEV)
+    scales = fb.kv_scales(fb.qkv_amax(dq, hq, hkv, D))
+    a = synth.attention_inputs(lens, hq, hkv, D, 16, seed=8)
+    kc = torch.zeros(a["num_slots"], hkv, D, dtype=torch.uint8, device=DEV)
+    vc = torch.zeros_like(kc)
+    fb.kv_cache_write(dq[:, hq * D:(hq + hkv) * D], dq[:, (hq + hkv) * D:], a["slot"].to(DEV), scales[1:2],
+                      scales[2:3], kc, vc)
+    b = len(lens)
+    q_rows = dq[-b:, :hq * D]                          # read in place: row stride (Hq + 2 Hkv) D
+    assert q_rows.stride(0) == (hq + 2 * hkv) * D
+    out = torch.empty(b, hq, D, dtype=torch.bfloat16, device=DEV)
+    fb.decode_attention(q_rows, kc, vc, a["block_table"].to(DEV), 16, a["context_lens"].to(DEV), scales[0:1],
+                        scales[1:2], scales[2:3], out=out)
+    torch.cuda.synchronize()
+    s = scales.cpu().numpy()
+    ref = oracle.decode_attention_ref(qkv[-b:, :hq * D].reshape(b, hq, D), kc.cpu().numpy(), vc.cpu().numpy(),
+                                      a["block_table"].numpy(), 16, np.array(lens), s[0], s[1], s[2])
+    assert_within_tolerance(out.float().cpu().numpy().reshape(b, -1), ref.reshape(b, -1), what="end to end")
+
+
+def test_full_size_decode_sampled(fp8blk_lib):
+    """The Llama-3.1-8B decode batch (256 sequences, 32/8 heads) at 2048
+    cached tokens each, caches of random codes; sampled sequences checked."""
+    b, hq, hkv, ctx, bs = 256, 32, 8, 2048, 16
+    blocks = ctx // bs
+    g = synth.generator(90)
+    perm = torch.randperm(b * blocks + 7, generator=g)[: b * blocks].to(torch.int32).reshape(b, blocks)
+    num_slots = (b * blocks + 7) * bs
+    kc = synth.random_cache_codes((num_slots, hkv, D), 1, DEV)
+    vc = synth.random_cache_codes((num_slots, hkv, D), 2, DEV)
+    q = torch.randn(b, hq, D, generator=g).to(torch.bfloat16)
+    lens = torch.full((b,), ctx, dtype=torch.int32)
+    scales = torch.tensor([4.0 / 448, 0.004, 0.01], dtype=torch.float32, device=DEV)
+    out = fb.decode_attention(q.to(DEV), kc, vc, perm.to(DEV), bs, lens.to(DEV), scales[0:1], scales[1:2],
+                              scales[2:3])
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 255], torch.randint(0, b, (4,), generator=g).numpy()]))
+    # the oracle reads only the sampled sequences' pages, gathered into a
+    # small cache with the block table renumbered (page order is immaterial)
+    pages = perm[torch.from_numpy(rows)].reshape(-1).long().to(DEV)
+    small_k = kc.view(-1, bs, hkv, D)[pages].reshape(-1, hkv, D).cpu().numpy()
+    small_v = vc.view(-1, bs, hkv, D)[pages].reshape(-1, hkv, D).cpu().numpy()
+    table = np.arange(len(rows) * blocks).reshape(len(rows), blocks)
+    ref = oracle.decode_attention_ref(q[torch.from_numpy(rows)], small_k, small_v, table, bs, lens.numpy()[rows],
+                                      *scales.cpu().numpy())
+    got = out[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    assert_within_tolerance(got.reshape(len(rows), -1), ref.reshape(len(rows), -1), what="full-size decode")
