@@ -17,7 +17,9 @@ input -- each against the HBM roofline; ``kv_cache`` does the same for the
 FP8 KV-cache path (Q/K/V recalibration maxima, quantize-and-write of K and V
 into the cache) at the workload's attention shapes; ``backward`` times the
 dgrad and wgrad GEMMs of every linear (and their transposing quantizers)
-against the same rooflines.
+against the same rooflines; ``attention`` times the FP8 decode attention over
+the paged FP8 KV cache at the workload's heads for four context mixes,
+against the HBM roofline (one call: the split path's two kernels together).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -63,6 +65,7 @@ def parse():
     p.add_argument("--no-producers", action="store_true", help="skip timing the fused producer kernels")
     p.add_argument("--no-kv", action="store_true", help="skip timing the FP8 KV-cache path")
     p.add_argument("--no-backward", action="store_true", help="skip timing the backward GEMMs")
+    p.add_argument("--no-attention", action="store_true", help="skip timing the FP8 decode attention")
     p.add_argument("--backward-reps", type=int, default=3)
     p.add_argument("--producer-reps", type=int, default=20)
     p.add_argument("--cpu-sample-rows", type=int, default=8192)
@@ -264,6 +267,73 @@ def time_kv(fb, K, reps):
     out = {"heads": [hq, hkv, d],
            "qkv_amax": hbm_entry([t, (hq + 2 * hkv) * d], ms_amax, 2 * t * (hq + 2 * hkv) * d + 12),
            "kv_cache_write": hbm_entry([t, 2, w], ms_write, 2 * t * w * 2 + 2 * t * w + 8 * t + 8)}
+    return out
+
+
+ATTN_BATCH = 256           # sequences in one decode step
+ATTN_BLOCK = 16            # tokens per cache page
+
+
+def attention_case(workload, dev, lens, seed):
+    """One decode step of the workload's attention heads over a paged FP8 KV
+    cache holding ``lens`` tokens per sequence (pages shuffled over the pool;
+    cache codes random finite E4M3, since the kernel's speed does not depend
+    on the values)."""
+    import torch
+    import synth
+    hq, hkv, d = synth.ATTENTION[workload]
+    b = len(lens)
+    blocks = [(n + ATTN_BLOCK - 1) // ATTN_BLOCK for n in lens]
+    mb = max(1, max(blocks))
+    g = synth.generator(0x78, seed)
+    pool = sum(blocks) + 1
+    perm = torch.randperm(pool, generator=g).to(torch.int32)
+    table = torch.full((b, mb), -1, dtype=torch.int32)
+    used = 0
+    for i, nb in enumerate(blocks):
+        table[i, :nb] = perm[used:used + nb]
+        used += nb
+    return dict(q=torch.randn(b, hq, d, generator=g).to(torch.bfloat16).to(dev),
+                kc=synth.random_cache_codes((pool * ATTN_BLOCK, hkv, d), 2 * seed + 1, dev),
+                vc=synth.random_cache_codes((pool * ATTN_BLOCK, hkv, d), 2 * seed + 2, dev),
+                table=table.to(dev), lens=torch.tensor(lens, dtype=torch.int32).to(dev),
+                scales=torch.tensor([4.0 / 448, 0.004, 0.01], dtype=torch.float32, device=dev),
+                out=torch.empty(b, hq, d, dtype=torch.bfloat16, device=dev),
+                heads=(hq, hkv, d), blocks=sum(blocks), tokens=sum(lens))
+
+
+def time_attention(fb, workload, dev, reps):
+    """FP8 decode attention (one query token per sequence over its cached
+    tokens) at the workload's heads, four context mixes: 256 sequences of
+    2048 tokens, 256 ragged sequences of 1..4096 tokens, 32 sequences of
+    16384 tokens, and 4 sequences of 32768 tokens (the library then splits
+    the contexts into chunks merged by a second kernel). Algorithmic bytes:
+    each cached token's K and V rows of every KV head once (2 Hkv D bytes),
+    the block table entries in use, Q read and O written in bf16, lengths and
+    scales (the split path's fp32 partials are not counted)."""
+    import torch
+    import synth
+    g = synth.generator(0x79)
+    mixes = {"b256_ctx2048": [2048] * ATTN_BATCH,
+             "b256_ctx1to4096": torch.randint(1, 4097, (ATTN_BATCH,), generator=g).tolist(),
+             "b32_ctx16384": [16384] * 32,
+             "b4_ctx32768": [32768] * 4}
+    out = {}
+    for i, (name, lens) in enumerate(mixes.items()):
+        A = attention_case(workload, dev, lens, i)
+        hq, hkv, d = A["heads"]
+        sc = A["scales"]
+        b, mb = len(lens), A["table"].shape[1]
+        need = fb.fp8blk_decode_attention_workspace_size(b, hq, hkv, d, mb, ATTN_BLOCK, 0)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        ms = graph_time_ms(lambda: fb.decode_attention(A["q"], A["kc"], A["vc"], A["table"], ATTN_BLOCK, A["lens"],
+                                                       sc[0:1], sc[1:2], sc[2:3], out=A["out"], workspace=ws), reps)
+        nbytes = 2 * A["tokens"] * hkv * d + 4 * A["blocks"] + 2 * 2 * b * hq * d + 4 * b + 12
+        out[name] = hbm_entry([b, hq, hkv, d], ms, nbytes)
+        out[name]["split"] = need > 0
+        out[name]["tokens"] = A["tokens"]
+        del A
+        torch.cuda.empty_cache()
     return out
 
 
@@ -571,6 +641,12 @@ def main():
         for name, key in (("qkv_amax", "qkv_amax_kernel"), ("kv_cache_write", "kv_cache_write_kernel")):
             t = traffic_rec.get(key, {}).get("bytes_per_launch")
             out["kv_cache"][name]["traffic"] = None if t is None else round(t)
+    if not args.no_attention:
+        print("bench: timing the FP8 decode attention", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        out["attention"] = time_attention(fb, args.workload, dev, args.producer_reps)
+        for entry in out["attention"].values():
+            entry["traffic"] = None
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows)

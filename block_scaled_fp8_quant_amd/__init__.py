@@ -61,7 +61,7 @@ def load():
         "fp8blk_qkv_amax": [vp, i64, i64, i64, i64, vp, i32, vp],
         "fp8blk_quant_act_t": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_decode_attention": [vp, i64, i64, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp, vp, f32,
-                                    vp, i64, vp],
+                                    vp, i64, i64, vp, ctypes.c_size_t, vp],
         "fp8blk_quant_weight_t": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_gemm_rowscaled": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8blk_kv_scales": [vp, i64, vp, i32, vp],
@@ -71,6 +71,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.fp8blk_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64]
+    lib.fp8blk_decode_attention_workspace_size.restype = ctypes.c_size_t
     lib.fp8blk_status_string.argtypes = [ctypes.c_int]
     lib.fp8blk_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -112,9 +114,15 @@ def fp8blk_silu_mul_quant_act(gu, M, F, q, s, y, pow2, stream):
 
 
 def fp8blk_decode_attention(q, ldq, B, Hq, Hkv, D, k_cache, v_cache, num_slots, block_table, max_blocks,
-                            block_size, context_lens, q_scale, k_scale, v_scale, sm_scale, out, ldo, stream):
+                            block_size, context_lens, q_scale, k_scale, v_scale, sm_scale, out, ldo, split_tokens,
+                            workspace, workspace_bytes, stream):
     return _call("fp8blk_decode_attention", q, ldq, B, Hq, Hkv, D, k_cache, v_cache, num_slots, block_table,
-                 max_blocks, block_size, context_lens, q_scale, k_scale, v_scale, sm_scale, out, ldo, stream)
+                 max_blocks, block_size, context_lens, q_scale, k_scale, v_scale, sm_scale, out, ldo, split_tokens,
+                 workspace, workspace_bytes, stream)
+
+
+def fp8blk_decode_attention_workspace_size(B, Hq, Hkv, D, max_blocks, block_size, split_tokens):
+    return load().fp8blk_decode_attention_workspace_size(B, Hq, Hkv, D, max_blocks, block_size, split_tokens)
 
 
 def fp8blk_quant_act_t(x, M, K, qt, st, pow2, stream):
@@ -377,11 +385,15 @@ def wgrad(dy, x, pow2=False):
 
 
 def decode_attention(q, k_cache, v_cache, block_table, block_size, context_lens, q_scale, k_scale, v_scale,
-                     sm_scale=None, out=None):
+                     sm_scale=None, out=None, split=True, split_tokens=0, workspace=None):
     """FP8 decode attention: q [B, Hq, D] bf16 (or [B, Hq*D] rows with a row
     stride, e.g. a view into a qkv output), caches [slots, Hkv, D] uint8,
     block_table [B, max_blocks] int32, context_lens [B] int32, one-element
-    fp32 scale tensors, all on the device. Returns out [B, Hq, D] bf16."""
+    fp32 scale tensors, all on the device. Returns out [B, Hq, D] bf16.
+    split=False runs one workgroup per (sequence, KV head) over the whole
+    context; otherwise contexts are cut into chunks of split_tokens tokens
+    (0: the library's choice) whose partials go to ``workspace`` (a uint8
+    device tensor, allocated here when None)."""
     torch = _torch()
     if k_cache.dim() != 3 or v_cache.shape != k_cache.shape:
         raise ValueError("caches must be [slots, Hkv, D] and alike")
@@ -406,10 +418,19 @@ def decode_attention(q, k_cache, v_cache, block_table, block_size, context_lens,
     out = torch.empty((b, hq, d), dtype=torch.bfloat16, device=dev) if out is None else out
     _check(out, "out", torch.bfloat16, (b, hq, d), dev)
     sm = 1.0 / d ** 0.5 if sm_scale is None else float(sm_scale)
+    ws_ptr, ws_bytes = None, 0
+    if split:
+        need = fp8blk_decode_attention_workspace_size(b, hq, hkv, d, block_table.shape[1], block_size, split_tokens)
+        if need:
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+            if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+                raise ValueError("workspace must be a contiguous uint8 tensor on the device of q")
+            ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     fp8blk_decode_attention(q.data_ptr(), ldq, b, hq, hkv, d, k_cache.data_ptr(), v_cache.data_ptr(), slots,
                             block_table.data_ptr(), block_table.shape[1], block_size, context_lens.data_ptr(),
                             q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), sm, out.data_ptr(), hq * d,
-                            _stream(dev))
+                            split_tokens, ws_ptr, ws_bytes, _stream(dev))
     return out
 
 
@@ -492,6 +513,7 @@ __all__ = [
     "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act",
     "fp8blk_qkv_amax", "fp8blk_kv_scales", "fp8blk_kv_cache_write",
     "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled", "fp8blk_decode_attention",
+    "fp8blk_decode_attention_workspace_size",
     "quant_act", "quant_weight", "gemm", "grouped_gemm", "rmsnorm_quant_act", "silu_mul_quant_act",
     "qkv_amax", "kv_scales", "kv_cache_write", "quant_act_t", "quant_weight_t", "gemm_rowscaled",
     "dgrad", "wgrad", "decode_attention", "linear",

@@ -12,19 +12,26 @@
 // g = h / (Hq/Hkv); softmax in fp32; out[h] = sum_t p[h][t] v8[t][g] v_scale,
 // probabilities kept in fp32; bf16 output.
 //
-// One workgroup per (sequence, KV head); its four waves take interleaved
-// 64-token tiles of the context and keep their own running maximum, sum and
-// output (online softmax), merged through LDS at the end. Per tile:
+// Work decomposition: a workgroup of four waves takes one (sequence, KV head)
+// and either the whole context (direct mode: it writes the bf16 output) or
+// one chunk of it (split mode: it writes fp32 partials -- running maximum,
+// sum and unnormalized output per head -- to the workspace, and a second
+// kernel merges the chunks of each head). Splitting keeps the chip full when
+// there are few (sequence, KV head) pairs.
+// Within a workgroup the waves take interleaved 64-token tiles and keep
+// their own online-softmax state, merged through LDS. Per tile:
 //   * the 64 tokens' cache slots come from the block table (one per lane;
-//     out-of-range tokens, blocks or slots are masked);
+//     out-of-range tokens, blocks or slots are masked and read a zero row,
+//     so every load is unconditional and all of them are issued together);
 //   * QK^T: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 tokens, source 0 =
 //     the group's Q rows (heads, padded to 16 with zeros), source 1 = 16 K
 //     rows loaded straight from the cache. Lane l then holds the scores of
 //     heads 4(l/16)..+3 for token l%16 of the subtile, so every head's
 //     maximum and sum over the tile are reductions over one 16-lane DPP row;
 //   * PV on the VALU in fp32: 16 lanes cover the 128 values of one V row
-//     (8 bytes each, one coalesced 128-byte read), four rows in flight, and
-//     each lane accumulates G x 8 outputs; p comes from LDS.
+//     (8 bytes each, one coalesced 128-byte read), four rows per load
+//     instruction (each 16-lane group walks 16 consecutive tokens), and each
+//     lane accumulates G x 8 outputs; p comes from LDS.
 // The cache reads are the bound (K and V, 256 bytes per token and KV head).
 #include "common.h"
 #include "quant_common.h"
@@ -38,6 +45,14 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kHeadDim = 128;
 constexpr float kLog2eAttn = 1.44269504088896341f;
+
+// what a masked token reads in place of its K and V rows
+__device__ const uint32_t kZeroRow[kHeadDim / 4] = {};
+
+// A cache row pointer marked as global memory, so that its loads are global
+// (not flat) loads and do not hold up the LDS waits of the loop.
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+__device__ __forceinline__ gbytes as_global(const uint8_t* p) { return (gbytes)p; }
 
 __device__ __forceinline__ float row16_max_f(float v) {
   v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
@@ -61,24 +76,37 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int G>  // query heads per KV head: 1, 2, 4 or 8
+template <int G, bool SPLIT>  // G = query heads per KV head: 1, 2, 4 or 8
 __global__ __launch_bounds__(256) void decode_attention_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, int64_t Hkv, const uint8_t* __restrict__ k_cache,
     const uint8_t* __restrict__ v_cache, int64_t num_slots, const int32_t* __restrict__ block_table,
     int64_t max_blocks, int64_t block_size, const int32_t* __restrict__ context_lens,
     const float* __restrict__ q_scale, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
-    float sm_scale, uint16_t* __restrict__ out, int64_t ldo) {
+    float sm_scale, uint16_t* __restrict__ out, int64_t ldo, int64_t splits, int64_t chunk,
+    float* __restrict__ ws_acc, float* __restrict__ ws_ml, int64_t nchunks) {
   constexpr int D = kHeadDim;
   __shared__ __attribute__((aligned(16))) uint32_t q8[G * D / 4];
-  __shared__ int32_t slot_tile[4][64];
+  __shared__ __attribute__((aligned(16))) int32_t slot_tile[4][64];
   __shared__ __attribute__((aligned(16))) float ptile[4][64][G];
   __shared__ float m_w[4][G], l_w[4][G];
   __shared__ __attribute__((aligned(16))) float acc_w[4][G][D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t b = blockIdx.x / Hkv, gk = blockIdx.x % Hkv;
+  // XCD-aware order: workgroups go to the 8 XCDs round-robin, so XCD x runs
+  // blocks x, x+8, x+16, ...; those are mapped to the KV heads 0..Hkv-1 of
+  // chunks x, x+8, ... in turn. All heads of one chunk then run at the same
+  // time on one XCD and read the same cache pages together (a token's heads
+  // are adjacent in a slot), and the chunks of a sequence spread over XCDs.
+  const int64_t xcd = blockIdx.x % 8, xi = blockIdx.x / 8;
+  const int64_t gk = xi % Hkv, cidx = (xi / Hkv) * 8 + xcd;  // chunk cidx = b * splits + s
+  if (cidx >= nchunks) return;                                 // padding of the last group of 8
+  const int64_t b = cidx / splits, sidx = cidx % splits;
+  const int64_t wg = (b * Hkv + gk) * splits + sidx;          // partial index (split mode)
   const int64_t L = context_lens[b] > 0 ? context_lens[b] : 0;
+  const int64_t c0 = SPLIT ? sidx * chunk : 0;  // this workgroup's tokens [c0, c1)
+  const int64_t c1 = SPLIT ? (L < c0 + chunk ? L : c0 + chunk) : L;
+  if (SPLIT && c0 >= L) return;  // an empty chunk (uniform over the workgroup); the merge skips it
   const float qs = *q_scale, ks = *k_scale, vs = *v_scale;
 
   // Q of the group's G heads -> E4M3 codes in LDS
@@ -102,6 +130,9 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
   }
   const float s2scale = qs * ks * sm_scale * kLog2eAttn;  // scores in the log2 domain
   const int64_t row_bytes = Hkv * D;                    // one slot of one cache
+  const uint8_t* const kbase = k_cache + gk * D;
+  const uint8_t* const vbase = v_cache + gk * D;
+  const uint8_t* const zero = reinterpret_cast<const uint8_t*>(kZeroRow);
 
   // running state: lane group g holds heads 4g..4g+3 (entries r < 4)
   float m_run[4], l_run[4];
@@ -116,98 +147,160 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
 
-  for (int64_t t0 = (int64_t)wave * 64; t0 < L; t0 += 256) {  // uniform over the wave
-    {  // slots of the tile's tokens
-      const int64_t t = t0 + lane;
-      int32_t slot = -1;
-      if (t < L && t / block_size < max_blocks) {
-        const int64_t blk = block_table[b * max_blocks + t / block_size];
-        const int64_t s = blk * block_size + t % block_size;
-        if (blk >= 0 && s < num_slots) slot = (int32_t)s;
-      }
-      slot_tile[wave][lane] = slot;
-    }
+  // Software pipeline over this wave's tiles (tokens t0..t0+63, t0 advancing
+  // by 256): while tile i is computed, the K and V rows of tile i+1 and the
+  // block-table entries of tile i+2 are in flight. Loads past the last tile
+  // read the zero row (their tokens are masked), so every load is
+  // unconditional and the wait counts are the same in every iteration.
+  const uint32_t bs32 = (uint32_t)block_size;
+  const int32_t* const table_row = block_table + b * max_blocks;
+  auto table_entry = [&](int64_t t) {  // the block id of token t (block index clamped)
+    const uint32_t bi = (uint32_t)t / bs32;
+    return table_row[bi < (uint64_t)max_blocks ? bi : max_blocks - 1];
+  };
+  auto token_slot = [&](int64_t t, int32_t blk) {  // -1 for a masked token
+    const uint32_t bi = (uint32_t)t / bs32;
+    const int64_t s = (int64_t)blk * block_size + ((uint32_t)t - bi * bs32);
+    return (t < c1 && bi < (uint64_t)max_blocks && blk >= 0 && s < num_slots) ? (int32_t)s : -1;
+  };
+  int32_t kslot[4], vslot[16];
+  auto read_slots = [&](int32_t slot) {  // exchange the tile's slots through LDS
+    slot_tile[wave][lane] = slot;
     wave_lds_sync();
-
-    // QK^T: scores (log2 domain) of heads 4g+r, tokens 16u + c16
-    float s[4][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) kslot[u] = slot_tile[wave][16 * u + c16];
+#pragma unroll
+    for (int k = 0; k < 16; k += 4) {
+      const int4 v4 = *reinterpret_cast<const int4*>(&slot_tile[wave][16 * g + k]);
+      vslot[k] = v4.x;
+      vslot[k + 1] = v4.y;
+      vslot[k + 2] = v4.z;
+      vslot[k + 3] = v4.w;
+    }
+  };
+  // K rows of tokens 16u + c16 (bytes 16g..+15 and 64+16g..+15), kept in the
+  // cache hierarchy: the two halves of each row are read by two loads
+  u32x4 klo[4], khi[4];
+  const uint32_t row32 = (uint32_t)row_bytes;  // < 2^31 (checked on the host), as is every slot
+  auto row_or_zero = [&](const uint8_t* base, int32_t slot) {  // branch-free: one 32x32->64 multiply-add
+    const uint8_t* p = base + (uint64_t)(uint32_t)(slot > 0 ? slot : 0) * row32;
+    return as_global(slot >= 0 ? p : zero);
+  };
+  auto load_k = [&]() {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int32_t slot = slot_tile[wave][16 * u + c16];
-      v8i kfrag = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-      if (slot >= 0) {
-        const uint8_t* kr = k_cache + (int64_t)slot * row_bytes + gk * D;
-        const u32x4 lo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 16 * g));
-        const u32x4 hi = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kr + 64 + 16 * g));
-        kfrag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
-      }
-      const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qfrag, kfrag, v4f{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                     0, 127, 0, 127);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) s[u][r] = slot >= 0 ? d[r] * s2scale : -INFINITY;
+      const gbytes kr = row_or_zero(kbase, kslot[u]);
+      klo[u] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kr + 16 * g);
+      khi[u] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kr + 64 + 16 * g);
     }
+  };
+  // V rows of tokens 16g + k, bytes 8 c16..+7: each row is read once (streamed)
+  auto load_v = [&](int k) {
+    const gbytes vr = row_or_zero(vbase, vslot[k]);
+    return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(vr + 8 * c16));
+  };
 
-    // online softmax per head (lane group g, entry r): tile maximum over the
-    // 64 tokens = 4 subtiles x the 16 lanes of the row
-    float alpha[4];
+  int64_t t0 = c0 + (int64_t)wave * 64;
+  if (t0 < c1) {  // uniform over the wave
+    int32_t blk = table_entry(t0 + lane);
+    const int32_t slot0 = token_slot(t0 + lane, blk);
+    blk = table_entry(t0 + 256 + lane);  // tile i+1's entries
+    read_slots(slot0);
+    load_k();
+    u32x2 vw[16];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float mt = fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r]));
-      mt = row16_max_f(mt);
-      const float mn = fmaxf(m_run[r], mt);
-      const float ms = mn == -INFINITY ? 0.f : mn;  // no token yet: keep exp2 finite
-      alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - ms);
-      float psum = 0.f;
+    for (int k = 0; k < 16; ++k) vw[k] = load_v(k);
+
+    for (;;) {
+      // QK^T: scores (log2 domain) of heads 4g+r, tokens 16u + c16
+      float s[4][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        s[u][r] = __builtin_amdgcn_exp2f(s[u][r] - ms);
-        psum += s[u][r];
+        const v8i kfrag = v8i{(int)klo[u].x, (int)klo[u].y, (int)klo[u].z, (int)klo[u].w,
+                              (int)khi[u].x, (int)khi[u].y, (int)khi[u].z, (int)khi[u].w};
+        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qfrag, kfrag, v4f{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                       0, 0, 127, 0, 127);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[u][r] = kslot[u] >= 0 ? d[r] * s2scale : -INFINITY;
       }
-      l_run[r] = l_run[r] * alpha[r] + row16_sum_f(psum);
-      m_run[r] = mn;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (4 * g + r < G) ptile[wave][16 * u + c16][4 * g + r] = s[u][r];
-    wave_lds_sync();
+      // the scheduling barriers keep each stage's loads after the last use
+      // of the registers they overwrite (one register set per stage)
+      __builtin_amdgcn_sched_barrier(0);
 
-    // PV: lane = (token phase j = g, value chunk c16); rescale, then 16 tokens
-    float al[G];
+      // next tile: its slots (entries loaded one tile ago), the entries of
+      // the tile after it, its K rows
+      const int64_t tn = t0 + 256;
+      const int32_t slot_n = token_slot(tn + lane, blk);
+      blk = table_entry(tn + 256 + lane);
+      read_slots(slot_n);
+      load_k();
+      __builtin_amdgcn_sched_barrier(0);
+
+      // online softmax per head (lane group g, entry r): tile maximum over
+      // the 64 tokens = 4 subtiles x the 16 lanes of the row
+      float alpha[4];
 #pragma unroll
-    for (int h = 0; h < G; ++h)  // head h's factor lives in lane group h/4, entry h%4
-      al[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
+      for (int r = 0; r < 4; ++r) {
+        float mt = fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r]));
+        mt = row16_max_f(mt);
+        const float mn = fmaxf(m_run[r], mt);
+        const float ms = mn == -INFINITY ? 0.f : mn;  // no token yet: keep exp2 finite
+        alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - ms);
+        float psum = 0.f;
 #pragma unroll
-    for (int h = 0; h < G; ++h)
+        for (int u = 0; u < 4; ++u) {
+          s[u][r] = __builtin_amdgcn_exp2f(s[u][r] - ms);
+          psum += s[u][r];
+        }
+        l_run[r] = l_run[r] * alpha[r] + row16_sum_f(psum);
+        m_run[r] = mn;
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
-#pragma unroll 4
-    for (int k = 0; k < 16; ++k) {
-      const int tl = g + 4 * k;
-      const int32_t slot = slot_tile[wave][tl];
-      if (slot >= 0) {
-        const u32x2 vw = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x2*>(v_cache + (int64_t)slot * row_bytes + gk * D + 8 * c16));
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (4 * g + r < G) ptile[wave][16 * u + c16][4 * g + r] = s[u][r];
+      wave_lds_sync();
+
+      // PV: lane = (tokens 16g..16g+15, value chunk c16); rescale, then the
+      // 16 tokens (masked tokens have p = 0 and read zeros). Each V register
+      // is reloaded with the next tile's row as soon as it is consumed.
+      float al[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h)  // head h's factor lives in lane group h/4, entry h%4
+        al[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
+      // p of this lane's tokens, one token ahead of its use
+      typedef float pvec __attribute__((ext_vector_type(G)));
+      const pvec* prow = reinterpret_cast<const pvec*>(&ptile[wave][16 * g][0]);
+      pvec pn = prow[0];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const pvec p = pn;
+        if (k < 15) pn = prow[k + 1];
         float v[8];
-        const f32x2 v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw.x, false);
-        const f32x2 v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw.x, true);
-        const f32x2 v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw.y, false);
-        const f32x2 v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw.y, true);
+        const f32x2 v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k].x, false);
+        const f32x2 v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k].x, true);
+        const f32x2 v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k].y, false);
+        const f32x2 v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k].y, true);
+        vw[k] = load_v(k);
         v[0] = v0.x; v[1] = v0.y; v[2] = v1.x; v[3] = v1.y;
         v[4] = v2.x; v[5] = v2.y; v[6] = v3.x; v[7] = v3.y;
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const float p = ptile[wave][tl][h];
+        for (int h = 0; h < G; ++h)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(p, v[e], acc[h][e]);
-        }
+          for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(p[h], v[e], acc[h][e]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      t0 = tn;
+      if (t0 >= c1) break;
     }
-    wave_lds_sync();  // the next tile overwrites slot_tile and ptile
   }
 
-  // this wave's totals: sum the four token phases (lanes c16, +16, +32, +48)
+  // this wave's totals: sum the four token groups (lanes c16, +16, +32, +48)
 #pragma unroll
   for (int h = 0; h < G; ++h)
 #pragma unroll
@@ -245,21 +338,76 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       wsc[w] = __builtin_amdgcn_exp2f(m_w[w][h] - ms);
       lsum += l_w[w][h] * wsc[w];
     }
-    const float inv = lsum > 0.f ? vs / lsum : 0.f;
-    uint32_t packed[4];
+    float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; e += 2) {
-      float o0 = 0.f, o1 = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      o[e] = 0.f;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        o0 = __builtin_fmaf(acc_w[w][h][8 * ch + e], wsc[w], o0);
-        o1 = __builtin_fmaf(acc_w[w][h][8 * ch + e + 1], wsc[w], o1);
-      }
-      packed[e / 2] = (uint32_t)to_bf16_bits(o0 * inv) | ((uint32_t)to_bf16_bits(o1 * inv) << 16);
+      for (int w = 0; w < 4; ++w) o[e] = __builtin_fmaf(acc_w[w][h][8 * ch + e], wsc[w], o[e]);
     }
-    *reinterpret_cast<uint4*>(out + b * ldo + (gk * G + h) * D + 8 * ch) =
-        make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    if (SPLIT) {  // partial of this chunk: unnormalized output, maximum, sum
+      float4* dst = reinterpret_cast<float4*>(ws_acc + (wg * G + h) * D + 8 * ch);
+      dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+      if (ch == 0) *reinterpret_cast<float2*>(ws_ml + (wg * G + h) * 2) = make_float2(m, lsum);
+    } else {
+      const float inv = lsum > 0.f ? vs / lsum : 0.f;
+      uint32_t packed[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2)
+        packed[e / 2] = (uint32_t)to_bf16_bits(o[e] * inv) | ((uint32_t)to_bf16_bits(o[e + 1] * inv) << 16);
+      *reinterpret_cast<uint4*>(out + b * ldo + (gk * G + h) * D + 8 * ch) =
+          make_uint4(packed[0], packed[1], packed[2], packed[3]);
+    }
   }
+}
+
+// Merge of the chunk partials of one (sequence, query head): one wave, two
+// output values per lane.
+__global__ __launch_bounds__(64) void decode_attention_combine_kernel(
+    const float* __restrict__ ws_acc, const float* __restrict__ ws_ml, int64_t splits, int64_t chunk, int64_t Hq,
+    int64_t Hkv, const int32_t* __restrict__ context_lens, const float* __restrict__ v_scale,
+    uint16_t* __restrict__ out, int64_t ldo) {
+  const int lane = threadIdx.x;
+  const int64_t b = blockIdx.x / Hq, h = blockIdx.x % Hq;
+  const int64_t G = Hq / Hkv, gk = h / G, hh = h % G;
+  const int64_t L = context_lens[b] > 0 ? context_lens[b] : 0;
+  const int64_t full = (L + chunk - 1) / chunk;
+  const int64_t n = full < splits ? full : splits;
+  const int64_t p0 = (b * Hkv + gk) * splits;  // partial index of chunk 0
+  float m = -INFINITY;
+  for (int64_t s = 0; s < n; ++s) m = fmaxf(m, ws_ml[((p0 + s) * G + hh) * 2]);
+  const float ms = m == -INFINITY ? 0.f : m;
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int64_t s = 0; s < n; ++s) {
+    const float2 ml = *reinterpret_cast<const float2*>(ws_ml + ((p0 + s) * G + hh) * 2);
+    const float w = __builtin_amdgcn_exp2f(ml.x - ms);
+    const float2 a = *reinterpret_cast<const float2*>(ws_acc + ((p0 + s) * G + hh) * kHeadDim + 2 * lane);
+    lsum = __builtin_fmaf(ml.y, w, lsum);
+    o0 = __builtin_fmaf(a.x, w, o0);
+    o1 = __builtin_fmaf(a.y, w, o1);
+  }
+  const float inv = lsum > 0.f ? *v_scale / lsum : 0.f;
+  *reinterpret_cast<uint32_t*>(out + b * ldo + h * kHeadDim + 2 * lane) =
+      (uint32_t)to_bf16_bits(o0 * inv) | ((uint32_t)to_bf16_bits(o1 * inv) << 16);
+}
+
+constexpr int64_t kSplitUnit = 256;  // chunk sizes are multiples of one tile per wave
+constexpr int64_t kFillWGs = 256;    // one workgroup per CU keeps the cache reads at their best
+
+// Tokens per chunk for the split path: the caller's, else (automatic) the
+// whole addressable context -- no split -- when there are at least 256
+// (sequence, KV head) pairs, otherwise chunks sized so that about 256
+// workgroups run (a measured optimum: the direct path reaches its best
+// bandwidth with one workgroup per CU, and small chunks lose to the
+// pipeline start and the merge).
+int64_t split_chunk(int64_t B, int64_t Hkv, int64_t Lcap, int64_t split_tokens) {
+  if (split_tokens > 0) return split_tokens;
+  const int64_t pairs = B * Hkv;
+  if (pairs >= kFillWGs) return ((Lcap + kSplitUnit - 1) / kSplitUnit) * kSplitUnit;
+  const int64_t splits = (kFillWGs + pairs - 1) / pairs;
+  const int64_t c = (Lcap + splits - 1) / splits;
+  return ((c + kSplitUnit - 1) / kSplitUnit) * kSplitUnit;
 }
 
 }  // namespace
@@ -267,37 +415,98 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
 
 using namespace fp8blk;
 
+namespace {
+
+// Shape checks shared by the workspace query and the call.
+fp8blk_status attention_shape(int64_t B, int64_t Hq, int64_t Hkv, int64_t D, int64_t max_blocks,
+                              int64_t block_size, int64_t split_tokens) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || max_blocks < 1 || block_size < 1 || split_tokens < 0)
+    return FP8BLK_ERR_INVALID_ARG;
+  const int64_t G = Hq / Hkv;
+  if (D != kHeadDim || Hq % Hkv || (G != 1 && G != 2 && G != 4 && G != 8) || split_tokens % kSplitUnit ||
+      max_blocks > INT32_MAX || block_size > INT32_MAX || B * Hq > INT32_MAX)
+    return FP8BLK_ERR_SHAPE;
+  return FP8BLK_OK;
+}
+
+// Chunks per (sequence, KV head) for the split path (1: direct).
+int64_t attention_splits(int64_t B, int64_t Hkv, int64_t max_blocks, int64_t block_size, int64_t split_tokens,
+                         int64_t* chunk) {
+  const int64_t cap = max_blocks * block_size;  // tokens the block table can address
+  const int64_t lcap = cap < INT32_MAX ? cap : INT32_MAX;
+  *chunk = split_chunk(B, Hkv, lcap, split_tokens);
+  return (lcap + *chunk - 1) / *chunk;
+}
+
+}  // namespace
+
+extern "C" size_t fp8blk_decode_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                                          int64_t max_blocks, int64_t block_size,
+                                                          int64_t split_tokens) {
+  if (attention_shape(B, Hq, Hkv, D, max_blocks, block_size, split_tokens) != FP8BLK_OK || B == 0) return 0;
+  int64_t chunk;
+  const int64_t splits = attention_splits(B, Hkv, max_blocks, block_size, split_tokens, &chunk);
+  if (splits <= 1) return 0;
+  return (size_t)(B * Hq * splits) * (kHeadDim + 2) * sizeof(float);
+}
+
+
 extern "C" fp8blk_status fp8blk_decode_attention(const uint16_t* q, int64_t ldq, int64_t B, int64_t Hq, int64_t Hkv,
                                                  int64_t D, const uint8_t* k_cache, const uint8_t* v_cache,
                                                  int64_t num_slots, const int32_t* block_table, int64_t max_blocks,
                                                  int64_t block_size, const int32_t* context_lens,
                                                  const float* q_scale, const float* k_scale, const float* v_scale,
-                                                 float sm_scale, uint16_t* out, int64_t ldo, hipStream_t stream) {
-  if (B < 0 || Hq < 1 || Hkv < 1 || D < 1 || num_slots < 0 || max_blocks < 1 || block_size < 1 ||
-      !(sm_scale == sm_scale) || ldq < Hq * D || ldo < Hq * D)
-    return FP8BLK_ERR_INVALID_ARG;
-  const int64_t G = Hq / Hkv;
-  if (D != kHeadDim || Hq % Hkv || (G != 1 && G != 2 && G != 4 && G != 8) || ldq % 8 || ldo % 8)
-    return FP8BLK_ERR_SHAPE;
+                                                 float sm_scale, uint16_t* out, int64_t ldo, int64_t split_tokens,
+                                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  fp8blk_status st = attention_shape(B, Hq, Hkv, D, max_blocks, block_size, split_tokens);
+  if (st != FP8BLK_OK) return st;
+  if (num_slots < 0 || !(sm_scale == sm_scale) || ldq < Hq * D || ldo < Hq * D) return FP8BLK_ERR_INVALID_ARG;
+  if (ldq % 8 || ldo % 8 || num_slots > INT32_MAX || Hkv * D > INT32_MAX) return FP8BLK_ERR_SHAPE;
   if (B == 0) return FP8BLK_OK;
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !q_scale || !k_scale || !v_scale || !out)
     return FP8BLK_ERR_INVALID_ARG;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(q_scale, 4) || !aligned(k_scale, 4) ||
-      !aligned(v_scale, 4))
+      !aligned(v_scale, 4) || !aligned(workspace, 16))
     return FP8BLK_ERR_ALIGNMENT;
-  if (B * Hkv > INT32_MAX || num_slots > INT32_MAX) return FP8BLK_ERR_SHAPE;
-  const dim3 grid((uint32_t)(B * Hkv));
-#define FP8BLK_ATTN_LAUNCH(GV)                                                                                     \
-  hipLaunchKernelGGL(decode_attention_kernel<GV>, grid, dim3(256), 0, stream, q, ldq, Hkv, k_cache, v_cache,         \
-                     num_slots, block_table, max_blocks, block_size, context_lens, q_scale, k_scale, v_scale,       \
-                     sm_scale, out, ldo)
-  switch (G) {
-    case 1: FP8BLK_ATTN_LAUNCH(1); break;
-    case 2: FP8BLK_ATTN_LAUNCH(2); break;
-    case 4: FP8BLK_ATTN_LAUNCH(4); break;
-    default: FP8BLK_ATTN_LAUNCH(8); break;
+  const int64_t G = Hq / Hkv;
+  int64_t chunk = 0, splits = 1;
+  float *ws_acc = nullptr, *ws_ml = nullptr;
+  if (workspace) {
+    splits = attention_splits(B, Hkv, max_blocks, block_size, split_tokens, &chunk);
+    if (splits > 1) {
+      const size_t need = (size_t)(B * Hq * splits) * (kHeadDim + 2) * sizeof(float);
+      if (workspace_bytes < need) return FP8BLK_ERR_INVALID_ARG;
+      ws_acc = static_cast<float*>(workspace);
+      ws_ml = ws_acc + B * Hq * splits * kHeadDim;
+    }
   }
+  const bool split = splits > 1;
+  const int64_t nchunks = B * splits;
+  const int64_t blocks = ((nchunks + 7) / 8) * 8 * Hkv;  // a multiple of 8 for the XCD-aware order
+  if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  const dim3 grid((uint32_t)blocks);
+#define FP8BLK_ATTN_LAUNCH(GV, SV)                                                                                 \
+  hipLaunchKernelGGL((decode_attention_kernel<GV, SV>), grid, dim3(256), 0, stream, q, ldq, Hkv, k_cache, v_cache,  \
+                     num_slots, block_table, max_blocks, block_size, context_lens, q_scale, k_scale, v_scale,       \
+                     sm_scale, out, ldo, splits, chunk, ws_acc, ws_ml, nchunks)
+#define FP8BLK_ATTN_G(SV)                  \
+  switch (G) {                             \
+    case 1: FP8BLK_ATTN_LAUNCH(1, SV); break; \
+    case 2: FP8BLK_ATTN_LAUNCH(2, SV); break; \
+    case 4: FP8BLK_ATTN_LAUNCH(4, SV); break; \
+    default: FP8BLK_ATTN_LAUNCH(8, SV); break; \
+  }
+  if (split) {
+    FP8BLK_ATTN_G(true)
+    st = launch_status();
+    if (st != FP8BLK_OK) return st;
+    hipLaunchKernelGGL(decode_attention_combine_kernel, dim3((uint32_t)(B * Hq)), dim3(64), 0, stream, ws_acc,
+                       ws_ml, splits, chunk, Hq, Hkv, context_lens, v_scale, out, ldo);
+  } else {
+    FP8BLK_ATTN_G(false)
+  }
+#undef FP8BLK_ATTN_G
 #undef FP8BLK_ATTN_LAUNCH
   return launch_status();
 }

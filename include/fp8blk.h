@@ -288,11 +288,23 @@ fp8blk_status fp8blk_kv_cache_write(const uint16_t* k, const uint16_t* v, int64_
  *   q_scale, k_scale, v_scale: one fp32 each (device)
  *   sm_scale     softmax scale (1/sqrt(D) for standard attention)
  *   out          [B][ldo] bf16 out: Hq heads x D per row (16-byte aligned)
+ *   split_tokens 0 (the library picks) or a multiple of 256: tokens per chunk
+ *                when the context is split (see workspace)
+ *   workspace    NULL: one workgroup per (sequence, KV head) covers the whole
+ *                context and writes out directly. Otherwise device memory of
+ *                at least fp8blk_decode_attention_workspace_size(...) bytes
+ *                (16-byte aligned, owned by the caller, contents undefined on
+ *                entry and exit): each context is cut into chunks of
+ *                split_tokens tokens processed in parallel, their fp32
+ *                partials (maximum, sum, unnormalized output per head) are
+ *                kept here and merged by a second kernel on the same stream.
+ *                Calls that share a workspace must be ordered on one stream.
  *   D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}; ldq and ldo
  *   multiples of 8 and >= Hq*D; B >= 0 (0: no-op); block_size, max_blocks >= 1.
  * Tokens whose block index is past max_blocks, whose block id is negative or
  * whose slot is past num_slots are skipped; a sequence without tokens gives
- * zeros.
+ * zeros. A workspace smaller than the size query's value is
+ * FP8BLK_ERR_INVALID_ARG.
  */
 fp8blk_status fp8blk_decode_attention(const uint16_t* q, int64_t ldq, int64_t B, int64_t Hq,
                                       int64_t Hkv, int64_t D, const uint8_t* k_cache,
@@ -301,7 +313,20 @@ fp8blk_status fp8blk_decode_attention(const uint16_t* q, int64_t ldq, int64_t B,
                                       int64_t block_size, const int32_t* context_lens,
                                       const float* q_scale, const float* k_scale,
                                       const float* v_scale, float sm_scale,
-                                      uint16_t* out, int64_t ldo, hipStream_t stream);
+                                      uint16_t* out, int64_t ldo, int64_t split_tokens,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/*
+ * Workspace bytes fp8blk_decode_attention needs with these arguments for the
+ * split path (host only, no HIP call). 0 when the context is not split (the
+ * block table addresses at most one chunk) or the arguments are invalid.
+ * The chunk count depends only on B, Hkv, max_blocks * block_size and
+ * split_tokens, never on the context lengths.
+ */
+size_t fp8blk_decode_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv, int64_t D,
+                                              int64_t max_blocks, int64_t block_size,
+                                              int64_t split_tokens);
 
 /* Static, NUL-terminated description of a status code (host memory). */
 const char* fp8blk_status_string(fp8blk_status status);

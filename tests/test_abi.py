@@ -37,7 +37,7 @@ def test_header_declares_the_boundary():
         "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
         "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_qkv_amax", "fp8blk_kv_scales",
         "fp8blk_kv_cache_write", "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
-        "fp8blk_decode_attention", "fp8blk_status_string"])
+        "fp8blk_decode_attention", "fp8blk_decode_attention_workspace_size", "fp8blk_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -232,8 +232,8 @@ def test_gemm_rowscaled_validation(lib):
 def test_decode_attention_validation(lib):
     f = lib.fp8blk_decode_attention
     names = ["q", "ldq", "B", "Hq", "Hkv", "D", "kc", "vc", "slots", "table", "max_blocks", "bs", "lens",
-             "qs", "ks", "vs", "sm", "out", "ldo", "stream"]
-    ok = [P, 4096, 4, 32, 8, 128, P, P, 1024, P, 16, 16, P, P, P, P, 0.088, P, 4096, NULL]
+             "qs", "ks", "vs", "sm", "out", "ldo", "split", "ws", "ws_bytes", "stream"]
+    ok = [P, 4096, 4, 32, 8, 128, P, P, 1024, P, 16, 16, P, P, P, P, 0.088, P, 4096, 0, NULL, 0, NULL]
 
     def call(**kw):
         a = list(ok)
@@ -255,6 +255,29 @@ def test_decode_attention_validation(lib):
     for name, bad in (("q", P4), ("kc", P4), ("out", P4), ("table", P + 2), ("qs", P + 1)):
         assert call(**{name: bad}) == ALIGN, name
     assert call(B=0, q=NULL, out=NULL) == OK
+    assert call(split=-256) == INVALID
+    assert call(split=100) == SHAPE                        # not a multiple of 256
+    assert call(ws=P + 8, ws_bytes=1 << 30) == ALIGN
+    need = lib.fp8blk_decode_attention_workspace_size(4, 32, 8, 128, 256, 16, 0)
+    assert need > 0
+    assert call(max_blocks=256, ws=P, ws_bytes=need - 4) == INVALID   # workspace too small
+
+
+def test_decode_attention_workspace_size(lib):
+    size = lib.fp8blk_decode_attention_workspace_size
+    # 4 sequences, 32/8 heads, 16 blocks of 16 tokens: one 256-token chunk -> not split
+    assert size(4, 32, 8, 128, 16, 16, 0) == 0
+    # 4096 addressable tokens, 32 (sequence, KV head) pairs: the automatic
+    # chunk brings the grid to 256 workgroups (8 chunks of 512); partials of
+    # (128 + 2) floats per query head and chunk
+    assert size(4, 32, 8, 128, 256, 16, 0) == 4 * 32 * 8 * 130 * 4
+    assert size(4, 32, 8, 128, 256, 16, 1024) == 4 * 32 * 4 * 130 * 4
+    # 256 x 8 pairs fill the chip without splitting
+    assert size(256, 32, 8, 128, 256, 16, 0) == 0
+    assert size(256, 32, 8, 128, 256, 16, 256) == 256 * 32 * 16 * 130 * 4
+    assert size(4, 32, 8, 64, 256, 16, 0) == 0             # D != 128
+    assert size(4, 32, 8, 128, 256, 16, 100) == 0          # split not a multiple of 256
+    assert size(0, 32, 8, 128, 256, 16, 0) == 0
 
 
 def test_python_entry_points_raise(lib):

@@ -33,11 +33,16 @@ def build(lens, hq, hkv, seed=0, bs=16):
     return a, kc, vc, scales
 
 
-def run(a, kc, vc, scales, sm=None):
+MODES = {"direct": dict(split=False), "split_auto": dict(split=True),
+         "split_256": dict(split=True, split_tokens=256), "split_512": dict(split=True, split_tokens=512)}
+
+
+def run(a, kc, vc, scales, sm=None, mode="split_auto"):
     b, hq = a["q"].shape[0], a["q"].shape[1]
     out, check = guarded((b, hq, D), torch.bfloat16, DEV)
     fb.decode_attention(a["q"].to(DEV), kc, vc, a["block_table"].to(DEV), a["block_size"],
-                        a["context_lens"].to(DEV), scales[0:1], scales[1:2], scales[2:3], sm_scale=sm, out=out)
+                        a["context_lens"].to(DEV), scales[0:1], scales[1:2], scales[2:3], sm_scale=sm, out=out,
+                        **MODES[mode])
     check()
     return out
 
@@ -48,17 +53,41 @@ def reference(a, kc, vc, scales, sm=None):
                                        a["block_size"], a["context_lens"].numpy(), s[0], s[1], s[2], sm)
 
 
+@pytest.mark.parametrize("mode", list(MODES))
 @pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (32, 8), (32, 4)])
-def test_context_lengths_and_groups(fp8blk_lib, hq, hkv):
+def test_context_lengths_and_groups(fp8blk_lib, hq, hkv, mode):
     """Context lengths 0, 1, a partial 16-token subtile, one and two 64-token
-    tiles, more tiles than waves, ragged tails; every head-group size."""
-    lens = [0, 1, 15, 64, 65, 300, 1000, 257]
+    tiles, more tiles than waves, ragged tails, both sides of the 256- and
+    512-token chunk edges; every head-group size; the direct path and the
+    split path with the automatic and two explicit chunk sizes."""
+    lens = [0, 1, 15, 64, 65, 300, 1000, 257, 255, 256, 511, 512, 513]
     a, kc, vc, sc = build(lens, hq, hkv, seed=hq + hkv)
-    out = run(a, kc, vc, sc)
+    out = run(a, kc, vc, sc, mode=mode)
     ref = reference(a, kc, vc, sc)
     assert torch.all(out[0].float() == 0)
     assert_within_tolerance(out.float().cpu().numpy().reshape(len(lens), -1), ref.reshape(len(lens), -1),
-                            what="decode attention")
+                            what="decode attention (%s)" % mode)
+
+
+def test_split_workspace_reuse_and_size(fp8blk_lib):
+    """One workspace serves calls of different shapes in a row; the size
+    query matches the chunking (partials of 130 floats per head and chunk)."""
+    a, kc, vc, sc = build([700, 20, 1300], 32, 8, seed=11)
+    b, mb = 3, a["block_table"].shape[1]
+    need = fb.fp8blk_decode_attention_workspace_size(b, 32, 8, D, mb, 16, 256)
+    assert need == b * 32 * ((mb * 16 + 255) // 256) * 130 * 4
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ref = reference(a, kc, vc, sc)
+    for _ in range(2):
+        out = torch.empty(b, 32, D, dtype=torch.bfloat16, device=DEV)
+        fb.decode_attention(a["q"].to(DEV), kc, vc, a["block_table"].to(DEV), 16, a["context_lens"].to(DEV),
+                            sc[0:1], sc[1:2], sc[2:3], out=out, split_tokens=256, workspace=ws)
+        torch.cuda.synchronize()
+        assert_within_tolerance(out.float().cpu().numpy().reshape(b, -1), ref.reshape(b, -1), what="reuse")
+    small = torch.empty(16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(fb.Fp8BlkError):
+        fb.decode_attention(a["q"].to(DEV), kc, vc, a["block_table"].to(DEV), 16, a["context_lens"].to(DEV),
+                            sc[0:1], sc[1:2], sc[2:3], split_tokens=256, workspace=small)
 
 
 def test_softmax_scale_and_block_size(fp8blk_lib):
@@ -77,20 +106,22 @@ def test_single_token_is_its_value_row(fp8blk_lib):
     assert np.all(np.abs(out - ref) <= 2.0 ** -8 * np.abs(ref))
 
 
-def test_masked_tokens_are_skipped(fp8blk_lib):
+@pytest.mark.parametrize("mode", ["direct", "split_256"])
+def test_masked_tokens_are_skipped(fp8blk_lib, mode):
     """A negative block id, a block past the cache and a context longer than
     the block table: those tokens are left out, as if never cached."""
-    a, kc, vc, sc = build([40, 50, 20], 8, 4, seed=7)
+    a, kc, vc, sc = build([40, 50, 300], 8, 4, seed=7)
     table = a["block_table"].clone()
     table[0, 1] = -1                                   # tokens 16..31 of sequence 0
     table[1, 2] = a["num_slots"] // 16 + 5             # tokens 32..47 of sequence 1
     lens = a["context_lens"].clone()
-    lens[2] = 20 + 16 * table.shape[1]                 # past max_blocks * block_size
+    lens[2] = 300 + 16 * table.shape[1]                # past max_blocks * block_size
     b2 = dict(a, block_table=table, context_lens=lens)
-    out = run(b2, kc, vc, sc).float().cpu().numpy()
+    out = run(b2, kc, vc, sc, mode=mode).float().cpu().numpy()
     # the same attention on a cache holding only the kept tokens, repacked
     keep = {0: [t for t in range(40) if not 16 <= t < 32], 1: [t for t in range(50) if not 32 <= t < 48],
             2: list(range(16 * table.shape[1]))}
+    assert table.shape[1] == 19                        # sequence 2's 300 tokens fill its whole table row
     kcn, vcn = kc.cpu().numpy(), vc.cpu().numpy()
     rows_k, rows_v, new_table, new_lens, nxt = [], [], [], [], 0
     width = max(len(v) for v in keep.values())
