@@ -85,9 +85,13 @@ KERNEL_SOURCES = {"gemm_kernel": ("gemm.hip", "common.h"),
 QUANT_SOURCES = ("quant.hip", "quant_common.h", "common.h")
 
 
+ATTENTION_SOURCES = ("attention.hip", "quant_common.h", "common.h")
+
+
 def source_hash(kernel="gemm_kernel"):
     h = hashlib.sha256()
-    for name in KERNEL_SOURCES.get(kernel, QUANT_SOURCES):
+    names = ATTENTION_SOURCES if "decode_attention" in kernel else KERNEL_SOURCES.get(kernel, QUANT_SOURCES)
+    for name in names:
         with open(os.path.join(ROOT, "block_scaled_fp8_quant_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -511,6 +515,17 @@ def summarize_traffic(fetch_csv, write_csv):
                         "write_kib_per_dispatch": statistics.mean(kw), "dispatches": len(kf),
                         "bytes_per_launch": statistics.mean(kf) * 1024 * f_scale
                         + statistics.mean(kw) * 1024 * w_scale}
+    # decode attention: one record per instantiation (head-group size, split),
+    # e.g. "decode_attention_kernel<4, false>", and the merge kernel
+    for name in fetch:
+        if "decode_attention" not in name or name not in write:
+            continue
+        key = name.replace("void ", "").replace("fp8blk::(anonymous namespace)::", "").split("(")[0]
+        kf, kw = fetch[name], write[name]
+        kernels[key] = {"source_hash": source_hash(key), "fetch_kib_per_dispatch": statistics.mean(kf),
+                        "write_kib_per_dispatch": statistics.mean(kw), "dispatches": len(kf),
+                        "bytes_per_launch": statistics.mean(kf) * 1024 * f_scale
+                        + statistics.mean(kw) * 1024 * w_scale}
     g = kernels["gemm_kernel"]
     rec = {
         "source_hash": source_hash(),
@@ -645,8 +660,16 @@ def main():
         print("bench: timing the FP8 decode attention", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         out["attention"] = time_attention(fb, args.workload, dev, args.producer_reps)
+        import synth
+        g = synth.ATTENTION[args.workload][0] // synth.ATTENTION[args.workload][1]
+        direct = traffic_rec.get("decode_attention_kernel<%d, false>" % g, {}).get("bytes_per_launch")
+        part = traffic_rec.get("decode_attention_kernel<%d, true>" % g, {}).get("bytes_per_launch")
+        merge = traffic_rec.get("decode_attention_combine_kernel", {}).get("bytes_per_launch")
         for entry in out["attention"].values():
-            entry["traffic"] = None
+            # counters are kept per kernel, averaged over the mixes that ran it:
+            # the three direct-path mixes move the same algorithmic bytes within 0.4%
+            t = (part + merge if part is not None and merge is not None else None) if entry["split"] else direct
+            entry["traffic"] = None if t is None else round(t)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows)
