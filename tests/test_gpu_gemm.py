@@ -60,12 +60,23 @@ def test_integer_closed_form_is_exact(fp8blk_lib):
 @pytest.mark.parametrize("m,k,n", [
     (1, 128, 128), (7, 256, 384), (128, 128, 256), (130, 384, 128), (257, 1152, 640),
     (300, 512, 1024), (64, 4096, 256),
+    # at most 256 rows and >= 192 column tiles of 128: the 256x128 tile
+    (1, 384, 24576), (200, 256, 24576), (256, 128, 25600),
 ])
 def test_shapes_spanning_tiles(fp8blk_lib, m, k, n):
     g = synth.generator(7, seed=m + 3 * k + 5 * n)
     x = synth.activation(m, k, g, 0.005, 30.0)
     w = synth.weight(n, k, g)
     _layer_check(x, w)
+
+
+@pytest.mark.parametrize("m", [3, 256])
+def test_wide_few_rows_pow2(fp8blk_lib, m):
+    """The 256x128 tile with power-of-two scales (in-MFMA scaling)."""
+    g = synth.generator(9, seed=m)
+    x = synth.activation(m, 256, g, 0.01, 50.0)
+    w = synth.weight(24576, 256, g)
+    _layer_check(x, w, pow2=True)
 
 
 def test_zero_blocks_and_scale_doubling(fp8blk_lib):
