@@ -21,9 +21,9 @@ Readings taken where the pages are silent (each listed in the design doc):
       out[h, d] = sum_t softmax(s[h])_t dec(v8[t, g, d]) * v_scale
   rounded once to bf16 by the caller's comparison; a sequence with no
   cached tokens gives 0;
-* paged cache: token t of sequence b is in slot
-  block_table[b, t // block_size] * block_size + t % block_size of the
-  [slots, Hkv, D] caches written by the cache write.
+* paged cache: token t of sequence b is at offset t % block_size of page
+  block_table[b, t // block_size] of the [num_blocks, Hkv, block_size, D]
+  caches written by the cache write (head-major pages).
 
 Pins (tests/test_oracle_attention.py): one cached token returns its value
 row exactly; equal scores give the plain mean of the value rows; a dominant
@@ -41,16 +41,18 @@ from .quant import bf16_values
 
 def decode_attention_ref(q, k_cache, v_cache, block_table, block_size, context_lens, q_scale, k_scale, v_scale,
                          sm_scale=None):
-    """q [B, Hq, D] bf16; caches [slots, Hkv, D] E4M3 codes (uint8);
-    block_table [B, max_blocks] int; context_lens [B] int. Returns float64
-    [B, Hq, D]."""
+    """q [B, Hq, D] bf16; caches [num_blocks, Hkv, block_size, D] E4M3 codes
+    (uint8); block_table [B, max_blocks] int; context_lens [B] int. Returns
+    float64 [B, Hq, D]."""
     qv = bf16_values(q)
     b_, hq, d = qv.shape
     k_cache = np.asarray(k_cache, np.uint8)
     v_cache = np.asarray(v_cache, np.uint8)
+    if k_cache.ndim != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, Hkv, block_size, D] and alike")
     hkv = k_cache.shape[1]
-    if hq % hkv or k_cache.shape[2] != d or v_cache.shape != k_cache.shape:
-        raise ValueError("shapes: q [B, Hq, D], caches [slots, Hkv, D], Hq % Hkv == 0")
+    if hq % hkv or k_cache.shape[3] != d or k_cache.shape[2] != block_size:
+        raise ValueError("shapes: q [B, Hq, D], caches [num_blocks, Hkv, block_size, D], Hq % Hkv == 0")
     group = hq // hkv
     sm = 1.0 / np.sqrt(d) if sm_scale is None else float(np.float32(sm_scale))
     qs, ks, vs = (float(np.float32(s)) for s in (q_scale, k_scale, v_scale))
@@ -64,11 +66,11 @@ def decode_attention_ref(q, k_cache, v_cache, block_table, block_size, context_l
         if n == 0:
             continue
         t = np.arange(n)
-        slots = table[b, t // block_size] * block_size + t % block_size
+        blk, off = table[b, t // block_size], t % block_size
         for h in range(hq):
             g = h // group
-            s = (kd[slots, g, :] @ q8[b, h]) * qs * ks * sm
+            s = (kd[blk, g, off, :] @ q8[b, h]) * qs * ks * sm
             w = np.exp(s - s.max())
             w /= w.sum()
-            out[b, h] = (w @ vd[slots, g, :]) * vs
+            out[b, h] = (w @ vd[blk, g, off, :]) * vs
     return out

@@ -23,7 +23,9 @@ Readings taken where the pages are silent (each listed in the design doc):
 * cache entry = enc(RN32(x / s)) as for the linear layers, saturating at
   +-448 (tokens written after calibration may exceed the calibrated range;
   a quotient beyond the fp32 range saturates too); s = 0 gives +-0;
-* cache layout [num_slots][Hkv][D] per tensor; token t goes to slot
+* paged cache layout per tensor: [num_blocks][Hkv][block_size][D] -- each
+  page holds block_size tokens, head-major, so one head's rows of a page are
+  contiguous; slot = block * block_size + offset, and token t goes to slot
   slot[t]; a negative slot (padding) writes nothing; the slots of one call
   are distinct.
 
@@ -31,7 +33,7 @@ Pins (tests/test_oracle_kv_cache.py): maxima planted at known places and a
 brute-force Python scan; the per-tensor quantizer equals the pinned 1x128
 group quantizer when the tensor is one group; saturation and zero-scale
 cases; the dequantization error bound; the cache write against a per-token
-Python loop, with padding slots left untouched.
+Python loop over tokens and heads, with padding slots left untouched.
 """
 
 import numpy as np
@@ -72,18 +74,23 @@ def kv_quantize_ref(x, s):
 
 def kv_cache_write_ref(k, v, slot, k_cache, v_cache, k_scale, v_scale):
     """Write the quantized rows of k and v ([T, Hkv*D] bf16) into copies of
-    the caches ([num_slots, Hkv*D] uint8) at rows slot[t] (skipped when
-    negative). Returns the two new caches."""
+    the paged caches ([num_blocks, Hkv, block_size, D] uint8): head h of
+    token t goes to [slot[t] // block_size, h, slot[t] % block_size] (skipped
+    when slot[t] is negative). Returns the two new caches."""
     slot = np.asarray(slot, dtype=np.int64)
     kc = np.array(k_cache, dtype=np.uint8, copy=True)
     vc = np.array(v_cache, dtype=np.uint8, copy=True)
-    qk = kv_quantize_ref(k, k_scale)
-    qv = kv_quantize_ref(v, v_scale)
+    if kc.ndim != 4 or vc.shape != kc.shape:
+        raise ValueError("caches must be [num_blocks, Hkv, block_size, D] and alike")
+    nblk, hkv, bs, d = kc.shape
+    qk = kv_quantize_ref(k, k_scale).reshape(-1, hkv, d)
+    qv = kv_quantize_ref(v, v_scale).reshape(-1, hkv, d)
     live = slot >= 0
     if len(np.unique(slot[live])) != int(live.sum()):
         raise ValueError("slots of one call must be distinct")
-    if np.any(slot[live] >= kc.shape[0]):
+    if np.any(slot[live] >= nblk * bs):
         raise ValueError("slot out of range")
-    kc[slot[live]] = qk[live]
-    vc[slot[live]] = qv[live]
+    blk, off = slot[live] // bs, slot[live] % bs
+    kc[blk, :, off] = qk[live]
+    vc[blk, :, off] = qv[live]
     return kc, vc

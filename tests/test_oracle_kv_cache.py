@@ -82,23 +82,30 @@ def test_dequantization_error_bound():
 
 
 def test_cache_write_matches_token_loop():
+    """Head h of token i lands at page slot // 4, head h, row slot % 4 of the
+    head-major paged caches; every other row keeps its old bytes."""
     rng = np.random.default_rng(10)
-    t, hkv, d, slots = 9, 2, 8, 20
+    t, hkv, d, bs, nblk = 9, 2, 8, 4, 5
     k = bf16(rng.standard_normal((t, hkv * d)))
     v = bf16(rng.standard_normal((t, hkv * d)) * 7)
     slot = np.array([3, -1, 0, 19, 7, -1, 11, 4, 15])
-    kc0 = np.full((slots, hkv * d), 0xA5, np.uint8)
-    vc0 = np.full((slots, hkv * d), 0x5A, np.uint8)
+    kc0 = np.full((nblk, hkv, bs, d), 0xA5, np.uint8)
+    vc0 = np.full((nblk, hkv, bs, d), 0x5A, np.uint8)
     ks, vs = np.float32(0.01), np.float32(0.02)
     kc, vc = kv_cache_write_ref(k, v, slot, kc0, vc0, ks, vs)
     kv_, vv_ = oracle.bf16_values(k), oracle.bf16_values(v)
     for i in range(t):
         if slot[i] < 0:
             continue
-        for j in range(hkv * d):
-            assert kc[slot[i], j] == kv_quantize_ref(bf16([kv_[i, j]]), ks)[0]
-            assert vc[slot[i], j] == kv_quantize_ref(bf16([vv_[i, j]]), vs)[0]
-    untouched = np.setdiff1d(np.arange(slots), slot[slot >= 0])
-    assert np.all(kc[untouched] == 0xA5) and np.all(vc[untouched] == 0x5A)
+        page, row = divmod(int(slot[i]), bs)
+        for h in range(hkv):
+            for j in range(d):
+                assert kc[page, h, row, j] == kv_quantize_ref(bf16([kv_[i, h * d + j]]), ks)[0]
+                assert vc[page, h, row, j] == kv_quantize_ref(bf16([vv_[i, h * d + j]]), vs)[0]
+    for sl in np.setdiff1d(np.arange(nblk * bs), slot[slot >= 0]):
+        page, row = divmod(int(sl), bs)
+        assert np.all(kc[page, :, row] == 0xA5) and np.all(vc[page, :, row] == 0x5A)
     with pytest.raises(ValueError):
         kv_cache_write_ref(k, v, np.array([1, 1, 2, 3, 4, 5, 6, 7, 8]), kc0, vc0, ks, vs)
+    with pytest.raises(ValueError):
+        kv_cache_write_ref(k, v, np.array([20, -1, 0, 1, 2, 3, 4, 5, 6]), kc0, vc0, ks, vs)
