@@ -208,8 +208,9 @@ def time_producers(fb, P, reps):
 
 
 def build_kv(workload, dev):
-    """The workload's qkv projection output (one layer) and a KV cache of
-    2T slots, resident on the GPU, plus the scales and a slot permutation."""
+    """The workload's qkv projection output (one layer) and a paged KV cache
+    of 2T slots (pages of 16 tokens, head-major), resident on the GPU, plus
+    the scales and a slot permutation."""
     import torch
     import synth
     qkv, (hq, hkv, d) = synth.kv_inputs(workload)
@@ -220,13 +221,16 @@ def build_kv(workload, dev):
     return dict(qkv=dq, hq=hq, hkv=hkv, d=d, t=t, slot=slot,
                 amax=torch.empty(3, dtype=torch.float32, device=dev),
                 scale=torch.empty(3, dtype=torch.float32, device=dev),
-                kc=torch.zeros(2 * t, hkv * d, dtype=torch.uint8, device=dev),
-                vc=torch.zeros(2 * t, hkv * d, dtype=torch.uint8, device=dev))
+                kc=torch.zeros(2 * t // ATTN_BLOCK, hkv, ATTN_BLOCK, d, dtype=torch.uint8, device=dev),
+                vc=torch.zeros(2 * t // ATTN_BLOCK, hkv, ATTN_BLOCK, d, dtype=torch.uint8, device=dev))
 
 
-def graph_time_ms(fn, reps):
-    """Average time of fn over ``reps`` calls captured in a HIP graph and
-    replayed between two HIP events (fn run once first, outside)."""
+def graph_time_ms(fn, reps, rounds=3):
+    """Average time of fn over ``reps`` calls captured in a HIP graph: the
+    graph is replayed once to warm up, then ``rounds`` times between pairs of
+    HIP events; the median replay, divided by reps (fn run once first,
+    outside the graph)."""
+    import statistics
     import torch
     stream = torch.cuda.current_stream()
     fn()
@@ -237,14 +241,17 @@ def graph_time_ms(fn, reps):
             fn()
     graph.replay()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    graph.replay()
-    b.record(stream)
-    torch.cuda.synchronize()
+    times = []
+    for _ in range(rounds):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        graph.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / reps)
     del graph
-    return a.elapsed_time(b) / reps
+    return statistics.median(times)
 
 
 def hbm_entry(shape, ms, nbytes):
@@ -298,8 +305,8 @@ def attention_case(workload, dev, lens, seed):
         table[i, :nb] = perm[used:used + nb]
         used += nb
     return dict(q=torch.randn(b, hq, d, generator=g).to(torch.bfloat16).to(dev),
-                kc=synth.random_cache_codes((pool * ATTN_BLOCK, hkv, d), 2 * seed + 1, dev),
-                vc=synth.random_cache_codes((pool * ATTN_BLOCK, hkv, d), 2 * seed + 2, dev),
+                kc=synth.random_cache_codes((pool, hkv, ATTN_BLOCK, d), 2 * seed + 1, dev),
+                vc=synth.random_cache_codes((pool, hkv, ATTN_BLOCK, d), 2 * seed + 2, dev),
                 table=table.to(dev), lens=torch.tensor(lens, dtype=torch.int32).to(dev),
                 scales=torch.tensor([4.0 / 448, 0.004, 0.01], dtype=torch.float32, device=dev),
                 out=torch.empty(b, hq, d, dtype=torch.bfloat16, device=dev),

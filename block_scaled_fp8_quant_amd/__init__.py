@@ -65,7 +65,7 @@ def load():
         "fp8blk_quant_weight_t": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_gemm_rowscaled": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8blk_kv_scales": [vp, i64, vp, i32, vp],
-        "fp8blk_kv_cache_write": [vp, vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp],
+        "fp8blk_kv_cache_write": [vp, vp, i64, i64, i64, i64, vp, i64, i64, vp, vp, vp, vp, vp],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -145,8 +145,9 @@ def fp8blk_kv_scales(amax, n, scale, pow2, stream):
     return _call("fp8blk_kv_scales", amax, n, scale, int(pow2), stream)
 
 
-def fp8blk_kv_cache_write(k, v, ld, T, Hkv, D, slot, num_slots, k_scale, v_scale, k_cache, v_cache, stream):
-    return _call("fp8blk_kv_cache_write", k, v, ld, T, Hkv, D, slot, num_slots, k_scale, v_scale,
+def fp8blk_kv_cache_write(k, v, ld, T, Hkv, D, slot, num_slots, block_size, k_scale, v_scale, k_cache, v_cache,
+                          stream):
+    return _call("fp8blk_kv_cache_write", k, v, ld, T, Hkv, D, slot, num_slots, block_size, k_scale, v_scale,
                  k_cache, v_cache, stream)
 
 
@@ -389,15 +390,20 @@ def decode_attention(q, k_cache, v_cache, block_table, block_size, context_lens,
     """FP8 decode attention: q [B, Hq, D] bf16 (or [B, Hq*D] rows with a row
     stride, e.g. a view into a qkv output), caches [slots, Hkv, D] uint8,
     block_table [B, max_blocks] int32, context_lens [B] int32, one-element
-    fp32 scale tensors, all on the device. Returns out [B, Hq, D] bf16.
+    fp32 scale tensors, all on the device. The caches are head-major pages
+    [num_blocks, Hkv, block_size, D] (what kv_cache_write fills); block_size
+    must match their third dimension. Returns out [B, Hq, D] bf16.
     split=False runs one workgroup per (sequence, KV head) over the whole
     context; otherwise contexts are cut into chunks of split_tokens tokens
     (0: the library's choice) whose partials go to ``workspace`` (a uint8
     device tensor, allocated here when None)."""
     torch = _torch()
-    if k_cache.dim() != 3 or v_cache.shape != k_cache.shape:
-        raise ValueError("caches must be [slots, Hkv, D] and alike")
-    slots, hkv, d = k_cache.shape
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, Hkv, block_size, D] and alike")
+    nblk, hkv, bs, d = k_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size %d does not match the caches' pages of %d tokens" % (block_size, bs))
+    slots = nblk * bs
     b = q.shape[0]
     hq = (q.shape[1] * q.shape[2] if q.dim() == 3 else q.shape[1]) // d
     dev = q.device
@@ -470,9 +476,10 @@ def kv_scales(amax, pow2=False, scale=None):
 def kv_cache_write(k, v, slot, k_scale, v_scale, k_cache, v_cache):
     """Quantize the K and V rows of T tokens ([T, Hkv*D] bf16, or column
     slices of a qkv output whose rows are contiguous) with the per-tensor
-    scales (fp32 tensors of one element on the device) and write them to
-    k_cache / v_cache ([num_slots, Hkv, D] or [num_slots, Hkv*D] uint8) at
-    rows slot[t] (int64 [T] on the device; negative = skip)."""
+    scales (fp32 tensors of one element on the device) and write them to the
+    paged caches k_cache / v_cache ([num_blocks, Hkv, block_size, D] uint8,
+    head-major pages) at slots slot[t] (int64 [T] on the device; negative =
+    skip; slot = block * block_size + offset)."""
     torch = _torch()
     if k.dim() != 2 or v.shape != k.shape:
         raise ValueError("k and v must be 2-D and of the same shape")
@@ -484,18 +491,18 @@ def kv_cache_write(k, v, slot, k_scale, v_scale, k_cache, v_cache):
         if x.stride(1) != 1 or (t > 1 and x.stride(0) != k.stride(0)):
             raise ValueError("%s rows must be contiguous with a common row stride" % name)
     ld = k.stride(0) if t > 1 else width
-    num_slots = k_cache.shape[0]
-    hkv_d = k_cache[0].numel() if num_slots else width
-    if hkv_d != width:
-        raise ValueError("cache rows hold %d values, k rows %d" % (hkv_d, width))
+    if k_cache.dim() != 4:
+        raise ValueError("caches must be [num_blocks, Hkv, block_size, D]")
+    nblk, hkv, bs, d = k_cache.shape
+    if hkv * d != width:
+        raise ValueError("cache pages hold %d x %d values per token, k rows %d" % (hkv, d, width))
     for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
         if c.dtype != torch.uint8 or c.device != dev or not c.is_contiguous() or c.shape != k_cache.shape:
             raise ValueError("%s must be a contiguous uint8 cache like k_cache on the same device" % name)
     _check(slot, "slot", torch.int64, (t,), dev)
     _check(k_scale.reshape(-1), "k_scale", torch.float32, (1,), dev)
     _check(v_scale.reshape(-1), "v_scale", torch.float32, (1,), dev)
-    d = width  # passed as Hkv = 1, D = Hkv*D: the kernel only needs the row width
-    fp8blk_kv_cache_write(k.data_ptr(), v.data_ptr(), ld, t, 1, d, slot.data_ptr(), num_slots,
+    fp8blk_kv_cache_write(k.data_ptr(), v.data_ptr(), ld, t, hkv, d, slot.data_ptr(), nblk * bs, bs,
                           k_scale.data_ptr(), v_scale.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
                           _stream(dev))
 

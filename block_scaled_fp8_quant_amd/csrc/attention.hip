@@ -20,9 +20,12 @@
 // there are few (sequence, KV head) pairs.
 // Within a workgroup the waves take interleaved 64-token tiles and keep
 // their own online-softmax state, merged through LDS. Per tile:
-//   * the 64 tokens' cache slots come from the block table (one per lane;
+//   * the 64 tokens' cache rows come from the block table (one per lane;
 //     out-of-range tokens, blocks or slots are masked and read a zero row,
-//     so every load is unconditional and all of them are issued together);
+//     so every load is unconditional and all of them are issued together).
+//     The caches are head-major pages [blocks][Hkv][block_size][D]: a
+//     workgroup's rows of one page are one contiguous block_size x 128-byte
+//     run;
 //   * QK^T: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 tokens, source 0 =
 //     the group's Q rows (heads, padded to 16 with zeros), source 1 = 16 K
 //     rows loaded straight from the cache. Lane l then holds the scores of
@@ -86,21 +89,19 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     float* __restrict__ ws_acc, float* __restrict__ ws_ml, int64_t nchunks) {
   constexpr int D = kHeadDim;
   __shared__ __attribute__((aligned(16))) uint32_t q8[G * D / 4];
-  __shared__ __attribute__((aligned(16))) int32_t slot_tile[4][64];
+  __shared__ __attribute__((aligned(16))) int32_t row_tile[4][64];
   __shared__ __attribute__((aligned(16))) float ptile[4][64][G];
   __shared__ float m_w[4][G], l_w[4][G];
   __shared__ __attribute__((aligned(16))) float acc_w[4][G][D];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // XCD-aware order: workgroups go to the 8 XCDs round-robin, so XCD x runs
-  // blocks x, x+8, x+16, ...; those are mapped to the KV heads 0..Hkv-1 of
-  // chunks x, x+8, ... in turn. All heads of one chunk then run at the same
-  // time on one XCD and read the same cache pages together (a token's heads
-  // are adjacent in a slot), and the chunks of a sequence spread over XCDs.
-  const int64_t xcd = blockIdx.x % 8, xi = blockIdx.x / 8;
-  const int64_t gk = xi % Hkv, cidx = (xi / Hkv) * 8 + xcd;  // chunk cidx = b * splits + s
-  if (cidx >= nchunks) return;                                 // padding of the last group of 8
+  // Block order: the KV heads of one chunk are consecutive blocks, spread
+  // over the XCDs by the round-robin dispatch. With head-major pages this
+  // and an XCD-aware order (all heads of a chunk on one XCD) measured the
+  // same; with token-major slots the XCD-aware order was 9-10% faster.
+  const int64_t gk = blockIdx.x % Hkv, cidx = blockIdx.x / Hkv;  // chunk cidx = b * splits + s
+  if (cidx >= nchunks) return;
   const int64_t b = cidx / splits, sidx = cidx % splits;
   const int64_t wg = (b * Hkv + gk) * splits + sidx;          // partial index (split mode)
   const int64_t L = context_lens[b] > 0 ? context_lens[b] : 0;
@@ -129,9 +130,6 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     qfrag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
   const float s2scale = qs * ks * sm_scale * kLog2eAttn;  // scores in the log2 domain
-  const int64_t row_bytes = Hkv * D;                    // one slot of one cache
-  const uint8_t* const kbase = k_cache + gk * D;
-  const uint8_t* const vbase = v_cache + gk * D;
   const uint8_t* const zero = reinterpret_cast<const uint8_t*>(kZeroRow);
 
   // running state: lane group g holds heads 4g..4g+3 (entries r < 4)
@@ -158,54 +156,58 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     const uint32_t bi = (uint32_t)t / bs32;
     return table_row[bi < (uint64_t)max_blocks ? bi : max_blocks - 1];
   };
-  auto token_slot = [&](int64_t t, int32_t blk) {  // -1 for a masked token
+  // The cache row of token t for this KV head: head-major pages
+  // [num_slots / block_size][Hkv][block_size][D], so row (blk*Hkv + gk) *
+  // block_size + offset, in units of D bytes (< num_slots * Hkv < 2^31,
+  // checked on the host); -1 for a masked token.
+  auto token_row = [&](int64_t t, int32_t blk) {
     const uint32_t bi = (uint32_t)t / bs32;
-    const int64_t s = (int64_t)blk * block_size + ((uint32_t)t - bi * bs32);
-    return (t < c1 && bi < (uint64_t)max_blocks && blk >= 0 && s < num_slots) ? (int32_t)s : -1;
+    const uint32_t off = (uint32_t)t - bi * bs32;
+    const bool live = t < c1 && bi < (uint64_t)max_blocks && blk >= 0 && (int64_t)blk * block_size + off < num_slots;
+    return live ? (int32_t)(((int64_t)blk * Hkv + gk) * block_size + off) : -1;
   };
-  int32_t kslot[4], vslot[16];
-  auto read_slots = [&](int32_t slot) {  // exchange the tile's slots through LDS
-    slot_tile[wave][lane] = slot;
+  int32_t krow[4], vrow[16];
+  auto read_rows = [&](int32_t row) {  // exchange the tile's cache rows through LDS
+    row_tile[wave][lane] = row;
     wave_lds_sync();
 #pragma unroll
-    for (int u = 0; u < 4; ++u) kslot[u] = slot_tile[wave][16 * u + c16];
+    for (int u = 0; u < 4; ++u) krow[u] = row_tile[wave][16 * u + c16];
 #pragma unroll
     for (int k = 0; k < 16; k += 4) {
-      const int4 v4 = *reinterpret_cast<const int4*>(&slot_tile[wave][16 * g + k]);
-      vslot[k] = v4.x;
-      vslot[k + 1] = v4.y;
-      vslot[k + 2] = v4.z;
-      vslot[k + 3] = v4.w;
+      const int4 v4 = *reinterpret_cast<const int4*>(&row_tile[wave][16 * g + k]);
+      vrow[k] = v4.x;
+      vrow[k + 1] = v4.y;
+      vrow[k + 2] = v4.z;
+      vrow[k + 3] = v4.w;
     }
   };
   // K rows of tokens 16u + c16 (bytes 16g..+15 and 64+16g..+15), kept in the
   // cache hierarchy: the two halves of each row are read by two loads
   u32x4 klo[4], khi[4];
-  const uint32_t row32 = (uint32_t)row_bytes;  // < 2^31 (checked on the host), as is every slot
-  auto row_or_zero = [&](const uint8_t* base, int32_t slot) {  // branch-free: one 32x32->64 multiply-add
-    const uint8_t* p = base + (uint64_t)(uint32_t)(slot > 0 ? slot : 0) * row32;
-    return as_global(slot >= 0 ? p : zero);
+  auto row_or_zero = [&](const uint8_t* base, int32_t row) {  // branch-free
+    const uint8_t* p = base + ((uint64_t)(uint32_t)(row > 0 ? row : 0) << 7);  // D = 128 bytes per row
+    return as_global(row >= 0 ? p : zero);
   };
   auto load_k = [&]() {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const gbytes kr = row_or_zero(kbase, kslot[u]);
+      const gbytes kr = row_or_zero(k_cache, krow[u]);
       klo[u] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kr + 16 * g);
       khi[u] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kr + 64 + 16 * g);
     }
   };
   // V rows of tokens 16g + k, bytes 8 c16..+7: each row is read once (streamed)
   auto load_v = [&](int k) {
-    const gbytes vr = row_or_zero(vbase, vslot[k]);
+    const gbytes vr = row_or_zero(v_cache, vrow[k]);
     return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(vr + 8 * c16));
   };
 
   int64_t t0 = c0 + (int64_t)wave * 64;
   if (t0 < c1) {  // uniform over the wave
     int32_t blk = table_entry(t0 + lane);
-    const int32_t slot0 = token_slot(t0 + lane, blk);
+    const int32_t row0 = token_row(t0 + lane, blk);
     blk = table_entry(t0 + 256 + lane);  // tile i+1's entries
-    read_slots(slot0);
+    read_rows(row0);
     load_k();
     u32x2 vw[16];
 #pragma unroll
@@ -221,18 +223,18 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
         const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qfrag, kfrag, v4f{0.f, 0.f, 0.f, 0.f}, 0,
                                                                        0, 0, 127, 0, 127);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) s[u][r] = kslot[u] >= 0 ? d[r] * s2scale : -INFINITY;
+        for (int r = 0; r < 4; ++r) s[u][r] = krow[u] >= 0 ? d[r] * s2scale : -INFINITY;
       }
       // the scheduling barriers keep each stage's loads after the last use
       // of the registers they overwrite (one register set per stage)
       __builtin_amdgcn_sched_barrier(0);
 
-      // next tile: its slots (entries loaded one tile ago), the entries of
+      // next tile: its rows (entries loaded one tile ago), the entries of
       // the tile after it, its K rows
       const int64_t tn = t0 + 256;
-      const int32_t slot_n = token_slot(tn + lane, blk);
+      const int32_t row_n = token_row(tn + lane, blk);
       blk = table_entry(tn + 256 + lane);
-      read_slots(slot_n);
+      read_rows(row_n);
       load_k();
       __builtin_amdgcn_sched_barrier(0);
 
@@ -461,7 +463,7 @@ extern "C" fp8blk_status fp8blk_decode_attention(const uint16_t* q, int64_t ldq,
   fp8blk_status st = attention_shape(B, Hq, Hkv, D, max_blocks, block_size, split_tokens);
   if (st != FP8BLK_OK) return st;
   if (num_slots < 0 || !(sm_scale == sm_scale) || ldq < Hq * D || ldo < Hq * D) return FP8BLK_ERR_INVALID_ARG;
-  if (ldq % 8 || ldo % 8 || num_slots > INT32_MAX || Hkv * D > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  if (ldq % 8 || ldo % 8 || num_slots % block_size || num_slots > INT32_MAX / Hkv) return FP8BLK_ERR_SHAPE;
   if (B == 0) return FP8BLK_OK;
   if (!q || !k_cache || !v_cache || !block_table || !context_lens || !q_scale || !k_scale || !v_scale || !out)
     return FP8BLK_ERR_INVALID_ARG;
@@ -483,7 +485,7 @@ extern "C" fp8blk_status fp8blk_decode_attention(const uint16_t* q, int64_t ldq,
   }
   const bool split = splits > 1;
   const int64_t nchunks = B * splits;
-  const int64_t blocks = ((nchunks + 7) / 8) * 8 * Hkv;  // a multiple of 8 for the XCD-aware order
+  const int64_t blocks = nchunks * Hkv;
   if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
   const dim3 grid((uint32_t)blocks);
 #define FP8BLK_ATTN_LAUNCH(GV, SV)                                                                                 \

@@ -96,13 +96,16 @@ __global__ void kv_scales_kernel(const float* __restrict__ amax, int64_t n, floa
   if (i < n) scale[i] = group_scale(amax[i], pow2);
 }
 
-// One wave per token: K and V rows (row_units 16-byte units each, read with
-// row stride ld_units) are quantized with the per-tensor scales and written
-// to cache row slot[t] (skipped when negative or past the cache).
+// One wave per token: K and V rows (Hkv heads of head_units 16-byte bf16
+// units, read with row stride ld_units) are quantized with the per-tensor
+// scales and written to slot slot[t] of the head-major paged caches
+// [num_slots / block_size][Hkv][block_size][D] (skipped when negative or
+// past the cache): each head's 8-byte code units go to its own panel.
 __global__ __launch_bounds__(256) void kv_cache_write_kernel(
-    const u32x4* __restrict__ k, const u32x4* __restrict__ v, int64_t ld_units, int64_t T, int64_t row_units,
-    const int64_t* __restrict__ slot, int64_t num_slots, const float* __restrict__ k_scale,
-    const float* __restrict__ v_scale, u32x2* __restrict__ k_cache, u32x2* __restrict__ v_cache) {
+    const u32x4* __restrict__ k, const u32x4* __restrict__ v, int64_t ld_units, int64_t T, int64_t Hkv,
+    int64_t head_units, const int64_t* __restrict__ slot, int64_t num_slots, int64_t block_size,
+    const float* __restrict__ k_scale, const float* __restrict__ v_scale, u32x2* __restrict__ k_cache,
+    u32x2* __restrict__ v_cache) {
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform over the wave
@@ -114,8 +117,19 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   const bool vf = vs >= kCalibratedMinScale && vs <= kCalibratedMaxScale;
   const u32x4* kr = k + t * ld_units;
   const u32x4* vr = v + t * ld_units;
-  u32x2* kc = k_cache + sl * row_units;
-  u32x2* vc = v_cache + sl * row_units;
+  // head-major pages: head h of slot sl is row sl % block_size of head h's
+  // block_size x D panel in page sl / block_size
+  const int64_t page = sl / block_size, row = sl % block_size;
+  const int64_t first = (page * Hkv * block_size + row) * head_units;  // head 0's row (8-byte units)
+  const int64_t head_stride = block_size * head_units;
+  const uint32_t hu = (uint32_t)head_units;
+  u32x2* kc = k_cache + first;
+  u32x2* vc = v_cache + first;
+  const int64_t row_units = Hkv * head_units;
+  auto dst = [&](int64_t u) {  // unit u of the token's [Hkv][D] codes
+    const uint32_t h = (uint32_t)u / hu;
+    return (int64_t)h * head_stride + ((uint32_t)u - h * hu);
+  };
   for (int64_t u0 = 0; u0 < row_units; u0 += 128) {
     const int64_t u1 = u0 + lane, u2 = u0 + 64 + lane;
     const bool l1 = u1 < row_units, l2 = u2 < row_units;
@@ -126,12 +140,14 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
     const uint32_t wk1[4] = {k1.x, k1.y, k1.z, k1.w}, wv1[4] = {v1.x, v1.y, v1.z, v1.w};
     const uint32_t wk2[4] = {k2.x, k2.y, k2.z, k2.w}, wv2[4] = {v2.x, v2.y, v2.z, v2.w};
     if (l1) {
-      __builtin_nontemporal_store(encode8_calibrated(wk1, ks, kinv, kf), &kc[u1]);
-      __builtin_nontemporal_store(encode8_calibrated(wv1, vs, vinv, vf), &vc[u1]);
+      const int64_t d1 = dst(u1);
+      __builtin_nontemporal_store(encode8_calibrated(wk1, ks, kinv, kf), &kc[d1]);
+      __builtin_nontemporal_store(encode8_calibrated(wv1, vs, vinv, vf), &vc[d1]);
     }
     if (l2) {
-      __builtin_nontemporal_store(encode8_calibrated(wk2, ks, kinv, kf), &kc[u2]);
-      __builtin_nontemporal_store(encode8_calibrated(wv2, vs, vinv, vf), &vc[u2]);
+      const int64_t d2 = dst(u2);
+      __builtin_nontemporal_store(encode8_calibrated(wk2, ks, kinv, kf), &kc[d2]);
+      __builtin_nontemporal_store(encode8_calibrated(wv2, vs, vinv, vf), &vc[d2]);
     }
   }
 }
@@ -174,10 +190,10 @@ extern "C" fp8blk_status fp8blk_kv_scales(const float* amax, int64_t n, float* s
 
 extern "C" fp8blk_status fp8blk_kv_cache_write(const uint16_t* k, const uint16_t* v, int64_t ld, int64_t T,
                                                int64_t Hkv, int64_t D, const int64_t* slot, int64_t num_slots,
-                                               const float* k_scale, const float* v_scale, uint8_t* k_cache,
-                                               uint8_t* v_cache, hipStream_t stream) {
-  if (T < 0 || Hkv < 1 || D < 1 || num_slots < 0 || ld < Hkv * D) return FP8BLK_ERR_INVALID_ARG;
-  if (D % 8 || ld % 8) return FP8BLK_ERR_SHAPE;
+                                               int64_t block_size, const float* k_scale, const float* v_scale,
+                                               uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream) {
+  if (T < 0 || Hkv < 1 || D < 1 || num_slots < 0 || block_size < 1 || ld < Hkv * D) return FP8BLK_ERR_INVALID_ARG;
+  if (D % 8 || ld % 8 || num_slots % block_size || Hkv * D > INT32_MAX) return FP8BLK_ERR_SHAPE;
   if (T == 0) return FP8BLK_OK;
   if (!k || !v || !slot || !k_scale || !v_scale || (num_slots > 0 && (!k_cache || !v_cache)))
     return FP8BLK_ERR_INVALID_ARG;
@@ -187,8 +203,8 @@ extern "C" fp8blk_status fp8blk_kv_cache_write(const uint16_t* k, const uint16_t
   const int64_t blocks = (T + 3) / 4;  // one wave per token
   if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
   hipLaunchKernelGGL(kv_cache_write_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4*>(k), reinterpret_cast<const u32x4*>(v), ld / 8, T, Hkv * D / 8,
-                     slot, num_slots, k_scale, v_scale, reinterpret_cast<u32x2*>(k_cache),
+                     reinterpret_cast<const u32x4*>(k), reinterpret_cast<const u32x4*>(v), ld / 8, T, Hkv, D / 8,
+                     slot, num_slots, block_size, k_scale, v_scale, reinterpret_cast<u32x2*>(k_cache),
                      reinterpret_cast<u32x2*>(v_cache));
   return launch_status();
 }

@@ -248,24 +248,30 @@ fp8blk_status fp8blk_kv_scales(const float* amax, int64_t n, float* scale, int p
 
 /*
  * KV-cache quantize-and-write: for each token t with 0 <= slot[t] <
- * num_slots, k_cache[slot[t]][j] = E4M3(RN_fp32(k[t][j] / k_scale[0])) for
- * j < Hkv*D, and likewise v into v_cache with v_scale[0]. Codes saturate at
- * +-448 (tokens may exceed the calibrated range); a zero scale writes +-0.
- * Tokens with a negative slot (padding) or one past the cache write nothing.
+ * num_slots, head h of its K row goes to page slot[t] / block_size, panel h,
+ * row slot[t] % block_size of the paged cache:
+ *   k_cache[slot[t] / block_size][h][slot[t] % block_size][d]
+ *       = E4M3(RN_fp32(k[t][h*D + d] / k_scale[0])),
+ * and likewise v into v_cache with v_scale[0]. Codes saturate at +-448
+ * (tokens may exceed the calibrated range); a zero scale writes +-0. Tokens
+ * with a negative slot (padding) or one past the cache write nothing.
  *   k, v    [T][ld] bf16 in, the first Hkv*D columns of each row used (so
  *           they may point into a qkv projection output: ld = (Hq+2Hkv)*D)
  *           (16-byte aligned, ld % 8 == 0, ld >= Hkv*D)
  *   slot    [T] int64 (device)
  *   k_scale, v_scale: one fp32 each (device), e.g. from fp8blk_kv_scales
- *   k_cache, v_cache [num_slots][Hkv*D] E4M3 codes (16-byte aligned); a
- *           paged cache whose blocks are [block_size][Hkv][D] is this layout
- *           with slot = block * block_size + offset
+ *   k_cache, v_cache [num_slots / block_size][Hkv][block_size][D] E4M3
+ *           codes (16-byte aligned): pages of block_size tokens, head-major
+ *           within a page, so the rows of one KV head in a page are
+ *           contiguous (what the decode attention reads)
+ *   num_slots a multiple of block_size (whole pages), Hkv*D < 2^31
  *   The slots of one call must be distinct (else which token lands is
- *   unspecified). T >= 0 (0: no-op), Hkv >= 1, D >= 1 and D % 8 == 0.
+ *   unspecified). T >= 0 (0: no-op), Hkv >= 1, D >= 1 and D % 8 == 0,
+ *   block_size >= 1.
  */
 fp8blk_status fp8blk_kv_cache_write(const uint16_t* k, const uint16_t* v, int64_t ld, int64_t T,
                                     int64_t Hkv, int64_t D, const int64_t* slot, int64_t num_slots,
-                                    const float* k_scale, const float* v_scale,
+                                    int64_t block_size, const float* k_scale, const float* v_scale,
                                     uint8_t* k_cache, uint8_t* v_cache, hipStream_t stream);
 
 /*
@@ -281,9 +287,12 @@ fp8blk_status fp8blk_kv_cache_write(const uint16_t* k, const uint16_t* v, int64_
  * with the softmax and the weighted sum in fp32.
  *   q            [B][ldq] bf16: the first Hq*D values of row b are sequence b's
  *                query heads (so q may point into a qkv projection output)
- *   k_cache, v_cache [num_slots][Hkv][D] E4M3 codes (fp8blk_kv_cache_write)
- *   block_table  [B][max_blocks] int32 (device): token t of sequence b is in
- *                slot block_table[b][t / block_size] * block_size + t % block_size
+ *   k_cache, v_cache [num_slots / block_size][Hkv][block_size][D] E4M3
+ *                codes, head-major pages (fp8blk_kv_cache_write);
+ *                num_slots a multiple of block_size, num_slots*Hkv < 2^31
+ *   block_table  [B][max_blocks] int32 (device): token t of sequence b is
+ *                row t % block_size of page block_table[b][t / block_size]
+ *                (slot block_table[b][t / block_size] * block_size + t % block_size)
  *   context_lens [B] int32 (device): cached tokens per sequence
  *   q_scale, k_scale, v_scale: one fp32 each (device)
  *   sm_scale     softmax scale (1/sqrt(D) for standard attention)

@@ -177,11 +177,11 @@ def test_kv_scales_validation(lib):
 
 def test_kv_cache_write_validation(lib):
     f = lib.fp8blk_kv_cache_write
-    ok = [P, P, 1024, 4, 8, 128, P, 16, P, P, P, P, NULL]
+    ok = [P, P, 1024, 4, 8, 128, P, 16, 16, P, P, P, P, NULL]
 
     def call(**kw):
         a = list(ok)
-        names = ["k", "v", "ld", "T", "Hkv", "D", "slot", "slots", "ks", "vs", "kc", "vc", "stream"]
+        names = ["k", "v", "ld", "T", "Hkv", "D", "slot", "slots", "bs", "ks", "vs", "kc", "vc", "stream"]
         for key, val in kw.items():
             a[names.index(key)] = val
         return f(*a)
@@ -192,6 +192,8 @@ def test_kv_cache_write_validation(lib):
     assert call(ld=1000) == INVALID                           # ld < Hkv*D
     assert call(D=100, ld=800) == SHAPE                       # D % 8
     assert call(ld=1028) == SHAPE                             # ld % 8
+    assert call(bs=0) == INVALID
+    assert call(slots=24) == SHAPE                            # not whole pages of 16
     for name in ("k", "v", "slot", "ks", "vs", "kc", "vc"):
         assert call(**{name: NULL}) == INVALID, name
     for name, bad in (("k", P4), ("v", P4), ("slot", P4), ("ks", P + 2), ("kc", P4), ("vc", P4)):
@@ -250,6 +252,8 @@ def test_decode_attention_validation(lib):
     assert call(Hq=12) == SHAPE                           # Hq % Hkv
     assert call(Hq=128, ldq=16384, ldo=16384) == SHAPE    # Hq / Hkv = 16
     assert call(ldq=4100) == SHAPE
+    assert call(slots=1000) == SHAPE                       # not whole pages of 16
+    assert call(slots=1 << 28, Hkv=8) == SHAPE             # num_slots * Hkv >= 2^31
     for name in ("q", "kc", "vc", "table", "lens", "qs", "ks", "vs", "out"):
         assert call(**{name: NULL}) == INVALID, name
     for name, bad in (("q", P4), ("kc", P4), ("out", P4), ("table", P + 2), ("qs", P + 1)):

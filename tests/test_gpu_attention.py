@@ -23,8 +23,8 @@ def build(lens, hq, hkv, seed=0, bs=16):
     a = synth.attention_inputs(lens, hq, hkv, D, bs, seed)
     k, v = a["k"].to(DEV), a["v"].to(DEV)
     num_slots = a["num_slots"]
-    kc = torch.zeros(num_slots, hkv, D, dtype=torch.uint8, device=DEV)
-    vc = torch.zeros(num_slots, hkv, D, dtype=torch.uint8, device=DEV)
+    kc = torch.zeros(num_slots // bs, hkv, bs, D, dtype=torch.uint8, device=DEV)
+    vc = torch.zeros(num_slots // bs, hkv, bs, D, dtype=torch.uint8, device=DEV)
     amax = torch.stack([a["q"].float().abs().max(), a["k"].float().abs().max(), a["v"].float().abs().max()])
     scales = fb.kv_scales(amax.to(DEV))
     if k.shape[0]:
@@ -122,7 +122,7 @@ def test_masked_tokens_are_skipped(fp8blk_lib, mode):
     keep = {0: [t for t in range(40) if not 16 <= t < 32], 1: [t for t in range(50) if not 32 <= t < 48],
             2: list(range(16 * table.shape[1]))}
     assert table.shape[1] == 19                        # sequence 2's 300 tokens fill its whole table row
-    kcn, vcn = kc.cpu().numpy(), vc.cpu().numpy()
+    kcn, vcn = kc.cpu().numpy(), vc.cpu().numpy()      # [pages, Hkv, 16, D]
     rows_k, rows_v, new_table, new_lens, nxt = [], [], [], [], 0
     width = max(len(v) for v in keep.values())
     for bi in range(3):
@@ -131,14 +131,15 @@ def test_masked_tokens_are_skipped(fp8blk_lib, mode):
             blk = int(a["block_table"][bi, t // 16]) if t // 16 < table.shape[1] else -1
             if blk < 0:
                 continue
-            slot = blk * 16 + t % 16
-            rows_k.append(kcn[slot])
-            rows_v.append(vcn[slot])
+            rows_k.append(kcn[blk, :, t % 16])
+            rows_v.append(vcn[blk, :, t % 16])
             ids.append(nxt)
             nxt += 1
         new_lens.append(len(ids))
         new_table.append(ids + [0] * (width - len(ids)))
-    ref = oracle.decode_attention_ref(a["q"], np.stack(rows_k), np.stack(rows_v), np.array(new_table), 1,
+    # pages of one token each: [tokens, Hkv, 1, D]
+    ref = oracle.decode_attention_ref(a["q"], np.stack(rows_k)[:, :, None], np.stack(rows_v)[:, :, None],
+                                      np.array(new_table), 1,
                                       np.array(new_lens), *sc.cpu().numpy())
     assert_within_tolerance(out.reshape(3, -1), ref.reshape(3, -1), what="masked tokens")
 
@@ -153,7 +154,7 @@ def test_end_to_end_recalibrate_write_attend(fp8blk_lib):
     dq = qkv.to(DEV)
     scales = fb.kv_scales(fb.qkv_amax(dq, hq, hkv, D))
     a = synth.attention_inputs(lens, hq, hkv, D, 16, seed=8)
-    kc = torch.zeros(a["num_slots"], hkv, D, dtype=torch.uint8, device=DEV)
+    kc = torch.zeros(a["num_slots"] // 16, hkv, 16, D, dtype=torch.uint8, device=DEV)
     vc = torch.zeros_like(kc)
     fb.kv_cache_write(dq[:, hq * D:(hq + hkv) * D], dq[:, (hq + hkv) * D:], a["slot"].to(DEV), scales[1:2],
                       scales[2:3], kc, vc)
@@ -177,9 +178,8 @@ def test_full_size_decode_sampled(fp8blk_lib):
     blocks = ctx // bs
     g = synth.generator(90)
     perm = torch.randperm(b * blocks + 7, generator=g)[: b * blocks].to(torch.int32).reshape(b, blocks)
-    num_slots = (b * blocks + 7) * bs
-    kc = synth.random_cache_codes((num_slots, hkv, D), 1, DEV)
-    vc = synth.random_cache_codes((num_slots, hkv, D), 2, DEV)
+    kc = synth.random_cache_codes((b * blocks + 7, hkv, bs, D), 1, DEV)
+    vc = synth.random_cache_codes((b * blocks + 7, hkv, bs, D), 2, DEV)
     q = torch.randn(b, hq, D, generator=g).to(torch.bfloat16)
     lens = torch.full((b,), ctx, dtype=torch.int32)
     scales = torch.tensor([4.0 / 448, 0.004, 0.01], dtype=torch.float32, device=DEV)
@@ -190,8 +190,8 @@ def test_full_size_decode_sampled(fp8blk_lib):
     # the oracle reads only the sampled sequences' pages, gathered into a
     # small cache with the block table renumbered (page order is immaterial)
     pages = perm[torch.from_numpy(rows)].reshape(-1).long().to(DEV)
-    small_k = kc.view(-1, bs, hkv, D)[pages].reshape(-1, hkv, D).cpu().numpy()
-    small_v = vc.view(-1, bs, hkv, D)[pages].reshape(-1, hkv, D).cpu().numpy()
+    small_k = kc[pages].cpu().numpy()
+    small_v = vc[pages].cpu().numpy()
     table = np.arange(len(rows) * blocks).reshape(len(rows), blocks)
     ref = oracle.decode_attention_ref(q[torch.from_numpy(rows)], small_k, small_v, table, bs, lens.numpy()[rows],
                                       *scales.cpu().numpy())
