@@ -79,6 +79,10 @@ from .backward import (
     gemm_rowscaled_ref,
     dgrad_ref,
     wgrad_ref,
+    padded_offsets,
+    quant_act_t_grouped_ref,
+    grouped_dgrad_ref,
+    grouped_wgrad_ref,
 )
 from .attention import decode_attention_ref
 from .gemm import (
@@ -100,5 +104,6 @@ __all__ = [
     "rmsnorm_ref", "silu_mul_ref", "round_bf16",
     "qkv_amax_ref", "kv_scales_ref", "kv_quantize_ref", "kv_cache_write_ref",
     "quant_act_t_ref", "quant_weight_t_ref", "gemm_rowscaled_ref", "dgrad_ref", "wgrad_ref",
+    "padded_offsets", "quant_act_t_grouped_ref", "grouped_dgrad_ref", "grouped_wgrad_ref",
     "decode_attention_ref",
 ]

@@ -20,12 +20,29 @@ activations and gradients, 128x128 blocks for weights:
       dW[n, k] = sum_b SA[n, b] SB[k, b] sum_{m in b} A[n, m] B[k, m]
   with A = Q(dY^T) [N, M], B = Q(X^T) [K, M], b over M/128 blocks.
 
+Mixture-of-experts layers (rows sorted by expert, offsets[E+1]; weights
+[E, N, K]) take the same rules per expert:
+
+* grouped dgrad  dX[rows of e] = dY[rows of e] W_e: the activation quantizer
+  on dY and W_e's blocks transposed, i.e. the grouped GEMM with [E, K, N]
+  weights;
+* grouped wgrad  dW_e = dY_e^T X_e over expert e's M_e tokens. Reading (the
+  pages are silent): the 128x1 groups start at each expert's first token and
+  an expert's last, partial group is completed with zero rows -- zeros
+  change neither a group's maximum nor the sums -- so the transposed operands
+  live on a padded token axis where expert e owns columns
+  pad[e] .. pad[e+1], pad[e] = sum_{e' < e} ceil(M_e' / 128) * 128.
+
 Pins (tests/test_oracle_backward.py): the row-scaled GEMM against the
 pinned block-scaled GEMM when each 128-row block of B shares its scales,
 against exact Fraction sums on a tiny case, and scale linearity per row; the
 transposed quantizers against per-group loops of the pinned group and block
 quantizers; dgrad and wgrad equal to the exact products dY W and dY^T X
-when every group is exactly representable (lossless quantization).
+when every group is exactly representable (lossless quantization). Grouped
+forms: the grouped transposed quantizer against the pinned group quantizer
+on each zero-completed group; grouped dgrad and wgrad against the exact
+per-expert products on lossless inputs (ragged experts, an empty one); one
+expert of a multiple of 128 tokens reduces to the dense wgrad.
 """
 
 import numpy as np
@@ -86,3 +103,71 @@ def wgrad_ref(dy, x, pow2=False):
     qa, sa = quant_act_t_ref(dy, pow2)
     qb, sb = quant_act_t_ref(x, pow2)
     return gemm_rowscaled_ref(qa, sa, qb, sb)
+
+
+def padded_offsets(offsets):
+    """pad[e] = sum over e' < e of ceil(M_e' / 128) * 128 (int64 [E+1]): where
+    expert e's tokens start on the padded token axis of the grouped wgrad."""
+    m = np.diff(np.asarray(offsets, dtype=np.int64))
+    return np.concatenate([[0], np.cumsum((m + GROUP - 1) // GROUP * GROUP)])
+
+
+def _expert_padded(x, lo, hi):
+    """Rows lo..hi of bf16 values x, completed with zero rows to a multiple of 128."""
+    rows = x[lo:hi]
+    pad = (-(hi - lo)) % GROUP
+    return np.concatenate([rows, np.zeros((pad, x.shape[1]))]) if pad else rows
+
+
+def quant_act_t_grouped_ref(x, offsets, pow2=False):
+    """128x1 groups of X [M, K] (rows sorted by expert) starting at each
+    expert's first row, the last group of each expert completed with zeros.
+    Returns (Q^T uint8 [K, P], S^T float32 [K, P/128]), P = pad[E]: expert
+    e's tokens are columns pad[e] .. pad[e] + M_e, its padding columns up to
+    pad[e+1] hold code 0 (and count in their group's scale as zeros)."""
+    xv = bf16_values(x)
+    off = np.asarray(offsets, dtype=np.int64)
+    pad = padded_offsets(off)
+    k = xv.shape[1]
+    qt = np.zeros((k, int(pad[-1])), np.uint8)
+    st = np.zeros((k, int(pad[-1]) // GROUP), np.float32)
+    for e in range(len(off) - 1):
+        if off[e + 1] == off[e]:
+            continue
+        xe = _expert_padded(xv, off[e], off[e + 1])
+        q, sc = quant_act_ref(np.ascontiguousarray(xe.T), pow2)   # 1x128 groups of X_e^T
+        qt[:, pad[e]:pad[e + 1]] = q
+        st[:, pad[e] // GROUP:pad[e + 1] // GROUP] = sc
+    return qt, st
+
+
+def grouped_dgrad_ref(dy, w, offsets, pow2=False):
+    """dX [M, K] for dY [M, N] (rows sorted by expert) and W [E, N, K]: the
+    dense dgrad of each expert's rows against its weights. float64."""
+    from .gemm import gemm_ref
+    off = np.asarray(offsets, dtype=np.int64)
+    qa, sa = quant_act_ref(dy, pow2)
+    out = np.zeros((qa.shape[0], w.shape[2]))
+    for e in range(len(off) - 1):
+        if off[e + 1] == off[e]:
+            continue
+        qwt, swt = quant_weight_t_ref(w[e], pow2)
+        out[off[e]:off[e + 1]] = gemm_ref(qa[off[e]:off[e + 1]], sa[off[e]:off[e + 1]], qwt, swt)
+    return out
+
+
+def grouped_wgrad_ref(dy, x, offsets, pow2=False):
+    """dW [E, N, K] = per expert dY_e^T X_e with both operands in 128x1 groups
+    along the expert's tokens, the last group completed with zero rows
+    (dense wgrad on the zero-completed rows). Empty experts give zeros."""
+    dyv, xv = bf16_values(dy), bf16_values(x)
+    off = np.asarray(offsets, dtype=np.int64)
+    e_count = len(off) - 1
+    out = np.zeros((e_count, dyv.shape[1], xv.shape[1]))
+    for e in range(e_count):
+        if off[e + 1] == off[e]:
+            continue
+        qa, sa = quant_act_ref(np.ascontiguousarray(_expert_padded(dyv, off[e], off[e + 1]).T), pow2)
+        qb, sb = quant_act_ref(np.ascontiguousarray(_expert_padded(xv, off[e], off[e + 1]).T), pow2)
+        out[e] = gemm_rowscaled_ref(qa, sa, qb, sb)
+    return out

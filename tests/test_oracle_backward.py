@@ -14,7 +14,8 @@ import pytest
 import torch
 
 import oracle
-from oracle.backward import (dgrad_ref, gemm_rowscaled_ref, quant_act_t_ref, quant_weight_t_ref, wgrad_ref)
+from oracle.backward import (dgrad_ref, gemm_rowscaled_ref, grouped_dgrad_ref, grouped_wgrad_ref, padded_offsets,
+                             quant_act_t_grouped_ref, quant_act_t_ref, quant_weight_t_ref, wgrad_ref)
 
 
 def bf16(a):
@@ -121,3 +122,71 @@ def test_dgrad_and_wgrad_equal_exact_products_when_lossless():
     for pow2 in (False, True):
         assert np.array_equal(dgrad_ref(bf16(dy), bf16(w), pow2), dy @ w)
         assert np.array_equal(wgrad_ref(bf16(dy), bf16(x), pow2), dy.T @ x)
+
+
+# ------------------------------------------------------------ grouped (MoE)
+
+OFFSETS = np.array([0, 100, 100, 356, 357, 557])        # 100, 0, 256, 1, 200 rows
+
+
+def test_padded_offsets():
+    assert np.array_equal(padded_offsets(OFFSETS), [0, 128, 128, 384, 512, 768])
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_transposed_quantizer_group_by_group(pow2):
+    """Each expert's 128-token groups (the last completed with zeros) are
+    quantized as 1x128 groups of the pinned quantizer would be; padding
+    columns hold code 0."""
+    rng = np.random.default_rng(26)
+    x = bf16(rng.standard_normal((557, 3)) * np.array([1, 50, 1e-2]))
+    q, s = quant_act_t_grouped_ref(x, OFFSETS, pow2)
+    pad = padded_offsets(OFFSETS)
+    assert q.shape == (3, 768) and s.shape == (3, 6)
+    xv = oracle.bf16_values(x)
+    for e in range(5):
+        lo, hi = OFFSETS[e], OFFSETS[e + 1]
+        for j in range((hi - lo + 127) // 128):
+            rows = xv[lo + 128 * j:min(hi, lo + 128 * j + 128)]
+            for col in range(3):
+                g = np.zeros(128)
+                g[:len(rows)] = rows[:, col]
+                qg, sg = oracle.quant_act_ref(bf16(g[None, :]), pow2)
+                c0 = pad[e] + 128 * j
+                assert np.array_equal(q[col, c0:c0 + 128], qg[0])
+                assert s[col, c0 // 128] == sg[0, 0]
+                assert np.all(q[col, c0 + len(rows):c0 + 128] == 0)
+
+
+def test_grouped_dgrad_and_wgrad_exact_when_lossless():
+    """Per expert, dX = dY_e W_e and dW_e = dY_e^T X_e exactly when every
+    group and block is exactly representable (maxima planted at the start of
+    every expert's 128-token groups); the empty expert gets zeros."""
+    rng = np.random.default_rng(27)
+    m, n, k, e_count = OFFSETS[-1], 256, 384, 5
+    dy = lossless(rng, (m, n), 1)
+    x = lossless(rng, (m, k), 0)
+    w = lossless(rng, (e_count, n, k), None)
+    dy[:, ::128] = 448.0                       # 1x128 groups of dY along N (dgrad)
+    for e in range(e_count):
+        for r in range(OFFSETS[e], OFFSETS[e + 1], 128):
+            dy[r, :] = 448.0                   # 128x1 groups along each expert's tokens (wgrad)
+            x[r, :] = -448.0
+    w[:, ::128, ::128] = 448.0
+    sdy, sw, sx = 2.0 ** -3, 2.0 ** -10, 2.0 ** 2
+    dy, w, x = dy * sdy, w * sw, x * sx
+    for pow2 in (False, True):
+        dx = grouped_dgrad_ref(bf16(dy), bf16(w), OFFSETS, pow2)
+        dw = grouped_wgrad_ref(bf16(dy), bf16(x), OFFSETS, pow2)
+        for e in range(e_count):
+            lo, hi = OFFSETS[e], OFFSETS[e + 1]
+            assert np.array_equal(dx[lo:hi], dy[lo:hi] @ w[e])
+            assert np.array_equal(dw[e], dy[lo:hi].T @ x[lo:hi])
+        assert np.all(dw[1] == 0)
+
+
+def test_grouped_wgrad_one_expert_is_dense_wgrad():
+    rng = np.random.default_rng(28)
+    dy = bf16(rng.standard_normal((256, 128)))
+    x = bf16(rng.standard_normal((256, 256)) * 3)
+    assert np.array_equal(grouped_wgrad_ref(dy, x, [0, 256])[0], wgrad_ref(dy, x))
