@@ -63,6 +63,9 @@ def load():
         "fp8blk_decode_attention": [vp, i64, i64, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp, vp, f32,
                                     vp, i64, i64, vp, ctypes.c_size_t, vp],
         "fp8blk_quant_weight_t": [vp, i64, i64, vp, vp, i32, vp],
+        "fp8blk_quant_weight_t_grouped": [vp, i64, i64, i64, vp, vp, i32, vp],
+        "fp8blk_quant_act_t_grouped": [vp, i64, i64, vp, i64, i64, vp, vp, i32, vp],
+        "fp8blk_grouped_gemm_rowscaled": [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp],
         "fp8blk_gemm_rowscaled": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8blk_kv_scales": [vp, i64, vp, i32, vp],
         "fp8blk_kv_cache_write": [vp, vp, i64, i64, i64, i64, vp, i64, i64, vp, vp, vp, vp, vp],
@@ -131,6 +134,18 @@ def fp8blk_quant_act_t(x, M, K, qt, st, pow2, stream):
 
 def fp8blk_quant_weight_t(w, N, K, qt, st, pow2, stream):
     return _call("fp8blk_quant_weight_t", w, N, K, qt, st, int(pow2), stream)
+
+
+def fp8blk_quant_weight_t_grouped(w, E, N, K, qt, st, pow2, stream):
+    return _call("fp8blk_quant_weight_t_grouped", w, E, N, K, qt, st, int(pow2), stream)
+
+
+def fp8blk_quant_act_t_grouped(x, M, K, offsets, E, ld, qt, st, pow2, stream):
+    return _call("fp8blk_quant_act_t_grouped", x, M, K, offsets, E, ld, qt, st, int(pow2), stream)
+
+
+def fp8blk_grouped_gemm_rowscaled(qa, sa, qb, sb, offsets, E, ld, N, K, y, stream):
+    return _call("fp8blk_grouped_gemm_rowscaled", qa, sa, qb, sb, offsets, E, ld, N, K, y, stream)
 
 
 def fp8blk_gemm_rowscaled(qa, sa, qb, sb, M, N, K, y, stream):
@@ -331,20 +346,84 @@ def quant_act_t(x, pow2=False, qt=None, st=None):
 
 def quant_weight_t(w, pow2=False, qt=None, st=None):
     """128x128 block quantisation of bf16 W[N, K], written transposed ->
-    (QW^T uint8 [K, N], SW^T fp32 [K/128, N/128])."""
+    (QW^T uint8 [K, N], SW^T fp32 [K/128, N/128]); an expert stack
+    [E, N, K] gives [E, K, N] and [E, K/128, N/128] (each expert's W^T)."""
     torch = _torch()
-    if w.dim() != 2:
-        raise ValueError("w must be 2-D [N, K]")
-    n, k = w.shape
-    _check(w, "w", torch.bfloat16, (n, k))
+    if w.dim() not in (2, 3):
+        raise ValueError("w must be [N, K] or an expert stack [E, N, K]")
+    e = w.shape[0] if w.dim() == 3 else 1
+    n, k = w.shape[-2:]
+    _check(w, "w", torch.bfloat16, tuple(w.shape))
     if n % BLOCK or k % BLOCK:
         raise ValueError("N and K must be multiples of 128")
-    qt = torch.empty((k, n), dtype=torch.uint8, device=w.device) if qt is None else qt
-    st = torch.empty((k // BLOCK, n // BLOCK), dtype=torch.float32, device=w.device) if st is None else st
-    _check(qt, "qt", torch.uint8, (k, n), w.device)
-    _check(st, "st", torch.float32, (k // BLOCK, n // BLOCK), w.device)
-    fp8blk_quant_weight_t(w.data_ptr(), n, k, qt.data_ptr(), st.data_ptr(), pow2, _stream(w.device))
+    lead = (e,) if w.dim() == 3 else ()
+    qt = torch.empty(lead + (k, n), dtype=torch.uint8, device=w.device) if qt is None else qt
+    st = torch.empty(lead + (k // BLOCK, n // BLOCK), dtype=torch.float32, device=w.device) if st is None else st
+    _check(qt, "qt", torch.uint8, lead + (k, n), w.device)
+    _check(st, "st", torch.float32, lead + (k // BLOCK, n // BLOCK), w.device)
+    fp8blk_quant_weight_t_grouped(w.data_ptr(), e, n, k, qt.data_ptr(), st.data_ptr(), pow2, _stream(w.device))
     return qt, st
+
+
+def padded_tokens(m, e):
+    """Length of the padded token axis the grouped wgrad operands are laid
+    out on: room for every expert's tokens rounded up to 128 (at most
+    m + 127 e), as a multiple of 128."""
+    return (m // BLOCK + e) * BLOCK
+
+
+def quant_act_t_grouped(x, offsets, pow2=False, ld=None, qt=None, st=None):
+    """128x1 groups of bf16 X [M, K] whose rows are sorted by expert
+    (offsets int32 [E+1] on the device): each expert's groups start at its
+    first row, its last group completed with zeros. Written transposed on a
+    padded token axis of ld columns (default padded_tokens(M, E)): expert e
+    owns columns pad[e] .. pad[e+1], pad[e] = sum over e' < e of
+    ceil(M_e' / 128) * 128. Returns (Q^T uint8 [K, ld], S^T fp32 [K, ld/128]);
+    columns past pad[E] are not written."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [M, K]")
+    m, k = x.shape
+    e = offsets.shape[0] - 1
+    dev = x.device
+    _check(x, "x", torch.bfloat16, (m, k))
+    _check(offsets, "offsets", torch.int32, (e + 1,), dev)
+    if k % 64:
+        raise ValueError("K must be a multiple of 64")
+    ld = padded_tokens(m, e) if ld is None else ld
+    qt = torch.empty((k, ld), dtype=torch.uint8, device=dev) if qt is None else qt
+    st = torch.empty((k, ld // BLOCK), dtype=torch.float32, device=dev) if st is None else st
+    _check(qt, "qt", torch.uint8, (k, ld), dev)
+    _check(st, "st", torch.float32, (k, ld // BLOCK), dev)
+    fp8blk_quant_act_t_grouped(x.data_ptr(), m, k, offsets.data_ptr(), e, ld, qt.data_ptr(), st.data_ptr(), pow2,
+                               _stream(dev))
+    return qt, st
+
+
+def grouped_gemm_rowscaled(qa, sa, qb, sb, offsets, y=None):
+    """Expert-grouped GEMM with per-row scales on both operands over each
+    expert's tokens (the grouped wgrad): qa [N, ld] / sa [N, ld/128] and
+    qb [K, ld] / sb [K, ld/128] from quant_act_t_grouped with the same
+    offsets. Returns Y bf16 [E, N, K]."""
+    torch = _torch()
+    if qa.dim() != 2 or qb.dim() != 2 or qa.shape[1] != qb.shape[1]:
+        raise ValueError("qa must be [N, ld] and qb [K, ld]")
+    n, ld = qa.shape
+    k = qb.shape[0]
+    e = offsets.shape[0] - 1
+    dev = qa.device
+    if n % BLOCK or k % BLOCK or ld % BLOCK:
+        raise ValueError("N, K and ld must be multiples of 128")
+    _check(qa, "qa", torch.uint8, (n, ld))
+    _check(sa, "sa", torch.float32, (n, ld // BLOCK), dev)
+    _check(qb, "qb", torch.uint8, (k, ld), dev)
+    _check(sb, "sb", torch.float32, (k, ld // BLOCK), dev)
+    _check(offsets, "offsets", torch.int32, (e + 1,), dev)
+    y = torch.empty((e, n, k), dtype=torch.bfloat16, device=dev) if y is None else y
+    _check(y, "y", torch.bfloat16, (e, n, k), dev)
+    fp8blk_grouped_gemm_rowscaled(qa.data_ptr(), sa.data_ptr(), qb.data_ptr(), sb.data_ptr(), offsets.data_ptr(),
+                                  e, ld, n, k, y.data_ptr(), _stream(dev))
+    return y
 
 
 def gemm_rowscaled(qa, sa, qb, sb, y=None):
@@ -375,6 +454,25 @@ def dgrad(dy, qwt, swt, pow2=False):
     quant_weight_t). Returns dX bf16 [M, K]."""
     qa, sa = quant_act(dy, pow2)
     return gemm(qa, sa, qwt, swt)
+
+
+def grouped_dgrad(dy, qwt, swt, offsets, pow2=False):
+    """dX = dY_e W_e per expert: dY [M, N] (rows sorted by expert) in 1x128
+    groups, times each expert's transposed weight codes (qwt [E, K, N], swt
+    [E, K/128, N/128] from quant_weight_t of the stack). Returns dX bf16
+    [M, K]."""
+    qa, sa = quant_act(dy, pow2)
+    return grouped_gemm(qa, sa, qwt, swt, offsets)
+
+
+def grouped_wgrad(dy, x, offsets, pow2=False):
+    """dW_e = dY_e^T X_e per expert (rows sorted by expert, offsets int32
+    [E+1] on the device), both operands in 128x1 groups along each expert's
+    tokens (the last group of an expert completed with zeros). Returns dW
+    bf16 [E, N, K]."""
+    qa, sa = quant_act_t_grouped(dy, offsets, pow2)
+    qb, sb = quant_act_t_grouped(x, offsets, pow2)
+    return grouped_gemm_rowscaled(qa, sa, qb, sb, offsets)
 
 
 def wgrad(dy, x, pow2=False):
@@ -520,8 +618,10 @@ __all__ = [
     "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act",
     "fp8blk_qkv_amax", "fp8blk_kv_scales", "fp8blk_kv_cache_write",
     "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled", "fp8blk_decode_attention",
-    "fp8blk_decode_attention_workspace_size",
+    "fp8blk_decode_attention_workspace_size", "fp8blk_quant_weight_t_grouped", "fp8blk_quant_act_t_grouped",
+    "fp8blk_grouped_gemm_rowscaled",
     "quant_act", "quant_weight", "gemm", "grouped_gemm", "rmsnorm_quant_act", "silu_mul_quant_act",
     "qkv_amax", "kv_scales", "kv_cache_write", "quant_act_t", "quant_weight_t", "gemm_rowscaled",
-    "dgrad", "wgrad", "decode_attention", "linear",
+    "dgrad", "wgrad", "decode_attention", "linear", "padded_tokens", "quant_act_t_grouped",
+    "grouped_gemm_rowscaled", "grouped_dgrad", "grouped_wgrad",
 ]

@@ -43,4 +43,55 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Find which expert owns M-tile `t` of the concatenated per-expert tile
+// lists (expert e has ceil(M_e / BM) tiles). Every lane of the wave
+// computes the same answer: lanes take 64 experts at a time and a wave
+// prefix sum turns per-expert tile counts into tile ranges. The results are
+// passed through readfirstlane so the compiler knows they are uniform (they
+// feed the scalar base addresses of buffer resources; otherwise each
+// resource would be built in a loop over the lanes).
+template <int BM>
+__device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int E, int t, int& expert,
+                                            int& tile_in_expert) {
+  const int lane = threadIdx.x & 63;
+  int base = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int cnt = e < E ? (off[e + 1] - off[e] + BM - 1) / BM : 0;
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));  // uniform: so is the branch
+    if (t < base + total) {
+      const bool mine = cnt > 0 && t >= base + incl - cnt && t < base + incl;
+      const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      expert = __builtin_amdgcn_readfirstlane(e0 + src);
+      tile_in_expert = __builtin_amdgcn_readfirstlane(t - base - __shfl(incl - cnt, src));
+      return true;
+    }
+    base += total;
+  }
+  return false;
+}
+
+// Sum over the experts before e of ceil(M_e' / BM): where expert e's tiles
+// start in the concatenated per-expert tile lists (the same in every lane,
+// returned as a uniform value).
+template <int BM>
+__device__ __forceinline__ int tiles_before(const int32_t* __restrict__ off, int e) {
+  const int lane = threadIdx.x & 63;
+  int total = 0;
+  for (int e0 = 0; e0 < e; e0 += 64) {
+    const int i = e0 + lane;
+    int cnt = i < e ? (off[i + 1] - off[i] + BM - 1) / BM : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) cnt += __shfl_xor(cnt, d);
+    total += cnt;
+  }
+  return __builtin_amdgcn_readfirstlane(total);
+}
+
 }  // namespace fp8blk

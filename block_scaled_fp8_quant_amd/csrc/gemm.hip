@@ -491,11 +491,17 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
 // floats: no LDS bank conflict), the weight scale is uniform over the
 // wave, and the 4 accumulators of a quad are 4 consecutive outputs of one
 // row, stored as one 8-byte write.
+//
+// K is the contraction length of this tile (K / 128 blocks), starting at K
+// block kb0 of operand rows ld bytes long (ld / 128 scales per row); the
+// plain GEMMs pass ld = K and kb0 = 0, the grouped wgrad an expert's token
+// range on the padded token axis (per-row scales only: the weight-block
+// scan below assumes ld = K, kb0 = 0).
 template <class C>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
                                           const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                           int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-                                          int64_t m0, int64_t n0, uint8_t* smem_generic) {
+                                          int64_t m0, int64_t n0, uint8_t* smem_generic, int64_t ld, int64_t kb0) {
   static_assert(C::TM % 4 == 0, "activation fragments alternate between two registers; scales read 4 at a time");
   lds_u8* smem = (lds_u8*)smem_generic;
   const int lane = threadIdx.x & 63;
@@ -504,42 +510,43 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
   const int wn = (wave % C::WAVES_N) * C::WN;
   const int g = lane >> 4, c16 = lane & 15;
   const int KB = __builtin_amdgcn_readfirstlane((int)(K / BK));  // K <= 2^24
+  const int64_t KBld = ld / BK;                                   // scales per operand row
 
   LoadPlan<C> lp;
 #pragma unroll
   for (int i = 0; i < C::A_WIN; ++i) {
     const int row = (wave * C::A_WIN + i) * 8 + (lane >> 3);
-    lp.a_off[i] = (uint32_t)row * (uint32_t)K + (((lane & 7) ^ swz_key(row)) << 4);
+    lp.a_off[i] = (uint32_t)row * (uint32_t)ld + (((lane & 7) ^ swz_key(row)) << 4);
   }
 #pragma unroll
   for (int i = 0; i < C::B_WIN; ++i) {
     const int row = (wave * C::B_WIN + i) * 8 + (lane >> 3);
-    lp.b_off[i] = (uint32_t)row * (uint32_t)K + (((lane & 7) ^ swz_key(row)) << 4);
+    lp.b_off[i] = (uint32_t)row * (uint32_t)ld + (((lane & 7) ^ swz_key(row)) << 4);
   }
-  lp.a = qa + m0 * K;
-  lp.b = qw + n0 * K;
-  lp.a_len = clamp_len((M - m0) * K);
-  lp.b_len = clamp_len((N - n0) * K);
+  lp.a = qa + m0 * ld + kb0 * BK;
+  lp.b = qw + n0 * ld + kb0 * BK;
+  lp.a_len = clamp_len((M - m0) * ld - kb0 * BK);
+  lp.b_len = clamp_len((N - n0) * ld - kb0 * BK);
   if (wave < C::BM / 64) {
     // Activation scales, permuted so that the TM scales one lane needs
     // (rows wm + 16i + l%16, i < TM) are contiguous: slot t = h*WM + c*TM + i
     // holds tile row h*WM + 16i + c.
     const int t = wave * 64 + lane, h = t / C::WM, rem = t % C::WM;
     const int row = h * C::WM + 16 * (rem % C::TM) + rem / C::TM;
-    lp.s = sa + m0 * KB;
-    lp.s_len = clamp_len((M - m0) * KB * 4);
-    lp.s_off = (uint32_t)row * (uint32_t)(KB * 4);
+    lp.s = sa + m0 * KBld + kb0;
+    lp.s_len = clamp_len(((M - m0) * KBld - kb0) * 4);
+    lp.s_off = (uint32_t)row * (uint32_t)(KBld * 4);
   } else if constexpr (C::RB) {
     // B-row scales of tile rows bw*64 + lane, in natural order (sw is SB[N][KB])
     const int bw = wave - C::BM / 64 < C::BN / 64 ? wave - C::BM / 64 : C::BN / 64 - 1;
-    lp.s = sw + n0 * KB;
-    lp.s_len = clamp_len((N - n0) * KB * 4);
-    lp.s_off = (uint32_t)(bw * 64 + lane) * (uint32_t)(KB * 4);
+    lp.s = sw + n0 * KBld + kb0;
+    lp.s_len = clamp_len(((N - n0) * KBld - kb0) * 4);
+    lp.s_off = (uint32_t)(bw * 64 + lane) * (uint32_t)(KBld * 4);
   } else {  // weight scales of column blocks n0/128 + lane (lanes past the tile's blocks repeat)
     constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;  // a 64-wide tile lies in one block
-    lp.s = sw + (n0 / kBlock) * KB;
-    lp.s_len = clamp_len((N / kBlock - n0 / kBlock) * KB * 4);
-    lp.s_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KB * 4);
+    lp.s = sw + (n0 / kBlock) * KBld + kb0;
+    lp.s_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
+    lp.s_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
   }
   // N % 128 == 0 and WN divides 128: a wave's columns are all in or all out
   const bool cols_valid = n0 + wn < N;
@@ -582,7 +589,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
   }
 
   if (!cols_valid) return;
-  // lane holds Y[m0 + wm + 16i + l%16][n0 + wn + 16j + 4*(l/16) + r], r < 4
+  // lane holds Y[m0 + wm + 16i + l%16][n0 + wn + 16j + 4*(l/16) + r], r < 4 (Y rows N long)
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int64_t row = m0 + wm + 16 * i + c16;
@@ -623,38 +630,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const uint8_t* __restrict
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS];
   int64_t m_tile, n_tile;
   tile_of_block(blockIdx.x, gridDim.x, m_tiles, n_tiles, m_tile, n_tile);
-  gemm_tile<Cfg>(qa, sa, qw, sw, M, N, K, y, m_tile * Cfg::BM, n_tile * Cfg::BN, smem);
-}
-
-// Find which expert owns M-tile `t` of the concatenated per-expert tile
-// lists (expert e has ceil(M_e / BM) tiles). Every lane of the wave
-// computes the same answer: lanes take 64 experts at a time and a wave
-// prefix sum turns per-expert tile counts into tile ranges.
-template <int BM>
-__device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int E, int t, int& expert,
-                                            int& tile_in_expert) {
-  const int lane = threadIdx.x & 63;
-  int base = 0;
-  for (int e0 = 0; e0 < E; e0 += 64) {
-    const int e = e0 + lane;
-    const int cnt = e < E ? (off[e + 1] - off[e] + BM - 1) / BM : 0;
-    int incl = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    const int total = __shfl(incl, 63);
-    if (t < base + total) {
-      const bool mine = cnt > 0 && t >= base + incl - cnt && t < base + incl;
-      const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
-      expert = e0 + src;
-      tile_in_expert = t - base - __shfl(incl - cnt, src);
-      return true;
-    }
-    base += total;
-  }
-  return false;
+  gemm_tile<Cfg>(qa, sa, qw, sw, M, N, K, y, m_tile * Cfg::BM, n_tile * Cfg::BN, smem, K, 0);
 }
 
 template <class Cfg>
@@ -666,14 +642,47 @@ __global__ __launch_bounds__(Cfg::NT) void grouped_gemm_kernel(const uint8_t* __
                                                                int64_t N, int64_t K, uint16_t* __restrict__ y,
                                                                int n_tiles) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS];
-  const int t = blockIdx.x / n_tiles, n_tile = blockIdx.x % n_tiles;
-  int e, tile;
-  if (!locate_tile<Cfg::BM>(offsets, E, t, e, tile)) return;  // uniform over the workgroup
-  const int64_t row0 = offsets[e];
-  const int64_t rows = offsets[e + 1] - row0;
+  // uniform (readfirstlane): the division runs on the vector unit
+  const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / n_tiles));
+  const int n_tile = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % n_tiles));
+  int e = 0, tile = 0;
+  const int found = __builtin_amdgcn_readfirstlane((int)locate_tile<Cfg::BM>(offsets, E, t, e, tile));
+  e = __builtin_amdgcn_readfirstlane(e);
+  tile = __builtin_amdgcn_readfirstlane(tile);
+  if (!found) return;  // uniform over the workgroup
+  // uniform (readfirstlane): they size the buffer resources of every K step
+  const int64_t row0 = __builtin_amdgcn_readfirstlane(offsets[e]);
+  const int64_t rows = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - row0;
   const int64_t KB = K / BK;
   gemm_tile<Cfg>(qa + row0 * K, sa + row0 * KB, qw + (int64_t)e * N * K, sw + (int64_t)e * (N / kBlock) * KB,
-                 rows, N, K, y + row0 * N, (int64_t)tile * Cfg::BM, (int64_t)n_tile * Cfg::BN, smem);
+                 rows, N, K, y + row0 * N, (int64_t)tile * Cfg::BM, (int64_t)n_tile * Cfg::BN, smem, K, 0);
+}
+
+// Grouped wgrad: dW_e [N][K] = the row-scaled product of rows of A = Q(dY^T)
+// [N][ld] and B = Q(X^T) [K][ld] over expert e's 128-token blocks of the
+// padded token axis (they start at block tiles_before<128>(offsets, e)).
+// One workgroup per (expert, output tile). Expert ranges are clamped to the
+// ld / 128 blocks of the operands, so offsets that break their contract give
+// wrong values, never an access outside the buffers.
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) void grouped_rowscaled_kernel(const uint8_t* __restrict__ qa,
+                                                                    const float* __restrict__ sa,
+                                                                    const uint8_t* __restrict__ qb,
+                                                                    const float* __restrict__ sb,
+                                                                    const int32_t* __restrict__ offsets, int64_t ld,
+                                                                    int64_t N, int64_t K, uint16_t* __restrict__ y,
+                                                                    int tiles_per_expert, int n_tiles) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS];
+  const int e = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / tiles_per_expert));
+  const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % tiles_per_expert));
+  const int64_t lb = ld / BK;
+  int64_t kb0 = tiles_before<BK>(offsets, e);
+  kb0 = kb0 < 0 ? 0 : (kb0 > lb ? lb : kb0);
+  int64_t kbn = ((int64_t)__builtin_amdgcn_readfirstlane(offsets[e + 1]) -
+                 __builtin_amdgcn_readfirstlane(offsets[e]) + BK - 1) / BK;
+  kbn = kbn < 0 ? 0 : (kbn > lb - kb0 ? lb - kb0 : kbn);
+  gemm_tile<Cfg>(qa, sa, qb, sb, N, K, kbn * BK, y + (int64_t)e * N * K, (int64_t)(t / n_tiles) * Cfg::BM,
+                 (int64_t)(t % n_tiles) * Cfg::BN, smem, ld, kb0);
 }
 
 fp8blk_status check_gemm_args(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
@@ -753,6 +762,32 @@ extern "C" fp8blk_status fp8blk_gemm_rowscaled(const uint8_t* qa, const float* s
   if (tiles_of<BigRB>(M, N) >= kCUs) return launch_gemm<BigRB>(qa, sa, qb, sb, M, N, K, y, stream);
   if (tiles_of<MidRB>(M, N) >= 2 * kCUs) return launch_gemm<MidRB>(qa, sa, qb, sb, M, N, K, y, stream);
   return launch_gemm<SmallRB>(qa, sa, qb, sb, M, N, K, y, stream);
+}
+
+// Expert-grouped wgrad (row scales on both operands): the tile from the
+// output's tile count, as for fp8blk_gemm_rowscaled.
+extern "C" fp8blk_status fp8blk_grouped_gemm_rowscaled(const uint8_t* qa, const float* sa, const uint8_t* qb,
+                                                       const float* sb, const int32_t* offsets, int64_t E,
+                                                       int64_t ld, int64_t N, int64_t K, uint16_t* y,
+                                                       hipStream_t stream) {
+  if (E < 1 || ld < 0 || N <= 0 || K <= 0) return FP8BLK_ERR_INVALID_ARG;
+  if (N % kBlock || K % kBlock || ld % kBlock || ld > kMaxK || E > INT32_MAX - 1) return FP8BLK_ERR_SHAPE;
+  if (!qa || !sa || !qb || !sb || !offsets || !y) return FP8BLK_ERR_INVALID_ARG;
+  if (!aligned(qa, 16) || !aligned(qb, 16) || !aligned(y, 16) || !aligned(sa, 4) || !aligned(sb, 4) ||
+      !aligned(offsets, 4))
+    return FP8BLK_ERR_ALIGNMENT;
+  auto launch = [&](auto cfg) {
+    using Cfg = decltype(cfg);
+    const int64_t n_tiles = K / Cfg::BN + (K % Cfg::BN != 0);
+    const int64_t per = (N / Cfg::BM + (N % Cfg::BM != 0)) * n_tiles;
+    if (per * E > INT32_MAX) return FP8BLK_ERR_SHAPE;
+    hipLaunchKernelGGL(grouped_rowscaled_kernel<Cfg>, dim3((uint32_t)(per * E)), dim3(Cfg::NT), 0, stream, qa, sa,
+                       qb, sb, offsets, ld, N, K, y, (int)per, (int)n_tiles);
+    return launch_status();
+  };
+  if (tiles_of<BigRB>(N, K) * E >= kCUs) return launch(BigRB{});
+  if (tiles_of<MidRB>(N, K) * E >= 2 * kCUs) return launch(MidRB{});
+  return launch(SmallRB{});
 }
 
 extern "C" fp8blk_status fp8blk_grouped_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw,

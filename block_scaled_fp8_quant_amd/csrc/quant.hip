@@ -110,21 +110,41 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const u32x4* __restri
 // two DPP steps, and store its 128 codes as one contiguous 128-byte run.
 constexpr int kTStride = 65;  // dwords per LDS row
 
+//
+// GROUPED: rows sorted by expert (offsets[E+1] on the device); the 128-row
+// tiles start at each expert's first row and rows past the expert's end
+// read as zero, and tile t of the concatenated per-expert tile lists is
+// written at columns 128t.. of Q^T rows ld long (the padded token axis).
+template <bool GROUPED>
 __global__ __launch_bounds__(256) void quant_act_t_kernel(const u32x4* __restrict__ x, int64_t M, int64_t K,
                                                           u32x4* __restrict__ qt, float* __restrict__ st,
-                                                          int pow2) {
+                                                          int pow2, const int32_t* __restrict__ offsets, int E,
+                                                          int64_t ld) {
   __shared__ uint32_t lds[64 * kTStride];
   const int t = threadIdx.x;
   const int64_t k_tiles = K / 64;
-  const int64_t m0 = (int64_t)(blockIdx.x / k_tiles) * 128, k0 = (int64_t)(blockIdx.x % k_tiles) * 64;
+  const int64_t tile = blockIdx.x / k_tiles, k0 = (int64_t)(blockIdx.x % k_tiles) * 64;
+  int64_t m0 = tile * 128, rows = 128;  // source rows m0 .. m0 + rows - 1
+  if (GROUPED) {
+    int e, j;
+    if (!locate_tile<128>(offsets, E, (int)tile, e, j) || (tile + 1) * 128 > ld) return;  // uniform
+    m0 = (int64_t)offsets[e] + 128 * (int64_t)j;
+    const int64_t end = offsets[e + 1] < M ? offsets[e + 1] : M;
+    rows = end - m0 < 128 ? end - m0 : 128;
+  } else {
+    ld = M;
+  }
   const int c = t & 7, q = t >> 3;
   const int64_t row_units = K / 8;
   u32x4 v[4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      v[2 * i + h] = __builtin_nontemporal_load(&x[(m0 + 2 * (q + 32 * i) + h) * row_units + k0 / 8 + c]);
+    for (int h = 0; h < 2; ++h) {
+      const int r = 2 * (q + 32 * i) + h;
+      v[2 * i + h] = (!GROUPED || r < rows) ? __builtin_nontemporal_load(&x[(m0 + r) * row_units + k0 / 8 + c])
+                                            : u32x4{0u, 0u, 0u, 0u};
+    }
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const uint32_t e0[4] = {v[2 * i].x, v[2 * i].y, v[2 * i].z, v[2 * i].w};      // row 2q'
@@ -150,10 +170,11 @@ __global__ __launch_bounds__(256) void quant_act_t_kernel(const u32x4* __restric
   u32x2 code[4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) code[g] = encode8(&w[4 * g], sc);
-  u32x4* dst = qt + (k0 + k) * (M / 16) + (m0 + 32 * p) / 16;
+  const int64_t c0 = tile * 128;  // destination column (= m0 for the plain layout)
+  u32x4* dst = qt + (k0 + k) * (ld / 16) + (c0 + 32 * p) / 16;
   __builtin_nontemporal_store(u32x4{code[0].x, code[0].y, code[1].x, code[1].y}, dst);
   __builtin_nontemporal_store(u32x4{code[2].x, code[2].y, code[3].x, code[3].y}, dst + 1);
-  if (p == 0) st[(k0 + k) * (M / 128) + m0 / 128] = sc;
+  if (p == 0) st[(k0 + k) * (ld / 128) + c0 / 128] = sc;
 }
 
 // 4x4 byte transpose: a[i] holds row i (byte j = column j); returns column j
@@ -183,6 +204,12 @@ __global__ __launch_bounds__(256) void quant_weight_t_kernel(const u32x4* __rest
   const int t = threadIdx.x;
   const int64_t kblocks = K / kBlock;
   const int64_t bi = blockIdx.x / kblocks, bj = blockIdx.x % kblocks;
+  {  // matrix blockIdx.y of a stack: W [E][N][K] -> W^T [E][K][N], scales [E][K/128][N/128]
+    const int64_t e = blockIdx.y;
+    w += e * N * (K / 8);
+    qt += e * K * (N / 16);
+    st += e * kblocks * (N / kBlock);
+  }
   const int R = t >> 4, C = t & 15;
   const int64_t row_units = K / 8;
   u32x4 v[8];
@@ -557,23 +584,46 @@ extern "C" fp8blk_status fp8blk_quant_act_t(const uint16_t* x, int64_t M, int64_
   if (!aligned(x, 16) || !aligned(qt, 16) || !aligned(st, 4)) return FP8BLK_ERR_ALIGNMENT;
   const int64_t blocks = (M / kBlock) * (K / 64);
   if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_act_t_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2);
+  hipLaunchKernelGGL(quant_act_t_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2, nullptr, 0,
+                     M);
   return launch_status();
 }
 
-extern "C" fp8blk_status fp8blk_quant_weight_t(const uint16_t* w, int64_t N, int64_t K, uint8_t* qt, float* st,
-                                               int pow2, hipStream_t stream) {
-  if (N < 0 || K <= 0 || (pow2 != 0 && pow2 != 1)) return FP8BLK_ERR_INVALID_ARG;
-  if (N % kBlock || K % kBlock) return FP8BLK_ERR_SHAPE;
+extern "C" fp8blk_status fp8blk_quant_act_t_grouped(const uint16_t* x, int64_t M, int64_t K, const int32_t* offsets,
+                                                    int64_t E, int64_t ld, uint8_t* qt, float* st, int pow2,
+                                                    hipStream_t stream) {
+  if (M < 0 || K <= 0 || E < 1 || ld < 0 || (pow2 != 0 && pow2 != 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (K % 64 || ld % kBlock || E > INT32_MAX - 1 || M > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  if (M == 0 || ld == 0) return FP8BLK_OK;
+  if (!x || !offsets || !qt || !st) return FP8BLK_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(offsets, 4) || !aligned(qt, 16) || !aligned(st, 4)) return FP8BLK_ERR_ALIGNMENT;
+  const int64_t tiles = ld / kBlock;  // the padded axis holds at most this many 128-token tiles
+  const int64_t blocks = tiles * (K / 64);
+  if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  hipLaunchKernelGGL(quant_act_t_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2, offsets,
+                     (int)E, ld);
+  return launch_status();
+}
+
+extern "C" fp8blk_status fp8blk_quant_weight_t_grouped(const uint16_t* w, int64_t E, int64_t N, int64_t K,
+                                                       uint8_t* qt, float* st, int pow2, hipStream_t stream) {
+  if (E < 1 || N < 0 || K <= 0 || (pow2 != 0 && pow2 != 1)) return FP8BLK_ERR_INVALID_ARG;
+  if (N % kBlock || K % kBlock || E > 65535) return FP8BLK_ERR_SHAPE;
   if (N == 0) return FP8BLK_OK;
   if (!w || !qt || !st) return FP8BLK_ERR_INVALID_ARG;
   if (!aligned(w, 16) || !aligned(qt, 16) || !aligned(st, 4)) return FP8BLK_ERR_ALIGNMENT;
   const int64_t blocks = (N / kBlock) * (K / kBlock);
   if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_weight_t_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream,
+  hipLaunchKernelGGL(quant_weight_t_kernel, dim3((uint32_t)blocks, (uint32_t)E), dim3(256), 0, stream,
                      reinterpret_cast<const u32x4*>(w), N, K, reinterpret_cast<u32x4*>(qt), st, pow2);
   return launch_status();
+}
+
+extern "C" fp8blk_status fp8blk_quant_weight_t(const uint16_t* w, int64_t N, int64_t K, uint8_t* qt, float* st,
+                                               int pow2, hipStream_t stream) {
+  return fp8blk_quant_weight_t_grouped(w, 1, N, K, qt, st, pow2, stream);
 }
 
 extern "C" fp8blk_status fp8blk_rmsnorm_quant_act(const uint16_t* x, const uint16_t* gamma, float eps, int64_t M,

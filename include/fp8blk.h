@@ -172,6 +172,64 @@ fp8blk_status fp8blk_gemm_rowscaled(const uint8_t* qa, const float* sa,
                                     uint16_t* y, hipStream_t stream);
 
 /*
+ * Backward GEMMs of the expert-grouped layer (rows sorted by expert,
+ * offsets[E+1] int32 on the device as for fp8blk_grouped_gemm; weights
+ * [E][N][K]), the dense rules per expert:
+ *   dgrad  dX_e = dY_e W_e: fp8blk_quant_act(dY), fp8blk_quant_weight_t_grouped
+ *          (W) -> [E][K][N], then fp8blk_grouped_gemm(..., E, M, K, N, dX);
+ *   wgrad  dW_e = dY_e^T X_e over expert e's tokens: fp8blk_quant_act_t_grouped
+ *          of dY and of X, then fp8blk_grouped_gemm_rowscaled.
+ * Reading for ragged experts (the pages are silent): the 128x1 groups start
+ * at each expert's first token and an expert's last group is completed with
+ * zero rows (zeros change neither the maximum nor the sums). The transposed
+ * operands live on a padded token axis of ld columns where expert e owns
+ * columns pad[e] .. pad[e+1], pad[e] = sum_{e' < e} ceil(M_e' / 128) * 128;
+ * ld >= pad[E] (M + 127 E always suffices, rounded up to a multiple of 128).
+ * Offsets are device data and not checked (nondecreasing, offsets[0] = 0,
+ * offsets[E] = M): when they break this the results are undefined, but no
+ * kernel reads or writes outside the buffers sized from M, E and ld.
+ */
+
+/*
+ * fp8blk_quant_weight_t for each matrix of a stack: w [E][N][K] -> qt
+ * [E][K][N], st [E][K/128][N/128]. 1 <= E <= 65535; otherwise as
+ * fp8blk_quant_weight_t (which is this with E = 1).
+ */
+fp8blk_status fp8blk_quant_weight_t_grouped(const uint16_t* w, int64_t E, int64_t N, int64_t K,
+                                            uint8_t* qt, float* st, int pow2, hipStream_t stream);
+
+/*
+ * 128x1 quantisation of x [M][K] (rows sorted by expert) per expert, written
+ * transposed on the padded token axis: for expert e and its j-th group of
+ * 128 rows (offsets[e] + 128j ..), qt[k][pad[e] + 128j + i] codes
+ * x[offsets[e] + 128j + i][k] for the expert's rows and 0 past them, and
+ * st[k][pad[e]/128 + j] is the group's scale. Columns past pad[E] are not
+ * written.
+ *   x [M][K] bf16 (16-byte aligned); qt [K][ld] codes (16-byte aligned);
+ *   st [K][ld/128] fp32; offsets [E+1] int32 (device)
+ *   M >= 0 (0: no-op), K % 64 == 0, ld % 128 == 0, E >= 1, pow2 in {0, 1}.
+ */
+fp8blk_status fp8blk_quant_act_t_grouped(const uint16_t* x, int64_t M, int64_t K,
+                                         const int32_t* offsets, int64_t E, int64_t ld,
+                                         uint8_t* qt, float* st, int pow2, hipStream_t stream);
+
+/*
+ * Grouped wgrad GEMM: for each expert e,
+ *   y[e][n][k] = bf16( sum over e's blocks b of sa[n][b] * sb[k][b] *
+ *                      sum_{t in block b} E4M3(qa[n][t]) * E4M3(qb[k][t]) )
+ * over the blocks pad[e]/128 .. pad[e+1]/128 of the padded token axis (an
+ * expert without tokens gets zeros).
+ *   qa [N][ld] codes, sa [N][ld/128]; qb [K][ld] codes, sb [K][ld/128]
+ *   (fp8blk_quant_act_t_grouped of dY and X); offsets [E+1] int32 (device)
+ *   y  [E][N][K] bf16 out (16-byte aligned)
+ *   E >= 1, N > 0, K > 0, N, K and ld multiples of 128, ld <= 2^24.
+ */
+fp8blk_status fp8blk_grouped_gemm_rowscaled(const uint8_t* qa, const float* sa,
+                                            const uint8_t* qb, const float* sb,
+                                            const int32_t* offsets, int64_t E, int64_t ld,
+                                            int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+
+/*
  * Fused producers: the bf16 input of a linear layer is computed and quantised
  * in one pass, so it is never written to and read back from HBM. Both pages
  * count the quantisation kernels as overhead and name kernel fusion as the

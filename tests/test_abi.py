@@ -37,7 +37,8 @@ def test_header_declares_the_boundary():
         "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
         "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_qkv_amax", "fp8blk_kv_scales",
         "fp8blk_kv_cache_write", "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
-        "fp8blk_decode_attention", "fp8blk_decode_attention_workspace_size", "fp8blk_status_string"])
+        "fp8blk_decode_attention", "fp8blk_decode_attention_workspace_size", "fp8blk_quant_weight_t_grouped",
+        "fp8blk_quant_act_t_grouped", "fp8blk_grouped_gemm_rowscaled", "fp8blk_status_string"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -282,6 +283,29 @@ def test_decode_attention_workspace_size(lib):
     assert size(4, 32, 8, 64, 256, 16, 0) == 0             # D != 128
     assert size(4, 32, 8, 128, 256, 16, 100) == 0          # split not a multiple of 256
     assert size(0, 32, 8, 128, 256, 16, 0) == 0
+
+
+def test_grouped_backward_validation(lib):
+    f = lib.fp8blk_quant_weight_t_grouped
+    assert f(P, 0, 128, 128, P, P, 0, NULL) == INVALID          # E < 1
+    assert f(P, 65536, 128, 128, P, P, 0, NULL) == SHAPE
+    assert f(P, 2, 130, 128, P, P, 0, NULL) == SHAPE
+    assert f(P4, 2, 128, 128, P, P, 0, NULL) == ALIGN
+    assert f(NULL, 2, 0, 128, NULL, NULL, 0, NULL) == OK         # N == 0: no-op
+    g = lib.fp8blk_quant_act_t_grouped
+    assert g(P, 100, 128, P, 0, 256, P, P, 0, NULL) == INVALID    # E < 1
+    assert g(P, 100, 100, P, 4, 256, P, P, 0, NULL) == SHAPE      # K % 64
+    assert g(P, 100, 128, P, 4, 200, P, P, 0, NULL) == SHAPE      # ld % 128
+    assert g(P, 100, 128, NULL, 4, 256, P, P, 0, NULL) == INVALID
+    assert g(P, 100, 128, P + 2, 4, 256, P, P, 0, NULL) == ALIGN
+    assert g(NULL, 0, 128, NULL, 4, 256, NULL, NULL, 0, NULL) == OK
+    h = lib.fp8blk_grouped_gemm_rowscaled
+    assert h(P, P, P, P, P, 0, 256, 128, 128, P, NULL) == INVALID    # E < 1
+    assert h(P, P, P, P, P, 4, 256, 130, 128, P, NULL) == SHAPE
+    assert h(P, P, P, P, P, 4, 200, 128, 128, P, NULL) == SHAPE       # ld % 128
+    assert h(P, P, P, P, P, 4, (1 << 24) + 128, 128, 128, P, NULL) == SHAPE
+    assert h(P, P, P, P, NULL, 4, 256, 128, 128, P, NULL) == INVALID
+    assert h(P, P, P, P, P + 2, 4, 256, 128, 128, P, NULL) == ALIGN
 
 
 def test_python_entry_points_raise(lib):

@@ -181,3 +181,112 @@ def test_dgrad_full_size_sampled(fp8blk_lib):
     y_ref = oracle.gemm_ref(qa, sa, qwt_r[kcols], swt_r[blocks])
     got = dx[torch.from_numpy(rows).to(DEV)][:, torch.from_numpy(kcols).to(DEV)].float().cpu().numpy()
     assert_within_tolerance(got, y_ref, what="sampled dgrad")
+
+
+# ------------------------------------------------------------ expert-grouped backward
+
+MOE_OFFSETS = [0, 100, 100, 356, 357, 557, 813]   # 100, 0, 256, 1, 200, 256 rows
+
+
+def _moe_case(seed, n, k, offsets=MOE_OFFSETS):
+    g = synth.generator(84, seed)
+    m = offsets[-1]
+    dy = (synth.activation(m, n, g, 0.005, 30.0).float() * 2.0 ** -10).to(torch.bfloat16)
+    x = synth.activation(m, k, g, 0.005, 30.0)
+    w = synth.weight((len(offsets) - 1) * n, k, g).reshape(len(offsets) - 1, n, k)
+    return dy, x, w, torch.tensor(offsets, dtype=torch.int32)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_quant_weight_t_grouped(fp8blk_lib, pow2):
+    _, _, w, _ = _moe_case(1, 256, 384)
+    e = w.shape[0]
+    qt, cq = guarded((e, 384, 256), torch.uint8, DEV)
+    st, cs = guarded((e, 3, 2), torch.float32, DEV)
+    fb.quant_weight_t(w.to(DEV), pow2, qt=qt, st=st)
+    cq()
+    cs()
+    for i in range(e):
+        q_r, s_r = oracle.quant_weight_t_ref(w[i], pow2)
+        assert_codes_equal(qt[i].cpu().numpy(), q_r, "expert %d transposed weight codes" % i)
+        assert_scales_equal(st[i].cpu().numpy(), s_r, "expert %d transposed weight scales" % i)
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("k", [64, 192])
+def test_quant_act_t_grouped(fp8blk_lib, k, pow2):
+    """Ragged experts (an empty one, a one-row one): codes and scales of
+    every expert group bit for bit, padding columns 0, and nothing written
+    past the padded axis' used part."""
+    _, x, _, off = _moe_case(2, 128, k)
+    m, e = x.shape[0], off.shape[0] - 1
+    ld = fb.padded_tokens(m, e)
+    qt, cq = guarded((k, ld), torch.uint8, DEV)
+    st, cs = guarded((k, ld // 128), torch.float32, DEV)
+    qt.fill_(0xA5)
+    st.fill_(-1.0)
+    fb.quant_act_t_grouped(x.to(DEV), off.to(DEV), pow2, qt=qt, st=st)
+    cq()
+    cs()
+    q_r, s_r = oracle.quant_act_t_grouped_ref(x, off.numpy(), pow2)
+    used = q_r.shape[1]
+    assert_codes_equal(qt[:, :used].cpu().numpy(), q_r, "grouped transposed codes")
+    assert_scales_equal(st[:, :used // 128].cpu().numpy(), s_r, "grouped transposed scales")
+    assert bool(torch.all(qt[:, used:] == 0xA5)) and bool(torch.all(st[:, used // 128:] == -1.0))
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+def test_grouped_dgrad(fp8blk_lib, pow2):
+    dy, _, w, off = _moe_case(3, 256, 384)
+    qwt, swt = fb.quant_weight_t(w.to(DEV), pow2)
+    dx = fb.grouped_dgrad(dy.to(DEV), qwt, swt, off.to(DEV), pow2)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_dgrad_ref(dy, w, off.numpy(), pow2)
+    assert_within_tolerance(dx.float().cpu().numpy(), ref, what="grouped dgrad")
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("n,k", [(256, 384), (128, 640)])
+def test_grouped_wgrad(fp8blk_lib, n, k, pow2):
+    """Every expert's dW within tolerance (rms per expert); the empty
+    expert's dW is exactly zero."""
+    dy, x, _, off = _moe_case(4 + n, n, k)
+    dw = fb.grouped_wgrad(dy.to(DEV), x.to(DEV), off.to(DEV), pow2)
+    torch.cuda.synchronize()
+    ref = oracle.grouped_wgrad_ref(dy, x, off.numpy(), pow2)
+    got = dw.float().cpu().numpy()
+    for i in range(ref.shape[0]):
+        if MOE_OFFSETS[i + 1] == MOE_OFFSETS[i]:
+            assert np.all(got[i] == 0)
+        else:
+            assert_within_tolerance(got[i], ref[i], what="grouped wgrad expert %d" % i)
+
+
+def test_grouped_backward_full_size_sampled(fp8blk_lib):
+    """Qwen3-30B-A3B gate_up (4096 tokens, top-8 of 128 experts, hidden 2048,
+    2 x 768 outputs): grouped dgrad on sampled rows and grouped wgrad on a
+    128 x 128 corner of sampled experts (largest, median, smallest). The
+    128x1 groups run along tokens within one column, so a column subset of
+    dY and X gives exactly that subset of dW."""
+    x, w, off = synth.moe_inputs(0, "gate_up")
+    m, (e, n, k) = x.shape[0], w.shape
+    g = synth.generator(85)
+    dy = (synth.activation(m, n, g, 0.005, 30.0).float() * 2.0 ** -10).to(torch.bfloat16)
+    offs = off.numpy().astype(np.int64)
+    od = off.to(DEV)
+    qwt, swt = fb.quant_weight_t(w.to(DEV))
+    dx = fb.grouped_dgrad(dy.to(DEV), qwt, swt, od)
+    dw = fb.grouped_wgrad(dy.to(DEV), x.to(DEV), od)
+    torch.cuda.synchronize()
+    sizes = np.diff(offs)
+    picks = sorted({int(np.argmax(sizes)), int(np.argsort(sizes)[len(sizes) // 2]), int(np.argmin(sizes))})
+    for ex in picks:
+        lo, hi = int(offs[ex]), int(offs[ex + 1])
+        rows = np.unique(np.array([lo, hi - 1, (lo + hi) // 2]))
+        ref = oracle.dgrad_ref(dy[torch.from_numpy(rows)], w[ex])
+        assert_within_tolerance(dx[torch.from_numpy(rows).to(DEV)].float().cpu().numpy(), ref,
+                                what="full-size grouped dgrad, expert %d" % ex)
+        cols_n, cols_k = slice(1408, 1536), slice(0, 128)
+        ref = oracle.grouped_wgrad_ref(dy[lo:hi, cols_n], x[lo:hi, cols_k], [0, hi - lo])[0]
+        assert_within_tolerance(dw[ex, cols_n, cols_k].float().cpu().numpy(), ref,
+                                what="full-size grouped wgrad, expert %d (%d tokens)" % (ex, hi - lo))
