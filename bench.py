@@ -404,6 +404,46 @@ def time_backward(fb, workload, dev, reps):
     return out
 
 
+def time_backward_moe(fb, dev, reps):
+    """The expert-grouped backward GEMMs of the MoE block (gate_up and down,
+    rows in expert order): grouped dgrad (quant_act of dY, the per-expert
+    transposed weight blocks, the grouped GEMM) and grouped wgrad (the
+    grouped transposed quantizer of dY and X on the padded token axis, the
+    grouped GEMM with per-row scales). GEMM roofline entries as for the
+    dense backward, algorithmic bytes counting the padded operands."""
+    import torch
+    import synth
+    out = {}
+    for which in ("gate_up", "down"):
+        x, w, off = synth.moe_inputs(0, which)
+        m, (e, n, k) = x.shape[0], w.shape
+        g = synth.generator(0x61)
+        dy = (synth.activation(m, n, g, 0.005, 30.0).float() * 2.0 ** -10).to(torch.bfloat16).to(dev)
+        xd, od = x.to(dev), off.to(dev)
+        qwt, swt = fb.quant_weight_t(w.to(dev))
+        qa, sa = fb.quant_act(dy)
+        dx = torch.empty(m, k, dtype=torch.bfloat16, device=dev)
+        qat, sat = fb.quant_act_t_grouped(dy, od)
+        qbt, sbt = fb.quant_act_t_grouped(xd, od)
+        dw = torch.empty(e, n, k, dtype=torch.bfloat16, device=dev)
+        t_dgrad = graph_time_ms(lambda: fb.grouped_gemm(qa, sa, qwt, swt, od, y=dx), reps)
+        t_wgrad = graph_time_ms(lambda: fb.grouped_gemm_rowscaled(qat, sat, qbt, sbt, od, y=dw), reps)
+        t_qat = graph_time_ms(lambda: (fb.quant_act_t_grouped(dy, od, qt=qat, st=sat),
+                                       fb.quant_act_t_grouped(xd, od, qt=qbt, st=sbt)), reps)
+        flops = 2.0 * m * n * k
+        pad = int(sum(((int(off[i + 1]) - int(off[i]) + 127) // 128) * 128 for i in range(e)))
+        out[which] = {
+            "shape": [m, n, k, e],
+            "dgrad": roofline(flops, m * n + e * n * k + 4 * m * n // 128 + 4 * e * n * k // 16384 + 2 * m * k,
+                              t_dgrad, None),
+            "wgrad": roofline(flops, (n + k) * pad + 4 * (n + k) * pad // 128 + 2 * e * n * k, t_wgrad, None),
+            "quant_act_t_grouped_us": round(t_qat * 1e3, 1),
+        }
+        del x, w, dy, xd, qwt, swt, qa, sa, dx, qat, sat, qbt, sbt, dw
+        torch.cuda.empty_cache()
+    return out
+
+
 def kernel_bytes(layers):
     """Algorithmic HBM bytes per launch kind, summed over one step."""
     qa = sum(2 * L["m"] * L["k"] + L["m"] * L["k"] + 4 * L["m"] * L["k"] // 128 for L in layers)
@@ -652,10 +692,13 @@ def main():
                           ("silu_mul_quant_act", "silu_mul_quant_act_kernel")):
             t = traffic_rec.get(key, {}).get("bytes_per_launch")
             out["producers"][name]["traffic"] = None if t is None else round(t)
-    if not args.no_backward and args.workload != "moe":
+    if not args.no_backward:
         print("bench: timing the backward GEMMs", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
-        out["backward"] = time_backward(fb, args.workload, dev, args.backward_reps)
+        if args.workload == "moe":
+            out["backward"] = time_backward_moe(fb, dev, args.backward_reps)
+        else:
+            out["backward"] = time_backward(fb, args.workload, dev, args.backward_reps)
     if not args.no_kv:
         print("bench: timing the FP8 KV-cache path", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
