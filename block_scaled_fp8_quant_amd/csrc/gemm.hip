@@ -60,16 +60,12 @@ constexpr int64_t kMaxK = int64_t(1) << 24;
 // RB_ = true: B carries one scale per row and K block, SB[N][KB] (the wgrad
 // operands: 128x1 groups on both sides), so the fold needs a scale per
 // output column.
-// KG_ > 1: KG_ groups of WAVES waves split the K loop inside the workgroup;
-// group g owns its own STAGES LDS stages and computes K blocks g, g + KG_,
-// g + 2 KG_, ..., and the groups' accumulators are added in group order at
-// the end (K / 128 must be a multiple of KG_).
-template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 2, bool RB_ = false, int KG_ = 1>
+template <int BM_, int BN_, int WAVES_M_, int WAVES_N_, int STAGES_ = 2, bool RB_ = false>
 struct Tile {
-  static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_, KG = KG_;
+  static constexpr int BM = BM_, BN = BN_, STAGES = STAGES_;
   static constexpr bool RB = RB_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
-  static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES * KG;
+  static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
   // 1 KB direct-load windows (8 rows of 128 bytes) per wave per K step
@@ -83,12 +79,7 @@ struct Tile {
   // A tile, B tile, BM row scales, then a 256-byte window of weight scales
   // (RB: BN row scales of B)
   static constexpr int STAGE = A_BYTES + B_BYTES + BM * 4 + (RB ? BN * 4 : 256);
-  static constexpr int GROUP_LDS = STAGES * STAGE;             // one K group's stages
-  static constexpr int LDS = KG * GROUP_LDS + 4 * WAVES * KG;   // stages, then one scale verdict per wave
-  // the accumulators of groups 1 .. KG-1, written over the stages after the K loop
-  static constexpr int REDUCE_BYTES = (KG - 1) * WAVES * (BM / WAVES_M) * (BN / WAVES_N) * 4;
-  static_assert(REDUCE_BYTES <= KG * GROUP_LDS, "K-group partial sums fit the stages");
-  static_assert(KG == 1 || !RB, "K groups: weight-block scales only");
+  static constexpr int LDS = STAGES * STAGE + 4 * WAVES;  // stages, then one scale verdict per wave
   // direct loads one wave issues per stage: its A and B windows and one scale window
   static constexpr int LOADS_PER_STAGE = A_WIN + B_WIN + 1;
   static_assert(STAGES == 2 || STAGES == 4 || STAGES == 8, "stage index is kb mod STAGES");
@@ -121,14 +112,8 @@ using BigRB = Tile<256, 256, 2, 4, 2, true>;
 using MidRB = Tile<128, 128, 2, 2, FP8BLK_MID_STAGES, true>;
 using SmallRB = Tile<64, 64, 1, 4, FP8BLK_SMALL_STAGES, true>;
 using Skinny = Tile<256, 128, 4, 2, 2>;
-// 64x64 tiles with the K loop split over 2 or 4 groups of 4 waves: few rows
-// and few column tiles (a decode step's narrower linears), where one
-// 4-wave workgroup per CU leaves each SIMD a single wave with 4 MFMAs per
-// K step.
-using SmallK2 = Tile<64, 64, 1, 4, 2, false, 2>;
-using SmallK4 = Tile<64, 64, 1, 4, 2, false, 4>;
 static_assert(Big::LDS <= 160 * 1024 && Mid::LDS <= 160 * 1024 && Small::LDS <= 160 * 1024 &&
-                  Skinny::LDS <= 160 * 1024 && SmallK2::LDS <= 160 * 1024 && SmallK4::LDS <= 160 * 1024,
+                  Skinny::LDS <= 160 * 1024,
               "LDS budget");
 static_assert(BigRB::LDS <= 160 * 1024 && MidRB::LDS <= 160 * 1024 && SmallRB::LDS <= 160 * 1024, "LDS budget");
 
@@ -222,7 +207,7 @@ __device__ __forceinline__ uint32_t clamp_len(int64_t bytes) {
 // same BN/128 weight scales into the stage's last window.
 template <class C>
 __device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp, int kb, int wave, bool live) {
-  const uint32_t koff = (uint32_t)kb * BK * C::KG;  // a K group's blocks are KG apart
+  const uint32_t koff = (uint32_t)kb * BK;
   const rsrc_t a = make_rsrc(lp.a, live ? lp.a_len : 0u);
   const rsrc_t b = make_rsrc(lp.b, live ? lp.b_len : 0u);
   const rsrc_t s = make_rsrc(lp.s, live ? lp.s_len : 0u);
@@ -235,7 +220,7 @@ __device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp
   const int window = wave < C::BM / 64 ? wave
                      : C::RB ? C::BM / 64 + (wave - C::BM / 64 < C::BN / 64 ? wave - C::BM / 64 : C::BN / 64 - 1)
                              : C::BM / 64;
-  dma4(s, lp.s_off, (uint32_t)kb * 4 * C::KG, stage + C::A_BYTES + C::B_BYTES + window * 256);
+  dma4(s, lp.s_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + window * 256);
 }
 
 // acc[j] += p[j] * sc for the TN accumulator quads of one m-subtile.
@@ -527,20 +512,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
                                           int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
                                           int64_t m0, int64_t n0, uint8_t* smem_generic, int64_t ld, int64_t kb0) {
   static_assert(C::TM % 4 == 0, "activation fragments alternate between two registers; scales read 4 at a time");
-  const int lane = threadIdx.x & 63;
-  // uniform: scalar addressing. kg = K group, wave = the wave within it
-  const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kg = wave_all / C::WAVES, wave = wave_all % C::WAVES;
-  uint8_t* const smem_all = smem_generic;
-  smem_generic += kg * C::GROUP_LDS;
   lds_u8* smem = (lds_u8*)smem_generic;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
   const int wm = (wave / C::WAVES_N) * C::WM;
   const int wn = (wave % C::WAVES_N) * C::WN;
   const int g = lane >> 4, c16 = lane & 15;
-  const int KB_all = __builtin_amdgcn_readfirstlane((int)(K / BK));  // K <= 2^24
-  const int KB = KB_all / C::KG;                                      // K steps of this group
-  const int64_t KBld = ld / BK;                                       // scales per operand row
-  kb0 += kg;                                                          // the group's first K block
+  const int KB = __builtin_amdgcn_readfirstlane((int)(K / BK));  // K <= 2^24
+  const int64_t KBld = ld / BK;                                   // scales per operand row
 
   LoadPlan<C> lp;
 #pragma unroll
@@ -601,45 +580,21 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     k_loop<C, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
   } else {
     ScaleScan<C> scan;
-    scan_begin<C>(scan, sa, sw, M, N, m0, n0, wave, KB_all, lane);  // every group scans all of K
+    scan_begin<C>(scan, sa, sw, M, N, m0, n0, wave, KB, lane);
 #pragma unroll
     for (int b = 0; b < C::STAGES; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
-    uint32_t* verdict = reinterpret_cast<uint32_t*>(smem_all + C::KG * C::GROUP_LDS);
+    uint32_t* verdict = reinterpret_cast<uint32_t*>(smem_generic + C::STAGES * C::STAGE);
     const bool ok = scan_end<C>(scan, lane);
-    if (lane == 0) verdict[wave_all] = ok ? 1u : 0u;
+    if (lane == 0) verdict[wave] = ok ? 1u : 0u;
     wait_vm<C::LOADS_PER_STAGE * (C::STAGES - 1)>();  // block 0 has landed (the scan's later loads too)
     lds_barrier();
     bool pow2 = true;
 #pragma unroll
-    for (int w = 0; w < C::WAVES * C::KG; ++w) pow2 = pow2 & (verdict[w] != 0u);
+    for (int w = 0; w < C::WAVES; ++w) pow2 = pow2 & (verdict[w] != 0u);
     if (pow2)
       k_loop<C, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
     else
       k_loop<C, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
-  }
-
-  if constexpr (C::KG > 1) {
-    // Groups 1 .. KG-1 leave their sums in LDS (over the stages: every wave
-    // has waited for its own direct loads, and the barrier covers the
-    // others'); group 0 adds them in group order, so the result does not
-    // depend on timing, and stores the tile.
-    v4f* red = reinterpret_cast<v4f*>(smem_all);  // [group-1][wave][i][j][lane]
-    lds_barrier();
-    if (kg > 0) {
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j)
-          red[((((kg - 1) * C::WAVES + wave) * C::TM + i) * C::TN + j) * 64 + lane] = acc[i][j];
-    }
-    lds_barrier();
-    if (kg > 0) return;
-#pragma unroll
-    for (int q = 1; q < C::KG; ++q)
-#pragma unroll
-      for (int i = 0; i < C::TM; ++i)
-#pragma unroll
-        for (int j = 0; j < C::TN; ++j) acc[i][j] += red[((((q - 1) * C::WAVES + wave) * C::TM + i) * C::TN + j) * 64 + lane];
   }
 
   if (!cols_valid) return;
@@ -794,11 +749,7 @@ int64_t tiles_of(int64_t M, int64_t N) {
 
 // At most 256 rows with at least 3/4 of the CUs' worth of 256x128 tiles:
 // Skinny. Otherwise the largest tile that still gives every CU at least two
-// workgroups' worth of tiles; below that, 64x64 tiles, with the K loop split
-// over 2 or 4 groups of waves where few tiles would leave the CUs short of
-// waves (the groups' sums are added in a fixed order, so results are
-// deterministic; their rounding differs from an unsplit sum within the
-// accumulation tolerance).
+// workgroups' worth of tiles; below that, the smallest.
 extern "C" fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                                      int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const fp8blk_status st = check_gemm_args(qa, sa, qw, sw, M, N, K, y);
@@ -807,14 +758,6 @@ extern "C" fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa, const u
     return launch_gemm<Skinny>(qa, sa, qw, sw, M, N, K, y, stream);
   if (tiles_of<Big>(M, N) >= kCUs) return launch_gemm<Big>(qa, sa, qw, sw, M, N, K, y, stream);
   if (tiles_of<Mid>(M, N) >= 2 * kCUs) return launch_gemm<Mid>(qa, sa, qw, sw, M, N, K, y, stream);
-  // 64x64 tiles. Split K inside the workgroup where that measured faster:
-  // at most half the CUs' worth of tiles (4 groups), or at most one tile per
-  // CU with a K loop of at most 32 blocks (2 groups); a full chip of tiles
-  // over a long K runs faster unsplit.
-  const int64_t tiles = tiles_of<Small>(M, N), kb = K / kBlock;
-  if (tiles <= kCUs / 2 && kb % 4 == 0 && kb >= 16) return launch_gemm<SmallK4>(qa, sa, qw, sw, M, N, K, y, stream);
-  if (tiles <= kCUs && kb % 2 == 0 && kb >= 8 && kb <= 32)
-    return launch_gemm<SmallK2>(qa, sa, qw, sw, M, N, K, y, stream);
   return launch_gemm<Small>(qa, sa, qw, sw, M, N, K, y, stream);
 }
 

@@ -94,9 +94,6 @@ fp8blk_status fp8blk_quant_weight(const uint16_t* w, int64_t N, int64_t K,
  *   y  [M][N] bf16 out (16-byte aligned)
  *   M >= 0 (M == 0: no-op), N > 0, K > 0, N % 128 == 0, K % 128 == 0,
  *   K <= 2^24 (the kernels address a 256-row tile with 32-bit offsets).
- * The fp32 accumulation order follows from (M, N, K): for few 64x64 tiles
- * the K blocks are summed in 2 or 4 interleaved groups whose sums are then
- * added in group order. The same call always gives the same bits.
  */
 fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa,
                           const uint8_t* qw, const float* sw,

@@ -244,23 +244,22 @@ def test_each_tile_configuration(fp8blk_lib, m, k, n, pow2):
 
 @pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("m,k,n", [
-    (100, 2048, 512),    # 16 tiles of 64x64, 16 K blocks: the K loop split over 4 groups of waves
-    (1, 4096, 1024),     # one row, 32 K blocks: 4 groups
-    (200, 1024, 4096),   # 256 tiles, 8 K blocks, M tail: 2 groups
+    (100, 2048, 512),    # 16 tiles of 64x64 over 16 K blocks, M tail
+    (1, 4096, 1024),     # one row, 32 K blocks
+    (200, 1024, 4096),   # 256 tiles of 64x64, 8 K blocks, M tail
 ])
-def test_split_k_tiles(fp8blk_lib, m, k, n, pow2):
-    """64x64 tiles whose K loop is split over groups of waves inside the
-    workgroup, each group summing every 2nd or 4th K block and the groups'
-    sums added in group order; with fold and with power-of-two scales."""
+def test_few_tiles_long_k(fp8blk_lib, m, k, n, pow2):
+    """Few 64x64 tiles over many K blocks (the four-stage pipeline's refills
+    and the zero-length loads past the end), with fold and with
+    power-of-two scales."""
     g = synth.generator(16, seed=m + k + n)
     x = synth.activation(m, k, g, 0.005, 30.0)
     w = synth.weight(n, k, g)
     _layer_check(x, w, pow2)
 
 
-def test_split_k_deterministic(fp8blk_lib):
-    """The groups' partial sums are added in a fixed order: repeated calls
-    give the same bits."""
+def test_few_tiles_deterministic(fp8blk_lib):
+    """Repeated calls on a few-tile problem give the same bits."""
     g = synth.generator(17)
     qa, sa = fb.quant_act(synth.activation(100, 2048, g, 0.005, 30.0).to(DEV))
     qw, sw = fb.quant_weight(synth.weight(512, 2048, g).to(DEV))
