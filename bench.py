@@ -98,9 +98,11 @@ def source_hash(kernel="gemm_kernel"):
 
 
 def build_layers(workload, dev):
-    """Synthetic bf16 inputs resident on the GPU plus preallocated outputs."""
+    """Synthetic bf16 inputs resident on the GPU plus preallocated outputs
+    (and the split-K workspace of the few-row linears)."""
     import torch
     import synth
+    import block_scaled_fp8_quant_amd as fb
     layers = []
     if workload == "moe":
         for which in ("gate_up", "down"):
@@ -121,7 +123,9 @@ def build_layers(workload, dev):
     for li, (name, k, n) in enumerate(wl.linears):
         x, w = synth.linear_inputs(workload, li)
         m = wl.m
+        need = fb.fp8blk_gemm_workspace_size(m, n, k)
         layers.append(dict(name=name, x=x.to(dev), w=w.to(dev), m=m, n=n, k=k, e=0, pow2=wl.pow2,
+                           ws=torch.empty(need, dtype=torch.uint8, device=dev) if need else None,
                            qa=torch.empty(m, k, dtype=torch.uint8, device=dev),
                            sa=torch.empty(m, k // 128, dtype=torch.float32, device=dev),
                            qw=torch.empty(n, k, dtype=torch.uint8, device=dev),
@@ -156,7 +160,7 @@ def step(fb, layers, events=None):
         if L["e"]:
             timed("gemm", lambda: fb.grouped_gemm(L["qa"], L["sa"], L["qw"], L["sw"], L["off"], y=L["y"]))
         else:
-            timed("gemm", lambda: fb.gemm(L["qa"], L["sa"], L["qw"], L["sw"], y=L["y"]))
+            timed("gemm", lambda: fb.gemm(L["qa"], L["sa"], L["qw"], L["sw"], y=L["y"], workspace=L["ws"]))
 
 
 RMS_EPS = 1e-5
@@ -371,7 +375,9 @@ def time_backward(fb, workload, dev, reps):
         qat, sat = fb.quant_act_t(dy, pow2)
         qbt, sbt = fb.quant_act_t(x, pow2)
         dw = torch.empty(n, k, dtype=torch.bfloat16, device=dev)
-        t_dgrad = graph_time_ms(lambda: fb.gemm(qa, sa, qwt, swt, y=dx), reps)
+        need = fb.fp8blk_gemm_workspace_size(m, k, n)  # dX [m, k] contracts over n
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        t_dgrad = graph_time_ms(lambda: fb.gemm(qa, sa, qwt, swt, y=dx, workspace=ws), reps)
         t_wgrad = graph_time_ms(lambda: fb.gemm_rowscaled(qat, sat, qbt, sbt, y=dw), reps)
         t_qat = graph_time_ms(lambda: (fb.quant_act_t(dy, pow2, qt=qat, st=sat),
                                        fb.quant_act_t(x, pow2, qt=qbt, st=sbt)), reps)

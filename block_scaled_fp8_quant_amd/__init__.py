@@ -8,7 +8,7 @@ CPU fallback: if the library is missing, every call raises.
 
 Two layers:
   * ``fp8blk_quant_act``, ``fp8blk_quant_weight``, ``fp8blk_gemm``,
-    ``fp8blk_grouped_gemm``, ``fp8blk_rmsnorm_quant_act``,
+    ``fp8blk_gemm_ws``, ``fp8blk_grouped_gemm``, ``fp8blk_rmsnorm_quant_act``,
     ``fp8blk_silu_mul_quant_act``, ``fp8blk_qkv_amax``, ``fp8blk_kv_scales``,
     ``fp8blk_kv_cache_write``, ``fp8blk_quant_act_t``,
     ``fp8blk_quant_weight_t``, ``fp8blk_gemm_rowscaled``,
@@ -55,6 +55,7 @@ def load():
         "fp8blk_quant_act": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_quant_weight": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
+        "fp8blk_gemm_ws": [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_size_t, vp],
         "fp8blk_grouped_gemm": [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp],
         "fp8blk_rmsnorm_quant_act": [vp, vp, f32, i64, i64, vp, vp, vp, i32, vp],
         "fp8blk_silu_mul_quant_act": [vp, i64, i64, vp, vp, vp, i32, vp],
@@ -74,6 +75,8 @@ def load():
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.fp8blk_gemm_workspace_size.argtypes = [i64, i64, i64]
+    lib.fp8blk_gemm_workspace_size.restype = ctypes.c_size_t
     lib.fp8blk_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64]
     lib.fp8blk_decode_attention_workspace_size.restype = ctypes.c_size_t
     lib.fp8blk_status_string.argtypes = [ctypes.c_int]
@@ -102,6 +105,14 @@ def fp8blk_quant_weight(w, N, K, q, s, pow2, stream):
 
 def fp8blk_gemm(qa, sa, qw, sw, M, N, K, y, stream):
     return _call("fp8blk_gemm", qa, sa, qw, sw, M, N, K, y, stream)
+
+
+def fp8blk_gemm_ws(qa, sa, qw, sw, M, N, K, y, workspace, workspace_bytes, stream):
+    return _call("fp8blk_gemm_ws", qa, sa, qw, sw, M, N, K, y, workspace, workspace_bytes, stream)
+
+
+def fp8blk_gemm_workspace_size(M, N, K):
+    return load().fp8blk_gemm_workspace_size(M, N, K)
 
 
 def fp8blk_grouped_gemm(qa, sa, qw, sw, offsets, E, total_M, N, K, y, stream):
@@ -232,8 +243,13 @@ def quant_weight(w, pow2=False, q=None, s=None):
     return q, s
 
 
-def gemm(qa, sa, qw, sw, y=None):
-    """Y[M, N] bf16 = block-scaled (QA, SA) x (QW, SW)^T."""
+def gemm(qa, sa, qw, sw, y=None, split=True, workspace=None):
+    """Y[M, N] bf16 = block-scaled (QA, SA) x (QW, SW)^T.
+
+    split: few-row problems may split K over a workspace (fp8blk_gemm_ws);
+    ``workspace`` (a contiguous uint8 device tensor of at least
+    fp8blk_gemm_workspace_size(M, N, K) bytes) is allocated here when not
+    given. split=False runs fp8blk_gemm."""
     torch = _torch()
     if qa.dim() != 2 or qw.dim() != 2:
         raise ValueError("qa must be [M, K] and qw [N, K]")
@@ -248,8 +264,17 @@ def gemm(qa, sa, qw, sw, y=None):
     _check(sw, "sw", torch.float32, (n // BLOCK, k // BLOCK), dev)
     y = torch.empty((m, n), dtype=torch.bfloat16, device=dev) if y is None else y
     _check(y, "y", torch.bfloat16, (m, n), dev)
-    fp8blk_gemm(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), m, n, k, y.data_ptr(),
-                _stream(dev))
+    need = fp8blk_gemm_workspace_size(m, n, k) if split else 0
+    if need:
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        if workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous uint8 tensor on the device of qa")
+        fp8blk_gemm_ws(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), m, n, k, y.data_ptr(),
+                       workspace.data_ptr(), workspace.numel(), _stream(dev))
+    else:
+        fp8blk_gemm(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), m, n, k, y.data_ptr(),
+                    _stream(dev))
     return y
 
 
@@ -614,7 +639,8 @@ def linear(x, qw, sw, pow2=False):
 
 __all__ = [
     "BLOCK", "Fp8BlkError", "LIB_PATH", "load",
-    "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
+    "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_gemm_ws", "fp8blk_gemm_workspace_size",
+    "fp8blk_grouped_gemm",
     "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act",
     "fp8blk_qkv_amax", "fp8blk_kv_scales", "fp8blk_kv_cache_write",
     "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled", "fp8blk_decode_attention",

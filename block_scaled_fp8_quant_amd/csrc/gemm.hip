@@ -509,11 +509,16 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
 // plain GEMMs pass ld = K and kb0 = 0, the grouped wgrad an expert's token
 // range on the padded token axis (per-row scales only: the weight-block
 // scan below assumes ld = K, kb0 = 0).
-template <class C>
+//
+// PARTIAL: the tile's fp32 sums go to part[M][N] (16-byte stores, y is not
+// used) and the K loop always folds (the split-K GEMM passes a K range of
+// the operands, which the power-of-two scan does not handle).
+template <class C, bool PARTIAL = false>
 __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const float* __restrict__ sa,
                                           const uint8_t* __restrict__ qw, const float* __restrict__ sw,
                                           int64_t M, int64_t N, int64_t K, uint16_t* __restrict__ y,
-                                          int64_t m0, int64_t n0, uint8_t* smem_generic, int64_t ld, int64_t kb0) {
+                                          int64_t m0, int64_t n0, uint8_t* smem_generic, int64_t ld, int64_t kb0,
+                                          float* __restrict__ part = nullptr) {
   static_assert(C::TM % 4 == 0, "activation fragments alternate between two registers; scales read 4 at a time");
   lds_u8* smem = (lds_u8*)smem_generic;
   const int lane = threadIdx.x & 63;
@@ -574,8 +579,8 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
   // flight while one is computed. The loop body is branch-free: past the
   // last block the refill uses resources of length zero (out-of-range loads
   // fetch nothing) and the fragments read ahead are not used.
-  if constexpr (C::RB) {
-    // per-row scales on both operands: always the fold path
+  if constexpr (C::RB || PARTIAL) {
+    // per-row scales on both operands, or a K range: always the fold path
 #pragma unroll
     for (int b = 0; b < C::STAGES; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
     wait_vm<C::LOADS_PER_STAGE * (C::STAGES - 1)>();  // block 0 has landed
@@ -602,6 +607,18 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
 
   if (!cols_valid) return;
   // lane holds Y[m0 + wm + 16i + l%16][n0 + wn + 16j + 4*(l/16) + r], r < 4 (Y rows N long)
+  if constexpr (PARTIAL) {
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i) {
+      const int64_t row = m0 + wm + 16 * i + c16;
+      if (row < M) {
+        float* pr = part + row * N + n0 + wn + 4 * g;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) *reinterpret_cast<v4f*>(pr + 16 * j) = acc[i][j];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < C::TM; ++i) {
     const int64_t row = m0 + wm + 16 * i + c16;
@@ -643,6 +660,37 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const uint8_t* __restrict
   int64_t m_tile, n_tile;
   tile_of_block(blockIdx.x, gridDim.x, m_tiles, n_tiles, m_tile, n_tile);
   gemm_tile<Cfg>(qa, sa, qw, sw, M, N, K, y, m_tile * Cfg::BM, n_tile * Cfg::BN, smem, K, 0);
+}
+
+// Split-K GEMM for few rows (M <= BM: one row tile): workgroup b computes
+// column tile b / splits over K blocks [s KB / splits, (s+1) KB / splits),
+// s = b % splits, and writes its fp32 sums to part[s][M][N].
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) void gemm_splitk_kernel(const uint8_t* __restrict__ qa,
+                                                              const float* __restrict__ sa,
+                                                              const uint8_t* __restrict__ qw,
+                                                              const float* __restrict__ sw, int64_t M, int64_t N,
+                                                              int64_t K, float* __restrict__ part, int splits) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS];
+  const int n_tile = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / (uint32_t)splits));
+  const int split = __builtin_amdgcn_readfirstlane((int)(blockIdx.x % (uint32_t)splits));
+  const int64_t KB = K / BK;
+  const int64_t kb_lo = KB * split / splits, kb_hi = KB * (split + 1) / splits;
+  gemm_tile<Cfg, true>(qa, sa, qw, sw, M, N, (kb_hi - kb_lo) * BK, nullptr, 0, (int64_t)n_tile * Cfg::BN, smem, K,
+                       kb_lo, part + (int64_t)split * M * N);
+}
+
+// y = bf16(sum over s of part[s]), s in order (the result does not depend on
+// timing); 4 outputs per thread, M * N a multiple of 4.
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const v4f* __restrict__ part, int splits, int64_t n4,
+                                                            uint2* __restrict__ y) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  v4f sum = part[i];
+  for (int s = 1; s < splits; ++s) sum += part[(int64_t)s * n4 + i];
+  const uint32_t lo = (uint32_t)to_bf16_bits(sum[0]) | ((uint32_t)to_bf16_bits(sum[1]) << 16);
+  const uint32_t hi = (uint32_t)to_bf16_bits(sum[2]) | ((uint32_t)to_bf16_bits(sum[3]) << 16);
+  y[i] = make_uint2(lo, hi);
 }
 
 template <class Cfg>
@@ -747,6 +795,21 @@ int64_t tiles_of(int64_t M, int64_t N) {
   return ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
 }
 
+// K ranges of fp8blk_gemm_ws: 0 (the plain path) unless the rows fit one
+// 256-row tile, its 256x128 column tiles are too few to fill the CUs and K
+// is long (at least 64 blocks); then as many ranges as give about one
+// workgroup per CU, each at least 8 K blocks long. Measured against the
+// plain path at 256 rows: K = 14336 and 28672 gain 25-40%, K = 4096 loses
+// (the fp32 partials, S * M * N * 4 bytes written and read back, then
+// outweigh the weights).
+int64_t splitk_count(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || M > Skinny::BM || N <= 0 || K <= 0 || N % kBlock || K % kBlock || K > kMaxK) return 0;
+  const int64_t n_tiles = N / Skinny::BN, kb = K / kBlock;
+  if (n_tiles >= kCUs * 3 / 4 || kb < 64) return 0;  // the plain path is faster
+  const int64_t s = std::min<int64_t>(kCUs / n_tiles, kb / 8);
+  return s >= 2 ? s : 0;
+}
+
 }  // namespace
 }  // namespace fp8blk
 
@@ -762,6 +825,35 @@ extern "C" fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa, const u
   if (tiles_of<Big>(M, N) >= kCUs) return launch_gemm<Big>(qa, sa, qw, sw, M, N, K, y, stream);
   if (tiles_of<Mid>(M, N) >= 2 * kCUs) return launch_gemm<Mid>(qa, sa, qw, sw, M, N, K, y, stream);
   return launch_gemm<Small>(qa, sa, qw, sw, M, N, K, y, stream);
+}
+
+extern "C" size_t fp8blk_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
+  const int64_t s = splitk_count(M, N, K);
+  return s ? (size_t)(s * M * N) * sizeof(float) : 0;
+}
+
+// Few rows and few column tiles: the K loop is cut into splitk_count ranges
+// over 256x128 tiles, whose fp32 sums go to the workspace; a second kernel
+// adds them in range order and rounds to bf16. Otherwise fp8blk_gemm.
+extern "C" fp8blk_status fp8blk_gemm_ws(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                                        int64_t M, int64_t N, int64_t K, uint16_t* y, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+  const fp8blk_status st = check_gemm_args(qa, sa, qw, sw, M, N, K, y);
+  if (st != FP8BLK_OK || M == 0) return st;
+  const int64_t splits = splitk_count(M, N, K);
+  if (!workspace || splits == 0) return fp8blk_gemm(qa, sa, qw, sw, M, N, K, y, stream);
+  if (!aligned(workspace, 16)) return FP8BLK_ERR_ALIGNMENT;
+  if (workspace_bytes < fp8blk_gemm_workspace_size(M, N, K)) return FP8BLK_ERR_INVALID_ARG;
+  float* part = static_cast<float*>(workspace);
+  const int64_t n_tiles = N / Skinny::BN;
+  hipLaunchKernelGGL(gemm_splitk_kernel<Skinny>, dim3((uint32_t)(n_tiles * splits)), dim3(Skinny::NT), 0, stream, qa,
+                     sa, qw, sw, M, N, K, part, (int)splits);
+  const fp8blk_status ls = launch_status();
+  if (ls != FP8BLK_OK) return ls;
+  const int64_t n4 = M * N / 4;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const v4f*>(part), (int)splits, n4, reinterpret_cast<uint2*>(y));
+  return launch_status();
 }
 
 // Expert groups: 128-row tiles when the average expert has at least 128

@@ -101,6 +101,38 @@ fp8blk_status fp8blk_gemm(const uint8_t* qa, const float* sa,
                           uint16_t* y, hipStream_t stream);
 
 /*
+ * fp8blk_gemm with a caller-owned workspace that lets few-row problems with
+ * a long contraction (M <= 256, too few 256x128 column tiles to fill the
+ * CUs, K >= 8192: a decode step's down projection, the dgrad of a wide
+ * linear) split the K loop: each of S K ranges (S from M, N, K) writes its
+ * fp32 sums of the same y formula to the workspace, and a second kernel on
+ * the same stream adds the S ranges in order and rounds to bf16. The result
+ * is within the same accumulation tolerance as fp8blk_gemm's (it adds the
+ * same products in another order) and the same call always gives the same
+ * bits.
+ *   arguments as fp8blk_gemm, plus
+ *   workspace    NULL, or device memory of at least
+ *                fp8blk_gemm_workspace_size(M, N, K) bytes (16-byte aligned,
+ *                owned by the caller, contents undefined on entry and exit).
+ *                Calls that share a workspace must be ordered on one stream.
+ * With a NULL workspace, or when the size query gives 0, the call is exactly
+ * fp8blk_gemm. A workspace smaller than the size query's value is
+ * FP8BLK_ERR_INVALID_ARG.
+ */
+fp8blk_status fp8blk_gemm_ws(const uint8_t* qa, const float* sa,
+                             const uint8_t* qw, const float* sw,
+                             int64_t M, int64_t N, int64_t K, uint16_t* y,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * Workspace bytes fp8blk_gemm_ws uses for (M, N, K) (host only, no HIP
+ * call): S * M * N * 4 when it splits K into S ranges, else 0 (also for
+ * invalid shapes).
+ */
+size_t fp8blk_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/*
  * Expert-grouped block-scaled GEMM for mixture-of-experts layers (upppp.jp,
  * «まとめ»; greentreeone.com, «Реальные прирост производительности»): rows
  * offsets[e] .. offsets[e+1]-1 of (qa, sa) are multiplied by expert e's

@@ -34,7 +34,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
-        "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_grouped_gemm",
+        "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_gemm_ws", "fp8blk_gemm_workspace_size",
+        "fp8blk_grouped_gemm",
         "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_qkv_amax", "fp8blk_kv_scales",
         "fp8blk_kv_cache_write", "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
         "fp8blk_decode_attention", "fp8blk_decode_attention_workspace_size", "fp8blk_quant_weight_t_grouped",
@@ -100,6 +101,29 @@ def test_gemm_validation(lib):
     assert f(P, P, P, P, 4, 128, 128, P4, NULL) == ALIGN
     assert f(P, P + 1, P, P, 4, 128, 128, P, NULL) == ALIGN
     assert f(NULL, NULL, NULL, NULL, 0, 128, 128, NULL, NULL) == OK
+
+
+def test_gemm_ws_validation(lib):
+    f = lib.fp8blk_gemm_ws
+    size = lib.fp8blk_gemm_workspace_size
+    # the same argument checks as fp8blk_gemm, before the workspace is looked at
+    assert f(P, P, P, P, -1, 128, 128, P, P, 1 << 30, NULL) == INVALID
+    assert f(P, P, P, P, 4, 130, 128, P, P, 1 << 30, NULL) == SHAPE
+    assert f(P4, P, P, P, 4, 128, 128, P, P, 1 << 30, NULL) == ALIGN
+    assert f(NULL, NULL, NULL, NULL, 0, 128, 128, NULL, P, 0, NULL) == OK
+    # a decode step's down projection (256 x 4096, K = 14336): 32 column tiles of 128, K split 8 ways
+    need = size(256, 4096, 14336)
+    assert need == 8 * 256 * 4096 * 4
+    assert f(P, P, P, P, 256, 4096, 14336, P, P, need - 1, NULL) == INVALID
+    assert f(P, P, P, P, 256, 4096, 14336, P, P + 4, need, NULL) == ALIGN
+    # ranges of at least 8 K blocks, at least 64 blocks in all; a wide layer fills the CUs unsplit;
+    # more than 256 rows never split
+    assert size(1, 256, 8192) == 8 * 1 * 256 * 4
+    assert size(256, 12288, 8192) == 2 * 256 * 12288 * 4
+    assert size(256, 4096, 4096) == 0
+    assert size(256, 28672, 16384) == 0
+    assert size(257, 4096, 14336) == 0
+    assert size(0, 4096, 14336) == 0 and size(256, 130, 14336) == 0 and size(256, 4096, 130) == 0
 
 
 def test_grouped_gemm_validation(lib):

@@ -269,6 +269,50 @@ def test_few_tiles_deterministic(fp8blk_lib):
 
 
 @pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("m,k,n", [
+    (256, 8192, 1024),   # 8 column tiles of 128, K split into 8 ranges
+    (37, 8192, 512),     # M tail
+    (1, 16384, 256),     # one row, 16 ranges
+    (200, 8320, 384),    # 65 K blocks in 8 ranges of 8 and 9
+])
+def test_split_k_over_a_workspace(fp8blk_lib, m, k, n, pow2):
+    """Few rows, few column tiles and a long K: gemm() splits K over a
+    workspace (fp8blk_gemm_ws), the ranges' fp32 sums added in order."""
+    assert fb.fp8blk_gemm_workspace_size(m, n, k) > 0
+    g = synth.generator(18, seed=m + k + n)
+    x = synth.activation(m, k, g, 0.005, 30.0)
+    w = synth.weight(n, k, g)
+    _layer_check(x, w, pow2)
+
+
+def test_split_k_deterministic_and_fallback(fp8blk_lib):
+    """Repeated split calls give the same bits, also when one workspace
+    serves two problems in turn; a NULL workspace is exactly fp8blk_gemm."""
+    g = synth.generator(19)
+    x = synth.activation(256, 8192, g, 0.005, 30.0)
+    w = synth.weight(1024, 8192, g)
+    qa, sa = fb.quant_act(x.to(DEV))
+    qw, sw = fb.quant_weight(w.to(DEV))
+    ws = torch.empty(fb.fp8blk_gemm_workspace_size(256, 1024, 8192), dtype=torch.uint8, device=DEV)
+    y1 = fb.gemm(qa, sa, qw, sw, workspace=ws)
+    qa2, sa2 = fb.quant_act(synth.activation(64, 8192, g).to(DEV))
+    y_other = fb.gemm(qa2, sa2, qw, sw, workspace=ws)   # reuses (and overwrites) the workspace
+    y2 = fb.gemm(qa, sa, qw, sw, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    qa_r, sa_r = oracle.quant_act_ref(x)
+    qw_r, sw_r = oracle.quant_weight_ref(w)
+    assert_within_tolerance(y1.float().cpu().numpy(), oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r))
+    assert y_other.shape == (64, 1024)
+    y_plain = fb.gemm(qa, sa, qw, sw, split=False)
+    y_null = torch.empty_like(y_plain)
+    fb.fp8blk_gemm_ws(qa.data_ptr(), sa.data_ptr(), qw.data_ptr(), sw.data_ptr(), 256, 1024, 8192,
+                      y_null.data_ptr(), None, 0, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert torch.equal(y_plain.view(torch.int16), y_null.view(torch.int16))
+
+
+@pytest.mark.parametrize("pow2", [False, True])
 @pytest.mark.parametrize("k", [128, 384])
 def test_big_tile_one_and_odd_k_blocks(fp8blk_lib, k, pow2):
     """256x256 tiles with a single K block and with an odd number of blocks
