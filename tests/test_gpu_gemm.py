@@ -159,11 +159,10 @@ def test_grouped_with_empty_and_ragged_experts(fp8blk_lib):
     _grouped_check(x, w, off)
 
 
-def test_grouped_full_chunks_and_remainders(fp8blk_lib):
-    """Experts of at least 128 rows on average: each expert's full 256-row
-    chunks run on 256x256 tiles and the rest on 128x128 tiles (two
-    launches); sizes with 0, 1 and 2 chunks, remainders of 0, 1, 88, 130
-    and 255 rows, and an empty expert."""
+def test_grouped_large_and_ragged_experts(fp8blk_lib):
+    """Experts of at least 128 rows on average (128x128 tiles): experts
+    spanning up to five tiles with partial last tiles of 1 to 127 rows,
+    exactly two full tiles, and an empty expert."""
     counts = [600, 0, 256, 130, 1, 511, 300]
     off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32)
     assert int(off[-1]) >= 128 * len(counts)
