@@ -66,6 +66,15 @@ struct Tile {
   static constexpr bool RB = RB_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES;
+  // PAIR (the 256x256 tile): the first half of the waves issue every
+  // refill load, their own windows, those of wave w + WAVES/2 and the
+  // weight-scale window. Waves w and w + WAVES/2 share a SIMD and the
+  // older one, w, is issued first and finishes its rows of a K step well
+  // ahead of the younger, which then runs alone until the step's barrier;
+  // moving the younger wave's loads to the older balances the pair
+  // (5-10% faster on the prefill GEMMs; on the 256x128 tile it measured
+  // faster with hot operands but slower with the weights cold in HBM).
+  static constexpr bool PAIR = WAVES_M_ * WAVES_N_ == 8 && BM == 256 && BN == 256 && !RB_;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
   // 1 KB direct-load windows (8 rows of 128 bytes) per wave per K step
@@ -83,7 +92,7 @@ struct Tile {
   // direct loads one wave issues per stage: its A and B windows and one scale window
   static constexpr int LOADS_PER_STAGE = A_WIN + B_WIN + 1;
   static_assert(STAGES >= 2 && STAGES <= 8, "stage index is kb mod STAGES (a multiply for 3)");
-  static_assert(LOADS_PER_STAGE * (STAGES - 1) <= 63, "outstanding loads fit the vmcnt counter");
+  static_assert(LOADS_PER_STAGE * 2 * (STAGES - 1) <= 63, "outstanding loads fit the vmcnt counter");
 };
 
 // Tile configurations, picked per call from the problem shape (host side):
@@ -197,6 +206,9 @@ struct LoadPlan {
   uint32_t a_off[C::A_WIN], b_off[C::B_WIN], s_off;
   const void *a, *b, *s;        // first byte of the tile's rows (scales: row or column block)
   uint32_t a_len, b_len, s_len;  // bytes from there to the operand's end (clamped to 4 GB - 1)
+  const void* w;                 // PAIR: the weight-scale window's plan
+  uint32_t w_len, w_off;
+  uint32_t a_pair, b_pair;       // PAIR: byte distance to wave w + WAVES/2's rows
 };
 
 __device__ __forceinline__ uint32_t clamp_len(int64_t bytes) {
@@ -224,6 +236,41 @@ __device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp
                      : C::RB ? C::BM / 64 + (wave - C::BM / 64 < C::BN / 64 ? wave - C::BM / 64 : C::BN / 64 - 1)
                              : C::BM / 64;
   dma4(s, lp.s_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + window * 256);
+}
+
+// PAIR: wave w < WAVES/2 issues the loads of its own windows and of wave
+// w + WAVES/2's (the same lane offsets plus a fixed row distance: the
+// swizzle key repeats every 16 rows), its activation-scale window and the
+// weight-scale window; the other waves issue nothing.
+template <class C>
+__device__ __forceinline__ void issue_stage_pair(lds_u8* stage, const LoadPlan<C>& lp, int kb, int wave, bool live) {
+  constexpr int H = C::WAVES / 2;
+  const uint32_t koff = (uint32_t)kb * BK;
+  const rsrc_t a = make_rsrc(lp.a, live ? lp.a_len : 0u);
+  const rsrc_t b = make_rsrc(lp.b, live ? lp.b_len : 0u);
+  const rsrc_t s = make_rsrc(lp.s, live ? lp.s_len : 0u);
+  const rsrc_t w = make_rsrc(lp.w, live ? lp.w_len : 0u);
+#pragma unroll
+  for (int i = 0; i < C::A_WIN; ++i) {
+    dma16(a, lp.a_off[i], koff, stage + (wave * C::A_WIN + i) * 1024);
+    dma16(a, lp.a_off[i], koff + lp.a_pair, stage + ((wave + H) * C::A_WIN + i) * 1024);
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_WIN; ++i) {
+    dma16(b, lp.b_off[i], koff, stage + C::A_BYTES + (wave * C::B_WIN + i) * 1024);
+    dma16(b, lp.b_off[i], koff + lp.b_pair, stage + C::A_BYTES + ((wave + H) * C::B_WIN + i) * 1024);
+  }
+  dma4(s, lp.s_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + wave * 256);
+  dma4(w, lp.w_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + (C::BM / 64) * 256);
+}
+
+template <class C>
+__device__ __forceinline__ void refill(lds_u8* stage, const LoadPlan<C>& lp, int kb, int wave, bool live) {
+  if constexpr (C::PAIR) {
+    if (wave < C::WAVES / 2) issue_stage_pair<C>(stage, lp, kb, wave, live);  // uniform
+  } else {
+    issue_stage<C>(stage, lp, kb, wave, live);
+  }
 }
 
 // acc[j] += p[j] * sc for the TN accumulator quads of one m-subtile.
@@ -352,7 +399,7 @@ __device__ __forceinline__ bool scan_end(const ScaleScan<C>& sc, int lane) {
 // a power of two): the MFMA applies SW and SA itself as E8M0 block scales
 // (source 0 = weights: the wave's SW; source 1 = activations: the lane's
 // row's SA) and accumulates into acc directly, with no fold.
-template <class C, bool POW2>
+template <class C, bool POW2, bool LOADER = true>
 __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, const LoadPlan<C>& lp, int wave, int KB,
                                        int wm, int wn, int g, int c16, v4f (&acc)[C::TM][C::TN]) {
   constexpr int S = C::STAGES, LPS = C::LOADS_PER_STAGE;
@@ -468,9 +515,12 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
       ea_last = e8m0_of(srow[(C::TM - 1) / 4][(C::TM - 1) % 4]);
     else
       sc_last = C::RB ? srow[(C::TM - 1) / 4][(C::TM - 1) % 4] : srow[(C::TM - 1) / 4][(C::TM - 1) % 4] * swv;
-    wait_vm<LPS * (S - 2)>();  // (3) block kb+1 has landed
+    wait_vm<LPS * (C::PAIR ? 2 : 1) * (S - 2)>();  // (3) block kb+1 has landed
     lds_barrier();
-    issue_stage<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
+    if constexpr (!C::PAIR)
+      issue_stage<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
+    else if constexpr (LOADER)
+      issue_stage_pair<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
     sched_fence();
   }
   if constexpr (POW2) {
@@ -565,6 +615,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     lp.s_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
     lp.s_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
   }
+  if constexpr (C::PAIR) {
+    constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;
+    lp.w = sw + (n0 / kBlock) * KBld + kb0;
+    lp.w_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
+    lp.w_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
+    lp.a_pair = (uint32_t)(C::WAVES / 2 * C::A_WIN * 8) * (uint32_t)ld;
+    lp.b_pair = (uint32_t)(C::WAVES / 2 * C::B_WIN * 8) * (uint32_t)ld;
+  }
   // N % 128 == 0 and WN divides 128: a wave's columns are all in or all out
   const bool cols_valid = n0 + wn < N;
 
@@ -579,30 +637,44 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
   // flight while one is computed. The loop body is branch-free: past the
   // last block the refill uses resources of length zero (out-of-range loads
   // fetch nothing) and the fragments read ahead are not used.
+  // PAIR: the loading and the other waves run their own copy of the loop
+  // (no branch inside it); loading waves have twice the loads per stage
+  const bool loader = !C::PAIR || wave < C::WAVES / 2;
   if constexpr (C::RB || PARTIAL) {
     // per-row scales on both operands, or a K range: always the fold path
 #pragma unroll
-    for (int b = 0; b < C::STAGES; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
-    wait_vm<C::LOADS_PER_STAGE * (C::STAGES - 1)>();  // block 0 has landed
+    for (int b = 0; b < C::STAGES; ++b) refill<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
+    wait_vm<C::LOADS_PER_STAGE * (C::PAIR ? 2 : 1) * (C::STAGES - 1)>();  // block 0 has landed
     lds_barrier();
-    k_loop<C, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+    if (loader)
+      k_loop<C, false, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+    else
+      k_loop<C, false, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
   } else {
     ScaleScan<C> scan;
     scan_begin<C>(scan, sa, sw, M, N, m0, n0, wave, KB, lane);
 #pragma unroll
-    for (int b = 0; b < C::STAGES; ++b) issue_stage<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
+    for (int b = 0; b < C::STAGES; ++b) refill<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
     uint32_t* verdict = reinterpret_cast<uint32_t*>(smem_generic + C::STAGES * C::STAGE);
     const bool ok = scan_end<C>(scan, lane);
     if (lane == 0) verdict[wave] = ok ? 1u : 0u;
-    wait_vm<C::LOADS_PER_STAGE * (C::STAGES - 1)>();  // block 0 has landed (the scan's later loads too)
+    // block 0 has landed (the scan's later loads too); PAIR: twice the loads per stage
+    wait_vm<C::LOADS_PER_STAGE * (C::PAIR ? 2 : 1) * (C::STAGES - 1)>();
     lds_barrier();
     bool pow2 = true;
 #pragma unroll
     for (int w = 0; w < C::WAVES; ++w) pow2 = pow2 & (verdict[w] != 0u);
-    if (pow2)
-      k_loop<C, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
-    else
-      k_loop<C, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+    if (pow2) {
+      if (loader)
+        k_loop<C, true, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+      else
+        k_loop<C, true, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+    } else {
+      if (loader)
+        k_loop<C, false, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+      else
+        k_loop<C, false, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+    }
   }
 
   if (!cols_valid) return;
