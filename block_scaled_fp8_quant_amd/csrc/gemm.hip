@@ -66,15 +66,16 @@ struct Tile {
   static constexpr bool RB = RB_;
   static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
   static constexpr int WAVES = WAVES_M * WAVES_N, NT = 64 * WAVES;
-  // PAIR (the 256x256 tile): the first half of the waves issue every
+  // PAIR (the 256x256 tiles): the first half of the waves issue every
   // refill load, their own windows, those of wave w + WAVES/2 and the
-  // weight-scale window. Waves w and w + WAVES/2 share a SIMD and the
+  // weight-scale window (RB: wave w + WAVES/2's B-row scale window). Waves w and w + WAVES/2 share a SIMD and the
   // older one, w, is issued first and finishes its rows of a K step well
   // ahead of the younger, which then runs alone until the step's barrier;
   // moving the younger wave's loads to the older balances the pair
-  // (5-10% faster on the prefill GEMMs; on the 256x128 tile it measured
+  // (5-10% faster on the prefill GEMMs, 5-15% on the wgrad GEMMs; on the
+  // 256x128 tile it measured
   // faster with hot operands but slower with the weights cold in HBM).
-  static constexpr bool PAIR = WAVES_M_ * WAVES_N_ == 8 && BM == 256 && BN == 256 && !RB_;
+  static constexpr bool PAIR = WAVES_M_ * WAVES_N_ == 8 && BM == 256 && BN == 256;
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static constexpr int TM = WM / 16, TN = WN / 16;
   // 1 KB direct-load windows (8 rows of 128 bytes) per wave per K step
@@ -261,7 +262,8 @@ __device__ __forceinline__ void issue_stage_pair(lds_u8* stage, const LoadPlan<C
     dma16(b, lp.b_off[i], koff + lp.b_pair, stage + C::A_BYTES + ((wave + H) * C::B_WIN + i) * 1024);
   }
   dma4(s, lp.s_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + wave * 256);
-  dma4(w, lp.w_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + (C::BM / 64) * 256);
+  // weights: the one weight-scale window; RB: the B-row scales of wave w + WAVES/2
+  dma4(w, lp.w_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + (C::BM / 64 + (C::RB ? wave : 0)) * 256);
 }
 
 template <class C>
@@ -615,11 +617,17 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     lp.s_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
     lp.s_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
   }
-  if constexpr (C::PAIR) {
+  if constexpr (C::PAIR && C::RB) {  // B-row scales of tile rows 64w + lane
+    lp.w = sw + n0 * KBld + kb0;
+    lp.w_len = clamp_len(((N - n0) * KBld - kb0) * 4);
+    lp.w_off = (uint32_t)(wave * 64 + lane) * (uint32_t)(KBld * 4);
+  } else if constexpr (C::PAIR) {
     constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;
     lp.w = sw + (n0 / kBlock) * KBld + kb0;
     lp.w_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
     lp.w_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
+  }
+  if constexpr (C::PAIR) {
     lp.a_pair = (uint32_t)(C::WAVES / 2 * C::A_WIN * 8) * (uint32_t)ld;
     lp.b_pair = (uint32_t)(C::WAVES / 2 * C::B_WIN * 8) * (uint32_t)ld;
   }
