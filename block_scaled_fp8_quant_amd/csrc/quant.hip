@@ -100,30 +100,36 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const u32x4* __restri
 // (128 consecutive rows of one column) and written transposed; dgrad reads W
 // along N, so the weight's 128x128 blocks are written transposed.
 
-// X [M][K] -> Q^T [K][M], S^T [K][M/128]: one workgroup per 128 x 64 tile
-// (rows m0.., columns k0..). Thread t loads rows 2q, 2q+1 (q = t/8, +32)
-// of 16-byte column chunk t%8 and stores each column's two values as one
-// dword of LDS row k (a column of the tile) at dword q: 64 LDS rows of 128
-// values, row stride 65 dwords, so both these writes and the reads below
-// hit 64 distinct banks. Then thread t = 4k + p takes rows 32p..32p+31 of
-// column k: the four lanes of a quad hold one 128-row group, reduced by
-// two DPP steps, and store its 128 codes as one contiguous 128-byte run.
+// X [M][K] -> Q^T [K][M], S^T [K][M/128]: one workgroup of 4W threads per
+// 128 x W tile (rows m0.., columns k0..; W = 128 when K % 128 == 0 and
+// K <= 16384, else 64: each row is read in 256- or 128-byte pieces). Thread t loads rows 2q,
+// 2q+1 (q = t/(W/8), +32) of 16-byte column chunk t%(W/8) and stores each
+// column's two values as one dword of LDS row k (a column of the tile) at
+// dword q: W LDS rows of 128 values, row stride 65 dwords (the reads below
+// hit 64 distinct banks; with W = 128 the writes are 2-way). Then thread
+// t = 4k + p takes rows 32p..32p+31 of column k: the four lanes of a quad
+// hold one 128-row group, reduced by two DPP steps, and store its 128 codes
+// as one contiguous 128-byte run.
 constexpr int kTStride = 65;  // dwords per LDS row
+// 128-wide tiles up to this K (measured 2-13% faster than 64-wide at K = 4096 .. 14336 on 16384
+// rows, 4% slower at K = 28672)
+constexpr int64_t kQuantTWideMaxK = 16384;
 
 //
 // GROUPED: rows sorted by expert (offsets[E+1] on the device); the 128-row
 // tiles start at each expert's first row and rows past the expert's end
 // read as zero, and tile t of the concatenated per-expert tile lists is
 // written at columns 128t.. of Q^T rows ld long (the padded token axis).
-template <bool GROUPED>
-__global__ __launch_bounds__(256) void quant_act_t_kernel(const u32x4* __restrict__ x, int64_t M, int64_t K,
-                                                          u32x4* __restrict__ qt, float* __restrict__ st,
-                                                          int pow2, const int32_t* __restrict__ offsets, int E,
-                                                          int64_t ld) {
-  __shared__ uint32_t lds[64 * kTStride];
+template <int W, bool GROUPED>
+__global__ __launch_bounds__(4 * W) void quant_act_t_kernel(const u32x4* __restrict__ x, int64_t M, int64_t K,
+                                                            u32x4* __restrict__ qt, float* __restrict__ st,
+                                                            int pow2, const int32_t* __restrict__ offsets, int E,
+                                                            int64_t ld) {
+  static_assert(W == 64 || W == 128, "tile width: 8 or 16 sixteen-byte units per row");
+  __shared__ uint32_t lds[W * kTStride];
   const int t = threadIdx.x;
-  const int64_t k_tiles = K / 64;
-  const int64_t tile = blockIdx.x / k_tiles, k0 = (int64_t)(blockIdx.x % k_tiles) * 64;
+  const int64_t k_tiles = K / W;
+  const int64_t tile = blockIdx.x / k_tiles, k0 = (int64_t)(blockIdx.x % k_tiles) * W;
   int64_t m0 = tile * 128, rows = 128;  // source rows m0 .. m0 + rows - 1
   if (GROUPED) {
     int e, j;
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(256) void quant_act_t_kernel(const u32x4* __restric
   } else {
     ld = M;
   }
-  const int c = t & 7, q = t >> 3;
+  const int c = t % (W / 8), q = t / (W / 8);  // q < 32
   const int64_t row_units = K / 8;
   u32x4 v[4];
 #pragma unroll
@@ -582,11 +588,16 @@ extern "C" fp8blk_status fp8blk_quant_act_t(const uint16_t* x, int64_t M, int64_
   if (M == 0) return FP8BLK_OK;
   if (!x || !qt || !st) return FP8BLK_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(qt, 16) || !aligned(st, 4)) return FP8BLK_ERR_ALIGNMENT;
-  const int64_t blocks = (M / kBlock) * (K / 64);
+  const int64_t blocks = (M / kBlock) * (K / 64);  // the 64-wide count bounds the 128-wide one
   if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_act_t_kernel<false>, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2, nullptr, 0,
-                     M);
+  if (K % 128 == 0 && K <= kQuantTWideMaxK)
+    hipLaunchKernelGGL((quant_act_t_kernel<128, false>), dim3((uint32_t)(blocks / 2)), dim3(512), 0, stream,
+                       reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2, nullptr, 0,
+                       M);
+  else
+    hipLaunchKernelGGL((quant_act_t_kernel<64, false>), dim3((uint32_t)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2, nullptr, 0,
+                       M);
   return launch_status();
 }
 
@@ -601,9 +612,14 @@ extern "C" fp8blk_status fp8blk_quant_act_t_grouped(const uint16_t* x, int64_t M
   const int64_t tiles = ld / kBlock;  // the padded axis holds at most this many 128-token tiles
   const int64_t blocks = tiles * (K / 64);
   if (blocks > INT32_MAX) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(quant_act_t_kernel<true>, dim3((uint32_t)blocks), dim3(256), 0, stream,
-                     reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2, offsets,
-                     (int)E, ld);
+  if (K % 128 == 0 && K <= kQuantTWideMaxK)
+    hipLaunchKernelGGL((quant_act_t_kernel<128, true>), dim3((uint32_t)(blocks / 2)), dim3(512), 0, stream,
+                       reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2, offsets,
+                       (int)E, ld);
+  else
+    hipLaunchKernelGGL((quant_act_t_kernel<64, true>), dim3((uint32_t)blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4*>(x), M, K, reinterpret_cast<u32x4*>(qt), st, pow2, offsets,
+                       (int)E, ld);
   return launch_status();
 }
 
