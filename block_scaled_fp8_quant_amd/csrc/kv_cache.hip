@@ -109,14 +109,27 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // uniform over the wave
+  const u32x4* kr = k + t * ld_units;
+  const u32x4* vr = v + t * ld_units;
+  const int64_t row_units = Hkv * head_units;
+  // The first 128 units of K and V are loaded before the slot index is read,
+  // so the two memory round trips overlap (a skipped token wastes them).
+  u32x4 k1, v1, k2, v2;
+  auto load = [&](int64_t u0) {
+    const int64_t u1 = u0 + lane, u2 = u0 + 64 + lane;
+    const bool l1 = u1 < row_units, l2 = u2 < row_units;
+    k1 = l1 ? __builtin_nontemporal_load(&kr[u1]) : u32x4{0, 0, 0, 0};
+    v1 = l1 ? __builtin_nontemporal_load(&vr[u1]) : u32x4{0, 0, 0, 0};
+    k2 = l2 ? __builtin_nontemporal_load(&kr[u2]) : u32x4{0, 0, 0, 0};
+    v2 = l2 ? __builtin_nontemporal_load(&vr[u2]) : u32x4{0, 0, 0, 0};
+  };
+  load(0);
   const int64_t sl = slot[t];
   if (sl < 0 || sl >= num_slots) return;  // uniform
   const float ks = *k_scale, vs = *v_scale;
   const float kinv = 1.0f / ks, vinv = 1.0f / vs;  // correctly rounded (inf for a zero scale: unused)
   const bool kf = ks >= kCalibratedMinScale && ks <= kCalibratedMaxScale;
   const bool vf = vs >= kCalibratedMinScale && vs <= kCalibratedMaxScale;
-  const u32x4* kr = k + t * ld_units;
-  const u32x4* vr = v + t * ld_units;
   // head-major pages: head h of slot sl is row sl % block_size of head h's
   // block_size x D panel in page sl / block_size
   const int64_t page = sl / block_size, row = sl % block_size;
@@ -125,18 +138,14 @@ __global__ __launch_bounds__(256) void kv_cache_write_kernel(
   const uint32_t hu = (uint32_t)head_units;
   u32x2* kc = k_cache + first;
   u32x2* vc = v_cache + first;
-  const int64_t row_units = Hkv * head_units;
   auto dst = [&](int64_t u) {  // unit u of the token's [Hkv][D] codes
     const uint32_t h = (uint32_t)u / hu;
     return (int64_t)h * head_stride + ((uint32_t)u - h * hu);
   };
   for (int64_t u0 = 0; u0 < row_units; u0 += 128) {
+    if (u0 > 0) load(u0);  // uniform
     const int64_t u1 = u0 + lane, u2 = u0 + 64 + lane;
     const bool l1 = u1 < row_units, l2 = u2 < row_units;
-    const u32x4 k1 = l1 ? __builtin_nontemporal_load(&kr[u1]) : u32x4{0, 0, 0, 0};
-    const u32x4 v1 = l1 ? __builtin_nontemporal_load(&vr[u1]) : u32x4{0, 0, 0, 0};
-    const u32x4 k2 = l2 ? __builtin_nontemporal_load(&kr[u2]) : u32x4{0, 0, 0, 0};
-    const u32x4 v2 = l2 ? __builtin_nontemporal_load(&vr[u2]) : u32x4{0, 0, 0, 0};
     const uint32_t wk1[4] = {k1.x, k1.y, k1.z, k1.w}, wv1[4] = {v1.x, v1.y, v1.z, v1.w};
     const uint32_t wk2[4] = {k2.x, k2.y, k2.z, k2.w}, wv2[4] = {v2.x, v2.y, v2.z, v2.w};
     if (l1) {
