@@ -172,6 +172,18 @@ def test_grouped_large_and_ragged_experts(fp8blk_lib):
     _grouped_check(x, w, off)
 
 
+def test_grouped_256_row_tiles_ragged_experts(fp8blk_lib):
+    """Experts averaging at least 256 rows with K >= 2048 (256x256 tiles):
+    experts of 0, 1, 130, 256, 300, 511 and 600 rows, partial last tiles."""
+    counts = [600, 0, 256, 130, 1, 511, 300]
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32)
+    assert int(off[-1]) >= 256 * len(counts)
+    g = synth.generator(11)
+    x = synth.activation(int(off[-1]), 2048, g, 0.01, 50.0)
+    w = synth.weight(len(counts) * 256, 2048, g).reshape(len(counts), 256, 2048)
+    _grouped_check(x, w, off)
+
+
 def test_grouped_single_expert_equals_gemm(fp8blk_lib):
     x, w = synth.linear_inputs("tiny", 0)
     qa, sa = fb.quant_act(x.to(DEV))
