@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "fp8blk.h"
+#include "ranges.h"
 
 namespace fp8blk {
 
@@ -43,13 +44,17 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Find which expert owns M-tile `t` of the concatenated per-expert tile
-// lists (expert e has ceil(M_e / BM) tiles). Every lane of the wave
-// computes the same answer: lanes take 64 experts at a time and a wave
-// prefix sum turns per-expert tile counts into tile ranges. The results are
-// passed through readfirstlane so the compiler knows they are uniform (they
-// feed the scalar base addresses of buffer resources; otherwise each
-// resource would be built in a loop over the lanes).
+// Find which expert owns M-tile `t` (0 <= t < 2^24) of the concatenated
+// per-expert tile lists (expert e has ceil(M_e / BM) tiles). Every lane of
+// the wave computes the same answer: lanes take 64 experts at a time and a
+// wave prefix sum turns per-expert tile counts into tile ranges. The
+// results are passed through readfirstlane so the compiler knows they are
+// uniform (they feed the scalar base addresses of buffer resources;
+// otherwise each resource would be built in a loop over the lanes).
+// Counts come from tile_count (negative lengths count 0, each count at most
+// 2^24), so `base` stays below 2^24 + 2^30 and the returned expert is
+// always in [0, E); offsets that break their contract give a wrong expert
+// or tile, never an index outside the arrays.
 template <int BM>
 __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int E, int t, int& expert,
                                             int& tile_in_expert) {
@@ -57,7 +62,7 @@ __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int
   int base = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
-    const int cnt = e < E ? (off[e + 1] - off[e] + BM - 1) / BM : 0;
+    const int cnt = e < E ? tile_count(off[e], off[e + 1], BM) : 0;
     int incl = cnt;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
@@ -67,7 +72,9 @@ __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int
     const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));  // uniform: so is the branch
     if (t < base + total) {
       const bool mine = cnt > 0 && t >= base + incl - cnt && t < base + incl;
-      const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      const unsigned long long owners = (unsigned long long)__ballot(mine);
+      if (owners == 0ull) return false;  // uniform; unreachable with consistent counts
+      const int src = __ffsll(owners) - 1;
       expert = __builtin_amdgcn_readfirstlane(e0 + src);
       tile_in_expert = __builtin_amdgcn_readfirstlane(t - base - __shfl(incl - cnt, src));
       return true;
@@ -79,19 +86,20 @@ __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int
 
 // Sum over the experts before e of ceil(M_e' / BM): where expert e's tiles
 // start in the concatenated per-expert tile lists (the same in every lane,
-// returned as a uniform value).
+// returned as a uniform value; 64-bit, so broken offsets cannot wrap it).
 template <int BM>
-__device__ __forceinline__ int tiles_before(const int32_t* __restrict__ off, int e) {
+__device__ __forceinline__ int64_t tiles_before(const int32_t* __restrict__ off, int e) {
   const int lane = threadIdx.x & 63;
-  int total = 0;
+  int64_t total = 0;
   for (int e0 = 0; e0 < e; e0 += 64) {
     const int i = e0 + lane;
-    int cnt = i < e ? (off[i + 1] - off[i] + BM - 1) / BM : 0;
+    int cnt = i < e ? tile_count(off[i], off[i + 1], BM) : 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) cnt += __shfl_xor(cnt, d);
+    for (int d = 1; d < 64; d <<= 1) cnt += __shfl_xor(cnt, d);  // <= 64 * 2^24
     total += cnt;
   }
-  return __builtin_amdgcn_readfirstlane(total);
+  return ((int64_t)__builtin_amdgcn_readfirstlane((int)(total >> 32)) << 32) |
+         (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)total);
 }
 
 }  // namespace fp8blk

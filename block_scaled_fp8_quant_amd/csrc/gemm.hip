@@ -209,12 +209,16 @@ struct LoadPlan {
   uint32_t a_len, b_len, s_len;  // bytes from there to the operand's end (clamped to 4 GB - 1)
   const void* w;                 // PAIR: the weight-scale window's plan
   uint32_t w_len, w_off;
-  uint32_t a_pair, b_pair;       // PAIR: byte distance to wave w + WAVES/2's rows
+  // PAIR: the rows of wave w + WAVES/2 (the tile's second half), with their
+  // own resources. The buffer range check covers the VGPR offset only, not
+  // the scalar one, so a row distance passed as the scalar offset would let
+  // a row past the operand's end through; a resource that starts at the
+  // second half's first row puts that row under the check.
+  const void *a2, *b2;
+  uint32_t a2_len, b2_len;
 };
 
-__device__ __forceinline__ uint32_t clamp_len(int64_t bytes) {
-  return bytes < 0xFFFFFFFFll ? (uint32_t)bytes : 0xFFFFFFFFu;
-}
+
 
 // Direct loads of K block kb into `stage`; with live == false every
 // resource has length zero, so the loads fetch nothing. No branches: the
@@ -240,9 +244,10 @@ __device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp
 }
 
 // PAIR: wave w < WAVES/2 issues the loads of its own windows and of wave
-// w + WAVES/2's (the same lane offsets plus a fixed row distance: the
-// swizzle key repeats every 16 rows), its activation-scale window and the
-// weight-scale window; the other waves issue nothing.
+// w + WAVES/2's (the same lane offsets into the second half's resources,
+// which start a fixed row distance further: the swizzle key repeats every 16
+// rows), its activation-scale window and the weight-scale window; the other
+// waves issue nothing.
 template <class C>
 __device__ __forceinline__ void issue_stage_pair(lds_u8* stage, const LoadPlan<C>& lp, int kb, int wave, bool live) {
   constexpr int H = C::WAVES / 2;
@@ -251,15 +256,17 @@ __device__ __forceinline__ void issue_stage_pair(lds_u8* stage, const LoadPlan<C
   const rsrc_t b = make_rsrc(lp.b, live ? lp.b_len : 0u);
   const rsrc_t s = make_rsrc(lp.s, live ? lp.s_len : 0u);
   const rsrc_t w = make_rsrc(lp.w, live ? lp.w_len : 0u);
+  const rsrc_t a2 = make_rsrc(lp.a2, live ? lp.a2_len : 0u);
+  const rsrc_t b2 = make_rsrc(lp.b2, live ? lp.b2_len : 0u);
 #pragma unroll
   for (int i = 0; i < C::A_WIN; ++i) {
     dma16(a, lp.a_off[i], koff, stage + (wave * C::A_WIN + i) * 1024);
-    dma16(a, lp.a_off[i], koff + lp.a_pair, stage + ((wave + H) * C::A_WIN + i) * 1024);
+    dma16(a2, lp.a_off[i], koff, stage + ((wave + H) * C::A_WIN + i) * 1024);
   }
 #pragma unroll
   for (int i = 0; i < C::B_WIN; ++i) {
     dma16(b, lp.b_off[i], koff, stage + C::A_BYTES + (wave * C::B_WIN + i) * 1024);
-    dma16(b, lp.b_off[i], koff + lp.b_pair, stage + C::A_BYTES + ((wave + H) * C::B_WIN + i) * 1024);
+    dma16(b2, lp.b_off[i], koff, stage + C::A_BYTES + ((wave + H) * C::B_WIN + i) * 1024);
   }
   dma4(s, lp.s_off, (uint32_t)kb * 4, stage + C::A_BYTES + C::B_BYTES + wave * 256);
   // weights: the one weight-scale window; RB: the B-row scales of wave w + WAVES/2
@@ -627,9 +634,12 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     lp.w_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
     lp.w_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
   }
-  if constexpr (C::PAIR) {
-    lp.a_pair = (uint32_t)(C::WAVES / 2 * C::A_WIN * 8) * (uint32_t)ld;
-    lp.b_pair = (uint32_t)(C::WAVES / 2 * C::B_WIN * 8) * (uint32_t)ld;
+  if constexpr (C::PAIR) {  // the second half's rows, each range-checked against its operand's end
+    constexpr int64_t ha = C::WAVES / 2 * C::A_WIN * 8, hb = C::WAVES / 2 * C::B_WIN * 8;
+    lp.a2 = qa + (m0 + ha) * ld + kb0 * BK;
+    lp.b2 = qw + (n0 + hb) * ld + kb0 * BK;
+    lp.a2_len = clamp_len((M - m0 - ha) * ld - kb0 * BK);
+    lp.b2_len = clamp_len((N - n0 - hb) * ld - kb0 * BK);
   }
   // N % 128 == 0 and WN divides 128: a wave's columns are all in or all out
   const bool cols_valid = n0 + wn < N;
@@ -773,14 +783,17 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const v4f* __restric
   y[i] = make_uint2(lo, hi);
 }
 
+// Expert ranges come from the device offsets clamped to [0, total_M]
+// (expert_tile), so offsets that break their contract give wrong values,
+// never a read outside qa/sa or a write outside y.
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT) void grouped_gemm_kernel(const uint8_t* __restrict__ qa,
                                                                const float* __restrict__ sa,
                                                                const uint8_t* __restrict__ qw,
                                                                const float* __restrict__ sw,
                                                                const int32_t* __restrict__ offsets, int E,
-                                                               int64_t N, int64_t K, uint16_t* __restrict__ y,
-                                                               int n_tiles) {
+                                                               int64_t total_M, int64_t N, int64_t K,
+                                                               uint16_t* __restrict__ y, int n_tiles) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[Cfg::LDS];
   // uniform (readfirstlane): the division runs on the vector unit
   const int t = __builtin_amdgcn_readfirstlane((int)(blockIdx.x / n_tiles));
@@ -791,11 +804,13 @@ __global__ __launch_bounds__(Cfg::NT) void grouped_gemm_kernel(const uint8_t* __
   tile = __builtin_amdgcn_readfirstlane(tile);
   if (!found) return;  // uniform over the workgroup
   // uniform (readfirstlane): they size the buffer resources of every K step
-  const int64_t row0 = __builtin_amdgcn_readfirstlane(offsets[e]);
-  const int64_t rows = __builtin_amdgcn_readfirstlane(offsets[e + 1]) - row0;
+  int64_t row0, rows, m0;
+  if (!expert_tile(__builtin_amdgcn_readfirstlane(offsets[e]), __builtin_amdgcn_readfirstlane(offsets[e + 1]),
+                   total_M, tile, Cfg::BM, row0, rows, m0))
+    return;  // uniform
   const int64_t KB = K / BK;
   gemm_tile<Cfg>(qa + row0 * K, sa + row0 * KB, qw + (int64_t)e * N * K, sw + (int64_t)e * (N / kBlock) * KB,
-                 rows, N, K, y + row0 * N, (int64_t)tile * Cfg::BM, (int64_t)n_tile * Cfg::BN, smem, K, 0);
+                 rows, N, K, y + row0 * N, m0, (int64_t)n_tile * Cfg::BN, smem, K, 0);
 }
 
 // Grouped wgrad: dW_e [N][K] = the row-scaled product of rows of A = Q(dY^T)
@@ -818,9 +833,9 @@ __global__ __launch_bounds__(Cfg::NT) void grouped_rowscaled_kernel(const uint8_
   const int64_t lb = ld / BK;
   int64_t kb0 = tiles_before<BK>(offsets, e);
   kb0 = kb0 < 0 ? 0 : (kb0 > lb ? lb : kb0);
-  int64_t kbn = ((int64_t)__builtin_amdgcn_readfirstlane(offsets[e + 1]) -
-                 __builtin_amdgcn_readfirstlane(offsets[e]) + BK - 1) / BK;
-  kbn = kbn < 0 ? 0 : (kbn > lb - kb0 ? lb - kb0 : kbn);
+  int64_t kbn = tile_count(__builtin_amdgcn_readfirstlane(offsets[e]), __builtin_amdgcn_readfirstlane(offsets[e + 1]),
+                           BK);
+  kbn = kbn > lb - kb0 ? lb - kb0 : kbn;
   gemm_tile<Cfg>(qa, sa, qb, sb, N, K, kbn * BK, y + (int64_t)e * N * K, (int64_t)(t / n_tiles) * Cfg::BM,
                  (int64_t)(t % n_tiles) * Cfg::BN, smem, ld, kb0);
 }
@@ -866,7 +881,7 @@ fp8blk_status launch_grouped(const uint8_t* qa, const float* sa, const uint8_t* 
   const int64_t m_tiles = total_M / Cfg::BM + E;
   if (n_tiles * m_tiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
   hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3((uint32_t)(n_tiles * m_tiles)), dim3(Cfg::NT), 0, stream, qa,
-                     sa, qw, sw, offsets, (int)E, N, K, y, (int)n_tiles);
+                     sa, qw, sw, offsets, (int)E, total_M, N, K, y, (int)n_tiles);
   return launch_status();
 }
 

@@ -134,9 +134,11 @@ __global__ __launch_bounds__(4 * W) void quant_act_t_kernel(const u32x4* __restr
   if (GROUPED) {
     int e, j;
     if (!locate_tile<128>(offsets, E, (int)tile, e, j) || (tile + 1) * 128 > ld) return;  // uniform
-    m0 = (int64_t)offsets[e] + 128 * (int64_t)j;
-    const int64_t end = offsets[e + 1] < M ? offsets[e + 1] : M;
-    rows = end - m0 < 128 ? end - m0 : 128;
+    // the expert's rows clamped to [0, M]: offsets that break their
+    // contract give wrong codes, never a read outside x
+    const RowRange r = clamp_rows(offsets[e], offsets[e + 1], M);
+    m0 = r.lo + 128 * (int64_t)j;
+    rows = r.hi - m0 < 128 ? r.hi - m0 : 128;
   } else {
     ld = M;
   }
