@@ -29,7 +29,13 @@ Pins (tests/test_oracle_attention.py): one cached token returns its value
 row exactly; equal scores give the plain mean of the value rows; a dominant
 score selects its token; the softmax weights equal a Python loop with
 math.exp; permuting the pages (block table) leaves the output unchanged;
-grouped heads read their own KV head.
+grouped heads read their own KV head. The score scaling
+(q_scale * k_scale * sm_scale, default 1/sqrt(D)) is pinned against
+torch's scaled_dot_product_attention in float64 on the dequantized Q, K, V
+(default and explicit scale, grouped heads expanded, ragged lengths, paged
+tables) and against the two-token closed form: the first token's weight is
+the logistic function of the score difference. Planted mistakes in the
+scaling (k_scale dropped, sm_scale squared, 1/D for the default) fail them.
 """
 
 import numpy as np
@@ -37,6 +43,18 @@ import numpy as np
 from .e4m3 import decode
 from .kv_cache import kv_quantize_ref
 from .quant import bf16_values
+
+
+def softmax_scale(d, sm_scale):
+    """The softmax scale: 1/sqrt(D) for standard attention unless given
+    (then the fp32 value the kernels receive)."""
+    return 1.0 / np.sqrt(d) if sm_scale is None else float(np.float32(sm_scale))
+
+
+def scores(dots, qs, ks, sm):
+    """Scores from the exact dot products of the E4M3 values: the per-tensor
+    Q and K scales and the softmax scale multiply each one."""
+    return dots * qs * ks * sm
 
 
 def decode_attention_ref(q, k_cache, v_cache, block_table, block_size, context_lens, q_scale, k_scale, v_scale,
@@ -54,7 +72,7 @@ def decode_attention_ref(q, k_cache, v_cache, block_table, block_size, context_l
     if hq % hkv or k_cache.shape[3] != d or k_cache.shape[2] != block_size:
         raise ValueError("shapes: q [B, Hq, D], caches [num_blocks, Hkv, block_size, D], Hq % Hkv == 0")
     group = hq // hkv
-    sm = 1.0 / np.sqrt(d) if sm_scale is None else float(np.float32(sm_scale))
+    sm = softmax_scale(d, sm_scale)
     qs, ks, vs = (float(np.float32(s)) for s in (q_scale, k_scale, v_scale))
     q8 = decode(kv_quantize_ref(q, qs).reshape(b_, hq, d))
     kd = decode(k_cache)
@@ -69,7 +87,7 @@ def decode_attention_ref(q, k_cache, v_cache, block_table, block_size, context_l
         blk, off = table[b, t // block_size], t % block_size
         for h in range(hq):
             g = h // group
-            s = (kd[blk, g, off, :] @ q8[b, h]) * qs * ks * sm
+            s = scores(kd[blk, g, off, :] @ q8[b, h], qs, ks, sm)
             w = np.exp(s - s.max())
             w /= w.sum()
             out[b, h] = (w @ vd[blk, g, off, :]) * vs

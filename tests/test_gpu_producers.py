@@ -30,9 +30,9 @@ DEV = "cuda:0"
 # two products. 2^-14 leaves a wide margin while still being 64x finer than
 # a bf16 ulp.
 MID_WINDOW = 2.0 ** -14
-# Below the smallest normal number the kernel's fp32 arithmetic may flush
-# to zero; exact values there are compared as zero.
-TINY = 2.0 ** -126
+# No allowance for flushing: the kernels keep IEEE fp32 subnormals (no
+# flush-to-zero build option), so subnormal results, e.g. SiLU of a large
+# negative gate, are compared like any other value.
 
 
 def bits_of(t):
@@ -45,10 +45,9 @@ def assert_bf16_matches_exact(y_gpu, y_ref, what):
     bits_r, r = oracle.round_bf16(y_ref)
     bits_g = bits_of(y_gpu)
     diff = g != r
-    tiny = (np.abs(y_ref) < TINY) & (np.abs(g) < TINY)
     neighbours = np.abs(bits_g.astype(np.int64) - bits_r.astype(np.int64)) == 1
     near_mid = np.abs(y_ref - (g + r) / 2) <= MID_WINDOW * np.abs(y_ref)
-    bad = diff & ~tiny & ~(neighbours & near_mid)
+    bad = diff & ~(neighbours & near_mid)
     if bad.any():
         i = tuple(np.argwhere(bad)[0])
         raise AssertionError("%s: %d values off the exact producer's bf16 rounding; first at %s: "

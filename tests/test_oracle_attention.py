@@ -3,13 +3,18 @@
 Each check comes from something other than the oracle's own formulas: a
 single cached token (softmax of one score is 1), equal scores (the plain
 mean), a dominant score, a pure-Python loop with math.exp for the softmax
-and the weighted sum, page-permutation invariance of the block table, and
-grouped heads reading their own KV head.
+and the weighted sum, page-permutation invariance of the block table,
+grouped heads reading their own KV head, torch's
+scaled_dot_product_attention in float64 on the dequantized operands (the
+score scaling q_scale * k_scale * sm_scale and the default 1/sqrt(D)), and
+the two-token closed form (the logistic function of the score difference).
+Planted scaling mistakes must fail these pins.
 """
 
 import math
 
 import numpy as np
+import pytest
 import torch
 
 import oracle
@@ -113,3 +118,133 @@ def test_grouped_heads_read_their_kv_head():
     out = decode_attention_ref(q, kc, vc, table, bs, [9, 11], 0.05, 0.1, 0.25)
     assert np.all(out[:, 2:] == 0) and np.any(out[:, :2] != 0)
     assert np.all(decode_attention_ref(q, kc, vc, table, bs, [0, 0], 0.05, 0.1, 0.25) == 0)
+
+
+# --- score scaling: torch's scaled_dot_product_attention in float64 and the
+# two-token closed form ---
+
+def gather_dequantized(kc, vc, table, bs, n, b, hq, ks, vs):
+    """K and V of sequence b's first n tokens, read page by page with explicit
+    loops, dequantized (code value times the tensor scale) and expanded to
+    the Hq query heads (query head h reads KV head h // (Hq / Hkv))."""
+    hkv, d = kc.shape[1], kc.shape[3]
+    k = np.zeros((hkv, n, d))
+    v = np.zeros((hkv, n, d))
+    for t in range(n):
+        page, row = int(table[b][t // bs]), t % bs
+        for g in range(hkv):
+            k[g, t] = oracle.decode(kc[page, g, row]) * ks
+            v[g, t] = oracle.decode(vc[page, g, row]) * vs
+    rep = hq // hkv
+    return (torch.from_numpy(k).repeat_interleave(rep, dim=0), torch.from_numpy(v).repeat_interleave(rep, dim=0))
+
+
+def sdpa_reference(q_deq, kc, vc, table, bs, lens, ks, vs, sm_scale):
+    """torch SDPA (float64, CPU) per sequence on dequantized operands."""
+    b_, hq, d = q_deq.shape
+    out = np.zeros((b_, hq, d))
+    for b in range(b_):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        k, v = gather_dequantized(kc, vc, table, bs, n, b, hq, ks, vs)
+        q = torch.from_numpy(q_deq[b]).unsqueeze(1)                       # [Hq, 1, D]
+        kw = {} if sm_scale is None else {"scale": float(np.float32(sm_scale))}
+        out[b] = torch.nn.functional.scaled_dot_product_attention(q, k, v, **kw).squeeze(1).numpy()
+    return out
+
+
+def lossless_query(rng, b, hq, d, qs_pow2):
+    """A bf16 query whose per-tensor quantization is exact: each value is a
+    finite E4M3 value times a power-of-two scale, so q / q_scale is that E4M3
+    value and the dequantized query equals q itself."""
+    c = codes(rng, (b, hq, d))
+    vals = oracle.decode(c) * qs_pow2
+    return bf16(vals), vals
+
+
+@pytest.mark.parametrize("sm_scale", [None, 0.37, 2.0 ** -3])
+@pytest.mark.parametrize("hq,hkv", [(4, 2), (8, 1), (2, 2)])
+def test_matches_torch_sdpa_float64(sm_scale, hq, hkv):
+    rng = np.random.default_rng(40 + hq + hkv)
+    d, bs, pages = 16, 4, 40
+    b_ = 3
+    qs, ks, vs = 2.0 ** -7, 0.043, 0.29        # non-unit scales on every tensor
+    q, q_deq = lossless_query(rng, b_, hq, d, qs)
+    kc, vc = codes(rng, (pages, hkv, bs, d)), codes(rng, (pages, hkv, bs, d))
+    table = rng.permutation(pages)[: b_ * 9].reshape(b_, 9)
+    lens = [1, 17, 33]                          # ragged, partial last pages
+    out = decode_attention_ref(q, kc, vc, table, bs, lens, qs, ks, vs, sm_scale=sm_scale)
+    ref = sdpa_reference(q_deq, kc, vc, table, bs, lens, float(np.float32(ks)), float(np.float32(vs)), sm_scale)
+    assert np.allclose(out, ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+
+
+def test_matches_torch_sdpa_with_quantized_query():
+    """Any bf16 query: the oracle's scores use its per-tensor quantization of
+    Q (pinned in test_oracle_kv_cache.py); SDPA gets that dequantized Q."""
+    rng = np.random.default_rng(47)
+    b_, hq, hkv, d, bs, pages = 2, 4, 2, 32, 8, 12
+    q = bf16(rng.standard_normal((b_, hq, d)) * 3)
+    qs = float(np.float32(np.abs(oracle.bf16_values(q)).max() / 448))
+    ks, vs = 0.011, 0.7
+    kc, vc = codes(rng, (pages, hkv, bs, d)), codes(rng, (pages, hkv, bs, d))
+    table = rng.permutation(pages)[:10].reshape(b_, 5)
+    lens = [40, 9]
+    q_deq = oracle.decode(oracle.kv_quantize_ref(q, qs)).reshape(b_, hq, d) * qs
+    out = decode_attention_ref(q, kc, vc, table, bs, lens, qs, ks, vs)
+    ref = sdpa_reference(q_deq, kc, vc, table, bs, lens, float(np.float32(ks)), float(np.float32(vs)), None)
+    assert np.allclose(out, ref, rtol=1e-11, atol=1e-13 * np.abs(ref).max())
+
+
+def two_token_case(sm_scale, d=16):
+    """One query head over two cached tokens whose E4M3 dot products with the
+    query are 4 and 0 exactly: the query is 1.0 (code 0x38) times q_scale in
+    every dimension, the first key is 1.0 in four dimensions and 0 elsewhere,
+    the second key is 0."""
+    qs, ks, vs = 2.0 ** -4, 0.37, 1.5
+    q = bf16(np.full((1, 1, d), qs))
+    kc = np.zeros((1, 1, 2, d), np.uint8)
+    kc[0, 0, 0, :4] = 0x38
+    vc = np.zeros((1, 1, 2, d), np.uint8)
+    vc[0, 0, 0, :] = 0x40                       # 2.0
+    vc[0, 0, 1, :] = 0xB0                       # -0.5
+    out = decode_attention_ref(q, kc, vc, np.array([[0]]), 2, [2], qs, ks, vs, sm_scale=sm_scale)
+    sm = 1.0 / math.sqrt(d) if sm_scale is None else float(np.float32(sm_scale))
+    delta = 4.0 * qs * float(np.float32(ks)) * sm
+    w = 1.0 / (1.0 + math.exp(-delta))          # logistic weight of the first token
+    want = (w * 2.0 + (1.0 - w) * -0.5) * vs
+    return out[0, 0], want
+
+
+@pytest.mark.parametrize("sm_scale", [None, 0.7, 3.0])
+def test_two_token_closed_form(sm_scale):
+    got, want = two_token_case(sm_scale)
+    assert np.allclose(got, want, rtol=1e-14, atol=0)
+
+
+def test_scaling_mutations_are_caught(monkeypatch):
+    """Plant each plausible scaling mistake; a pin above must fail."""
+    import oracle.attention as oatt
+
+    def pins_hold():
+        ok = all(np.allclose(*two_token_case(s), rtol=1e-14, atol=0) for s in (None, 0.7))
+        try:
+            test_matches_torch_sdpa_float64(None, 4, 2)
+            test_matches_torch_sdpa_float64(0.37, 4, 2)
+        except AssertionError:
+            ok = False
+        return ok
+
+    assert pins_hold()
+    real_scores, real_sm = oatt.scores, oatt.softmax_scale
+    mutations = {
+        "k_scale dropped": ("scores", lambda dots, qs, ks, sm: real_scores(dots, qs, 1.0, sm)),
+        "q_scale dropped": ("scores", lambda dots, qs, ks, sm: real_scores(dots, 1.0, ks, sm)),
+        "sm_scale squared": ("scores", lambda dots, qs, ks, sm: real_scores(dots, qs, ks, sm * sm)),
+        "default 1/D": ("softmax_scale", lambda d, s: 1.0 / d if s is None else real_sm(d, s)),
+        "default 1": ("softmax_scale", lambda d, s: 1.0 if s is None else real_sm(d, s)),
+    }
+    for name, (attr, fn) in mutations.items():
+        with monkeypatch.context() as m:
+            m.setattr(oatt, attr, fn)
+            assert not pins_hold(), "planted mistake not caught: " + name
