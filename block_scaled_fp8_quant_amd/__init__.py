@@ -30,7 +30,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.s
 BLOCK = 128
 
 STATUS = {0: "FP8BLK_OK", 1: "FP8BLK_ERR_INVALID_ARG", 2: "FP8BLK_ERR_SHAPE",
-          3: "FP8BLK_ERR_ALIGNMENT", 4: "FP8BLK_ERR_HIP"}
+          3: "FP8BLK_ERR_ALIGNMENT", 4: "FP8BLK_ERR_HIP", 5: "FP8BLK_ERR_SCRATCH"}
+
+GEMM_SCRATCH_BYTES = 32 << 20   # FP8BLK_GEMM_SCRATCH_BYTES: static scratch of fp8blk_gemm_noalloc
 
 _lib = None
 
@@ -56,6 +58,7 @@ def load():
         "fp8blk_quant_weight": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_gemm": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8blk_gemm_ws": [vp, vp, vp, vp, i64, i64, i64, vp, vp, ctypes.c_size_t, vp],
+        "fp8blk_gemm_noalloc": [vp, vp, vp, vp, i64, i64, i64, vp, vp],
         "fp8blk_grouped_gemm": [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp],
         "fp8blk_rmsnorm_quant_act": [vp, vp, f32, i64, i64, vp, vp, vp, i32, vp],
         "fp8blk_silu_mul_quant_act": [vp, i64, i64, vp, vp, vp, i32, vp],
@@ -109,6 +112,10 @@ def fp8blk_gemm(qa, sa, qw, sw, M, N, K, y, stream):
 
 def fp8blk_gemm_ws(qa, sa, qw, sw, M, N, K, y, workspace, workspace_bytes, stream):
     return _call("fp8blk_gemm_ws", qa, sa, qw, sw, M, N, K, y, workspace, workspace_bytes, stream)
+
+
+def fp8blk_gemm_noalloc(qa, sa, qw, sw, M, N, K, y, stream):
+    return _call("fp8blk_gemm_noalloc", qa, sa, qw, sw, M, N, K, y, stream)
 
 
 def fp8blk_gemm_workspace_size(M, N, K):

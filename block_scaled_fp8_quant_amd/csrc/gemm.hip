@@ -37,6 +37,9 @@
 //   * workgroups are handed out round-robin over the 8 XCDs; the tile order
 //     gives each XCD a contiguous band of tiles so neighbours share A rows
 //     and B columns in that XCD's L2.
+#include <atomic>
+#include <mutex>
+
 #include "common.h"
 
 #ifndef FP8BLK_GEMM_GROUP_M
@@ -927,6 +930,62 @@ extern "C" size_t fp8blk_gemm_workspace_size(int64_t M, int64_t N, int64_t K) {
   return s ? (size_t)(s * M * N) * sizeof(float) : 0;
 }
 
+namespace fp8blk {
+namespace {
+
+// The split-K path: `splits` K ranges over 256x128 tiles write their fp32
+// sums to part[splits][M][N] (every element of each range's slice is
+// written, so part needs no clearing); a second kernel adds the ranges in
+// order and rounds to bf16.
+fp8blk_status launch_splitk(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw, int64_t M,
+                            int64_t N, int64_t K, uint16_t* y, float* part, int64_t splits, hipStream_t stream) {
+  const int64_t n_tiles = N / Skinny::BN;
+  hipLaunchKernelGGL(gemm_splitk_kernel<Skinny>, dim3((uint32_t)(n_tiles * splits)), dim3(Skinny::NT), 0, stream, qa,
+                     sa, qw, sw, M, N, K, part, (int)splits);
+  const fp8blk_status ls = launch_status();
+  if (ls != FP8BLK_OK) return ls;
+  const int64_t n4 = M * N / 4;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, stream,
+                     reinterpret_cast<const v4f*>(part), (int)splits, n4, reinterpret_cast<uint2*>(y));
+  return launch_status();
+}
+
+// Scratch of fp8blk_gemm_noalloc: the split-K partials in a static device
+// array, so the call allocates nothing. Each GPU the library runs on holds
+// its own copy until the process ends. Host code must not pass `scratch`
+// itself to a kernel (on the host the name stands for a host-side shadow,
+// not a device address): its device address is looked up once per device
+// and kept in scratch_ptr.
+static_assert(FP8BLK_GEMM_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) float scratch[FP8BLK_GEMM_SCRATCH_BYTES / sizeof(float)];
+
+constexpr int kMaxDevices = 256;
+std::atomic<float*> scratch_ptr[kMaxDevices];
+std::mutex scratch_mutex;
+
+// The device address of the current device's scratch array (hipGetSymbolAddress
+// with that device current, once per device; no allocation).
+fp8blk_status current_scratch(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FP8BLK_ERR_HIP;
+  float* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(scratch_mutex);
+    p = scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return FP8BLK_ERR_HIP;
+      p = static_cast<float*>(addr);
+      scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return FP8BLK_OK;
+}
+
+}  // namespace
+}  // namespace fp8blk
+
 // Few rows and few column tiles: the K loop is cut into splitk_count ranges
 // over 256x128 tiles, whose fp32 sums go to the workspace; a second kernel
 // adds them in range order and rounds to bf16. Otherwise fp8blk_gemm.
@@ -939,16 +998,23 @@ extern "C" fp8blk_status fp8blk_gemm_ws(const uint8_t* qa, const float* sa, cons
   if (!workspace || splits == 0) return fp8blk_gemm(qa, sa, qw, sw, M, N, K, y, stream);
   if (!aligned(workspace, 16)) return FP8BLK_ERR_ALIGNMENT;
   if (workspace_bytes < fp8blk_gemm_workspace_size(M, N, K)) return FP8BLK_ERR_INVALID_ARG;
-  float* part = static_cast<float*>(workspace);
-  const int64_t n_tiles = N / Skinny::BN;
-  hipLaunchKernelGGL(gemm_splitk_kernel<Skinny>, dim3((uint32_t)(n_tiles * splits)), dim3(Skinny::NT), 0, stream, qa,
-                     sa, qw, sw, M, N, K, part, (int)splits);
-  const fp8blk_status ls = launch_status();
-  if (ls != FP8BLK_OK) return ls;
-  const int64_t n4 = M * N / 4;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((uint32_t)((n4 + 255) / 256)), dim3(256), 0, stream,
-                     reinterpret_cast<const v4f*>(part), (int)splits, n4, reinterpret_cast<uint2*>(y));
-  return launch_status();
+  return launch_splitk(qa, sa, qw, sw, M, N, K, y, static_cast<float*>(workspace), splits, stream);
+}
+
+// fp8blk_gemm_ws with the library's static scratch as the workspace: the
+// same kernels, the same split count, so the same bits. The size check and
+// every argument check come before the first HIP call.
+extern "C" fp8blk_status fp8blk_gemm_noalloc(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
+                                             int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  const fp8blk_status st = check_gemm_args(qa, sa, qw, sw, M, N, K, y);
+  if (st != FP8BLK_OK || M == 0) return st;
+  const int64_t splits = splitk_count(M, N, K);
+  if (splits == 0) return fp8blk_gemm(qa, sa, qw, sw, M, N, K, y, stream);
+  if (fp8blk_gemm_workspace_size(M, N, K) > (size_t)FP8BLK_GEMM_SCRATCH_BYTES) return FP8BLK_ERR_SCRATCH;
+  float* part = nullptr;
+  const fp8blk_status ps = current_scratch(&part);
+  if (ps != FP8BLK_OK) return ps;
+  return launch_splitk(qa, sa, qw, sw, M, N, K, y, part, splits, stream);
 }
 
 // Expert groups: 256-row tiles when the average expert has at least 256

@@ -708,7 +708,8 @@ extern "C" const char* fp8blk_status_string(fp8blk_status status) {
     case FP8BLK_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or bad flag)";
     case FP8BLK_ERR_SHAPE: return "unsupported shape (K and N must be multiples of 128, GEMM K <= 2^24, E >= 1)";
     case FP8BLK_ERR_ALIGNMENT: return "misaligned pointer (data 16 bytes, scales 4 bytes)";
-    case FP8BLK_ERR_HIP: return "HIP kernel launch failed";
+    case FP8BLK_ERR_HIP: return "HIP kernel launch or device query failed";
+    case FP8BLK_ERR_SCRATCH: return "the call needs more device scratch than the library's static buffer holds";
   }
   return "unknown status";
 }

@@ -55,7 +55,8 @@ typedef enum {
   FP8BLK_ERR_INVALID_ARG = 1, /* null pointer, negative size, bad flag */
   FP8BLK_ERR_SHAPE = 2,       /* K or N not a multiple of 128, GEMM K > 2^24, E < 1 */
   FP8BLK_ERR_ALIGNMENT = 3,   /* data pointer not 16-byte aligned, scales not 4-byte */
-  FP8BLK_ERR_HIP = 4          /* a kernel launch failed */
+  FP8BLK_ERR_HIP = 4,         /* a kernel launch (or a device query) failed */
+  FP8BLK_ERR_SCRATCH = 5      /* the call needs more than the library's static scratch */
 } fp8blk_status;
 
 /* Number of elements of one activation group / weight block edge. */
@@ -128,9 +129,39 @@ fp8blk_status fp8blk_gemm_ws(const uint8_t* qa, const float* sa,
 /*
  * Workspace bytes fp8blk_gemm_ws uses for (M, N, K) (host only, no HIP
  * call): S * M * N * 4 when it splits K into S ranges, else 0 (also for
- * invalid shapes).
+ * invalid shapes). Never more than 256 rows x 32768 columns x 4 bytes
+ * (32 MiB): the split count times the column count is at most 256 column
+ * tiles of 128.
  */
 size_t fp8blk_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+
+/* Bytes of the static device scratch behind fp8blk_gemm_noalloc (32 MiB). */
+#define FP8BLK_GEMM_SCRATCH_BYTES (32u << 20)
+
+/*
+ * fp8blk_gemm_ws for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments as fp8blk_gemm (no workspace), same kernels, same split
+ * count and therefore the same bits as fp8blk_gemm_ws with a workspace; the
+ * split-K partials live in a static device array of
+ * FP8BLK_GEMM_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends. The call allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine. The first call on each device
+ * looks the array's device address up (hipGetSymbolAddress with that device
+ * current; make that first call outside graph capture) and keeps it.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's partials (each call writes every partial it reads, so nothing is
+ * cleared): calls on one device that overlap in time (unordered streams,
+ * several host threads) race and give undefined results; order them on one
+ * stream. Returns FP8BLK_ERR_SCRATCH (before any HIP call) if the split
+ * needs more than FP8BLK_GEMM_SCRATCH_BYTES, which the present split rule
+ * never does; FP8BLK_ERR_HIP if the address lookup fails.
+ */
+fp8blk_status fp8blk_gemm_noalloc(const uint8_t* qa, const float* sa,
+                                  const uint8_t* qw, const float* sw,
+                                  int64_t M, int64_t N, int64_t K,
+                                  uint16_t* y, hipStream_t stream);
 
 /*
  * Expert-grouped block-scaled GEMM for mixture-of-experts layers (upppp.jp,

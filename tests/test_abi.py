@@ -35,6 +35,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_gemm_ws", "fp8blk_gemm_workspace_size",
+        "fp8blk_gemm_noalloc",
         "fp8blk_grouped_gemm",
         "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_qkv_amax", "fp8blk_kv_scales",
         "fp8blk_kv_cache_write", "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
@@ -51,7 +52,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for st in range(5):
+    for st in range(6):
         assert lib.fp8blk_status_string(st)
     assert b"unknown" in lib.fp8blk_status_string(99)
 
@@ -345,3 +346,35 @@ def test_tensor_api_rejects_cpu_tensors():
     with pytest.raises(TypeError):
         fb.quant_act(torch.zeros(2, 128, dtype=torch.float32).cuda() if torch.cuda.is_available()
                      else torch.zeros(2, 128, dtype=torch.float32))
+
+
+def test_gemm_noalloc_validation(lib):
+    """The allocation-free GEMM checks its arguments like fp8blk_gemm, before
+    any HIP call (the device lookup of its scratch comes after)."""
+    f = lib.fp8blk_gemm_noalloc
+    assert f(P, P, P, P, -1, 128, 128, P, NULL) == INVALID
+    assert f(P, P, P, P, 4, 0, 128, P, NULL) == INVALID
+    assert f(P, P, P, P, 4, 100, 128, P, NULL) == SHAPE
+    assert f(P, P, P, P, 4, 128, 200, P, NULL) == SHAPE
+    assert f(NULL, P, P, P, 4, 128, 128, P, NULL) == INVALID
+    assert f(P, P, P, P, 4, 128, 128, NULL, NULL) == INVALID
+    assert f(P4, P, P, P, 4, 128, 128, P, NULL) == ALIGN
+    assert f(P, P + 2, P, P, 4, 128, 128, P, NULL) == ALIGN
+    assert f(NULL, NULL, NULL, NULL, 0, 128, 128, NULL, NULL) == OK     # M == 0 is a no-op
+
+
+def test_split_workspace_fits_the_static_scratch(lib):
+    """Every split the rule can choose fits FP8BLK_GEMM_SCRATCH_BYTES, so the
+    allocation-free GEMM never has to reject a valid shape; the header's
+    constant and the binding's agree."""
+    src = open(HEADER).read()
+    m = re.search(r"#define FP8BLK_GEMM_SCRATCH_BYTES \((\d+)u << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == fb.GEMM_SCRATCH_BYTES
+    size = lib.fp8blk_gemm_workspace_size
+    worst = 0
+    for mm in (1, 2, 64, 100, 128, 200, 255, 256, 257):
+        for n in range(128, 40000, 128 * 7):
+            for k in (4096, 8192, 8320, 12288, 14336, 28672, 1 << 20):
+                worst = max(worst, size(mm, n, k))
+    assert 0 < worst <= fb.GEMM_SCRATCH_BYTES
+    assert size(256, 4096, 14336) == fb.GEMM_SCRATCH_BYTES    # the decode down projection: the largest
