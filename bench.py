@@ -10,7 +10,14 @@ the measured step time (quantisation included), in TFLOP/s. ``roofline``
 covers the dominant kernel (the GEMM) with its average launch duration
 measured by HIP events on the launch stream inside the timed region.
 ``cpu_baseline`` times the CPU oracle on a bounded sample of the same
-workload. ``producers`` (after the timed region) times the two fused
+workload and checks the timed GPU outputs on those rows against it
+(``cpu_baseline.check``: codes and scales bit for bit, GEMM outputs within
+the tolerance). ``breakdown`` adds the median/p10/p90 of the per-step and
+per-GEMM event times, ``clocks`` the SCLK/MCLK seen during the timed region.
+``workloads`` gives the other workloads' lines (Llama-3.1-8B decode M = 256,
+Qwen3-8B with power-of-two scales M = 4096, Qwen3-30B-A3B MoE): GEMM times in
+the step and with the weights cold in HBM (a 1 GiB write before each
+launch), each linear against its roofline, and the quantisers' GB/s. ``producers`` (after the timed region) times the two fused
 producer kernels at the workload's shapes -- RMSNorm -> 1x128 quantisation
 of the qkv / gate_up input and SiLU(gate)*up -> quantisation of the down
 input -- each against the HBM roofline; ``kv_cache`` does the same for the
@@ -66,6 +73,11 @@ def parse():
     p.add_argument("--no-kv", action="store_true", help="skip timing the FP8 KV-cache path")
     p.add_argument("--no-backward", action="store_true", help="skip timing the backward GEMMs")
     p.add_argument("--no-attention", action="store_true", help="skip timing the FP8 decode attention")
+    p.add_argument("--no-workloads", action="store_true",
+                   help="skip the other workloads' GEMM and quantisation lines (``workloads``)")
+    p.add_argument("--workload-steps", type=int, default=10, help="timed steps per other workload")
+    p.add_argument("--cold-reps", type=int, default=7,
+                   help="GEMM launches per linear timed after a 1 GiB write (weights cold in HBM)")
     p.add_argument("--backward-reps", type=int, default=3)
     p.add_argument("--producer-reps", type=int, default=20)
     p.add_argument("--cpu-sample-rows", type=int, default=8192)
@@ -136,11 +148,15 @@ def build_layers(workload, dev):
     return layers
 
 
-def step(fb, layers, events=None):
+def step(fb, layers, events=None, whole_step=False):
     """One pass of the path. With ``events``, brackets every kernel launch
-    with HIP events on the launch stream: events[kind] gets (start, end)."""
+    with HIP events on the launch stream: events[kind] gets (start, end);
+    with ``whole_step`` also the whole pass (events["step"])."""
     import torch
     stream = torch.cuda.current_stream()
+    if events is not None and whole_step:
+        s0 = torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
 
     def timed(kind, fn):
         if events is None:
@@ -157,10 +173,117 @@ def step(fb, layers, events=None):
         timed("quant_weight", lambda: fb.quant_weight(L["w"], L["pow2"], q=L["qw"], s=L["sw"]))
     for L in layers:
         timed("quant_act", lambda: fb.quant_act(L["x"], L["pow2"], q=L["qa"], s=L["sa"]))
-        if L["e"]:
-            timed("gemm", lambda: fb.grouped_gemm(L["qa"], L["sa"], L["qw"], L["sw"], L["off"], y=L["y"]))
-        else:
-            timed("gemm", lambda: fb.gemm(L["qa"], L["sa"], L["qw"], L["sw"], y=L["y"], workspace=L["ws"]))
+        timed("gemm", lambda: run_gemm(fb, L))
+    if events is not None and whole_step:
+        s1 = torch.cuda.Event(enable_timing=True)
+        s1.record(stream)
+        events.setdefault("step", []).append((s0, s1))
+
+
+def run_gemm(fb, L):
+    """The layer's GEMM on its quantised operands (grouped for the MoE
+    layers; split-K over the preallocated workspace where the rule splits)."""
+    if L["e"]:
+        fb.grouped_gemm(L["qa"], L["sa"], L["qw"], L["sw"], L["off"], y=L["y"])
+    else:
+        fb.gemm(L["qa"], L["sa"], L["qw"], L["sw"], y=L["y"], workspace=L["ws"])
+
+
+def percentiles(vals):
+    """Median, 10th and 90th percentile of a list of times."""
+    import numpy as np
+    a = np.asarray(vals, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 4), "p10": round(float(np.percentile(a, 10)), 4),
+            "p90": round(float(np.percentile(a, 90)), 4), "n": int(a.size)}
+
+
+class ClockSampler:
+    """The GPU's shader (SCLK) and memory (MCLK) clocks while the timed
+    region runs: the current level of the amdgpu driver's DPM tables
+    (sysfs pp_dpm_sclk / pp_dpm_mclk, the line marked '*'), read every 10 ms
+    by a background thread (a file read, no GPU call), plus the table's
+    levels. Where sysfs is not readable, one ``amd-smi metric --clock``
+    reading after the region."""
+
+    def __init__(self):
+        import glob
+        self.files = {}
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            sc, mc = os.path.join(dev, "pp_dpm_sclk"), os.path.join(dev, "pp_dpm_mclk")
+            if os.access(sc, os.R_OK) and os.access(mc, os.R_OK):
+                self.files = {"sclk_mhz": sc, "mclk_mhz": mc}
+                break
+        self.samples = {"sclk_mhz": [], "mclk_mhz": []}
+        self._stop = None
+        self._thread = None
+
+    @staticmethod
+    def _current(path):
+        import re
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*[mM][hH]z", line)
+                        if m:
+                            return int(m.group(1))
+        except OSError:
+            return None
+        return None
+
+    @staticmethod
+    def _levels(path):
+        import re
+        try:
+            with open(path) as f:
+                return [int(m.group(1)) for m in re.finditer(r"(\d+)\s*[mM][hH]z", f.read())]
+        except OSError:
+            return []
+
+    def _run(self):
+        while not self._stop.is_set():
+            for key, path in self.files.items():
+                v = self._current(path)
+                if v is not None:
+                    self.samples[key].append(v)
+            self._stop.wait(0.01)
+
+    def start(self):
+        import threading
+        if not self.files:
+            return
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        out = {}
+        for key, vals in self.samples.items():
+            if vals:
+                out[key] = {"median": sorted(vals)[len(vals) // 2], "min": min(vals), "max": max(vals),
+                            "samples": len(vals)}
+        if out:
+            for key, path in self.files.items():
+                out[key]["levels"] = self._levels(path)
+            out["source"] = "sysfs pp_dpm_sclk/pp_dpm_mclk, 10 ms samples over the timed region"
+            return out
+        return amd_smi_clocks()
+
+
+def amd_smi_clocks():
+    """One reading of amd-smi's clock metrics (text, trimmed), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock"], capture_output=True, text=True, timeout=20)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    if r.returncode != 0:
+        return None
+    lines = [ln.strip() for ln in r.stdout.splitlines() if ln.strip()]
+    return {"source": "amd-smi metric --clock after the timed region", "text": " | ".join(lines)[:1500]}
 
 
 RMS_EPS = 1e-5
@@ -450,6 +573,122 @@ def time_backward_moe(fb, dev, reps):
     return out
 
 
+def gemm_alg_bytes(L):
+    """Algorithmic bytes of one GEMM launch: each operand once (codes, scales),
+    the bf16 output written."""
+    e = max(L["e"], 1)
+    return (L["m"] * L["k"] + L["n"] * L["k"] * e + 4 * L["m"] * L["k"] // 128 + 4 * L["n"] * L["k"] * e // 16384
+            + 2 * L["m"] * L["n"])
+
+
+def time_workload(fb, workload, dev, steps, warmup, cold_reps, traffic_db):
+    """One of the other workloads at its own shapes: ``steps`` eager passes of
+    the path (quant_weight, quant_act, GEMM per linear; HIP events around each
+    launch), then each GEMM timed alone ``cold_reps`` times right after a
+    1 GiB write (the 256 MB last-level cache then holds none of its weights:
+    a decode step's or an MoE layer's weights are read once per step from
+    HBM). Below the ridge (decode, MoE) the roofline entry is the cold GEMM
+    against the HBM peak; above it (Qwen3-8B, M = 4096) the in-step GEMM
+    against the FP8 peak. Medians over the launches."""
+    import torch
+    stream = torch.cuda.current_stream()
+    layers = build_layers(workload, dev)
+    for _ in range(warmup):
+        step(fb, layers)
+    torch.cuda.synchronize()
+    events = {}
+    for _ in range(steps):
+        step(fb, layers, events)
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    cold = {L["name"]: [] for L in layers}
+    for _ in range(cold_reps):
+        for L in layers:
+            flush.zero_()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            run_gemm(fb, L)
+            b.record(stream)
+            cold[L["name"]].append((a, b))
+    torch.cuda.synchronize()
+    nl = len(layers)
+    ms = {k: [a.elapsed_time(b) for a, b in v] for k, v in events.items()}
+    flops = sum(L["flops"] for L in layers)
+    alg = sum(gemm_alg_bytes(L) for L in layers)
+    per_layer = {}
+    hot_total = cold_total = 0.0
+    for i, L in enumerate(layers):
+        hot = percentiles(ms["gemm"][i::nl])
+        cl = percentiles([a.elapsed_time(b) for a, b in cold[L["name"]]])
+        hot_total += hot["median"]
+        cold_total += cl["median"]
+        ab = gemm_alg_bytes(L)
+        roof_us = max(L["flops"] / (FP8_PEAK_TFLOPS * 1e12), ab / (HBM_PEAK_GBS * 1e9)) * 1e6
+        per_layer[L["name"]] = {"shape_mnk": [L["m"], L["n"], L["k"]] + ([L["e"]] if L["e"] else []),
+                                "gemm_us": round(hot["median"] * 1e3, 1),
+                                "gemm_us_p10_p90": [round(hot["p10"] * 1e3, 1), round(hot["p90"] * 1e3, 1)],
+                                "gemm_cold_us": round(cl["median"] * 1e3, 1),
+                                "gemm_cold_us_p10_p90": [round(cl["p10"] * 1e3, 1), round(cl["p90"] * 1e3, 1)],
+                                "roofline_us": round(roof_us, 2),
+                                "frac_of_roofline_cold": round(roof_us / (cl["median"] * 1e3), 4)}
+    ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    hbm_bound = flops / alg < ridge
+    avg_ms = (cold_total if hbm_bound else hot_total) / nl
+    rec = (traffic_db or {}).get(workload) or {}
+    kern = "grouped_gemm_kernel" if workload == "moe" else "gemm_kernel"
+    krec = rec.get("kernels", {}).get(kern, {})
+    traffic = krec.get("bytes_per_launch") if krec.get("source_hash") == source_hash("gemm_kernel") else None
+    kb = kernel_bytes(layers)
+    qa_ms = sum(ms["quant_act"]) / steps
+    qw_ms = sum(ms["quant_weight"]) / steps
+    out = {
+        "config": {"workload": workload, "m": layers[0]["m"],
+                   "linears": [[L["name"], L["k"], L["n"]] + ([L["e"]] if L["e"] else []) for L in layers],
+                   "pow2": layers[0]["pow2"]},
+        "gemm_tflops_in_step": round(flops / (hot_total * 1e-3) / 1e12, 1),
+        "gemm_tflops_cold": round(flops / (cold_total * 1e-3) / 1e12, 1),
+        "roofline": roofline(flops / nl, alg / nl, avg_ms, traffic),
+        "timing": "cold (1 GiB written before each launch)" if hbm_bound else "in step (eager)",
+        "per_layer": per_layer,
+        "quant_act": {"gbs": round(kb["quant_act"] / (qa_ms * 1e-3) / 1e9, 1),
+                      "frac": round(kb["quant_act"] / (qa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                      "ms_per_step": round(qa_ms, 4)},
+        "quant_weight": {"gbs": round(kb["quant_weight"] / (qw_ms * 1e-3) / 1e9, 1),
+                         "frac": round(kb["quant_weight"] / (qw_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "ms_per_step": round(qw_ms, 4)},
+        "layer_rate_tflops": round(flops / ((hot_total + qa_ms) * 1e-3) / 1e12, 1),
+    }
+    for L in layers:
+        L.clear()
+    del layers, flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def snapshot_sample(layers, workload, rows, wrows):
+    """Host copies of the timed outputs on the rows the CPU baseline samples
+    (the first ``rows`` activation rows and ``wrows`` weight rows of each
+    linear; for the MoE layers, rows of the largest expert and its weights)."""
+    out = []
+    for L in layers:
+        if L["e"]:
+            offs = L["off"].cpu().numpy()
+            import numpy as np
+            e = int(np.argmax(np.diff(offs)))
+            lo, hi = int(offs[e]), int(offs[e + 1])
+            r0, r1 = lo, min(lo + rows, L["m"])
+            qw, sw = L["qw"][e], L["sw"][e]
+            yrows = min(r1, hi) - r0
+        else:
+            r0, r1 = 0, min(rows, L["m"])
+            qw, sw = L["qw"], L["sw"]
+            yrows = r1 - r0
+        out.append({"qa": L["qa"][r0:r1].cpu().numpy(), "sa": L["sa"][r0:r1].cpu().numpy(),
+                    "qw": qw[:wrows].cpu().numpy(), "sw": sw[:wrows // 128].cpu().numpy(),
+                    "y": L["y"][r0:r0 + yrows, :wrows].float().cpu().numpy(), "yrows": yrows})
+    return out
+
+
 def kernel_bytes(layers):
     """Algorithmic HBM bytes per launch kind, summed over one step."""
     qa = sum(2 * L["m"] * L["k"] + L["m"] * L["k"] + 4 * L["m"] * L["k"] // 128 for L in layers)
@@ -458,12 +697,15 @@ def kernel_bytes(layers):
     return {"quant_act": qa, "quant_weight": qw}
 
 
-def cpu_baseline(workload, rows, wrows):
+def cpu_baseline(workload, rows, wrows, gpu_sample=None):
     """The oracle (untuned) on a bounded sample: for each linear, ``rows``
-    activation rows and two 128-row weight blocks are quantised and
-    multiplied. Inputs are drawn first (untimed, like the GPU's resident
-    inputs); the timed part is oracle work only. Scaled to TFLOP/s of GEMM
-    work like the GPU value."""
+    activation rows and ``wrows`` weight rows are quantised and multiplied.
+    Inputs are drawn first (untimed, like the GPU's resident inputs); the
+    timed part is oracle work only. Scaled to TFLOP/s of GEMM work like the
+    GPU value. With ``gpu_sample`` (the timed GPU outputs on the same rows,
+    snapshot_sample), the oracle's results also check them: codes and scales
+    bit for bit, the GEMM outputs within |y - y_ref| <= 2^-7 |y_ref| +
+    1e-3 rms(y_ref)."""
     import numpy as np
     import oracle
     import synth
@@ -488,15 +730,40 @@ def cpu_baseline(workload, rows, wrows):
         desc = ("first %d activation rows x first %d weight rows of each of the %d linears: "
                 "oracle quantisation (numpy) + block-wise fp64 GEMM" % (rows, wrows, len(wl.linears)))
     flops = 0.0
+    results = []
     t0 = time.perf_counter()
     for xs, ws, pow2 in cases:
         qa, sa = oracle.quant_act_ref(xs, pow2)
         qw, sw = oracle.quant_weight_ref(ws, pow2)
-        oracle.gemm_ref(qa, sa, qw, sw)
+        y = oracle.gemm_ref(qa, sa, qw, sw)
         flops += 2.0 * xs.shape[0] * ws.shape[0] * xs.shape[1]
+        results.append((qa, sa, qw, sw, y))
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": desc, "seconds": round(dt, 2)}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": desc, "seconds": round(dt, 2)}
+    if gpu_sample is not None:
+        out["check"] = check_sample(results, gpu_sample)
+    return out
+
+
+def check_sample(results, gpu_sample):
+    """Compare the timed GPU outputs with the oracle's on the sampled rows."""
+    import numpy as np
+    import oracle
+    codes_bad = scales_bad = 0
+    worst = 0.0
+    ok = True
+    for (qa, sa, qw, sw, y), g in zip(results, gpu_sample):
+        codes_bad += int(np.count_nonzero(g["qa"] != qa) + np.count_nonzero(g["qw"] != qw))
+        scales_bad += int(np.count_nonzero(g["sa"].view(np.uint32) != sa.view(np.uint32))
+                          + np.count_nonzero(g["sw"].view(np.uint32) != sw.view(np.uint32)))
+        if g["yrows"] > 0:
+            good, w = oracle.tolerance_ok(g["y"].astype(np.float64), y[:g["yrows"]])
+            ok = ok and good
+            worst = max(worst, float(w))
+    return {"codes_mismatched": codes_bad, "scales_mismatched": scales_bad, "gemm_within_tolerance": bool(ok),
+            "gemm_worst_ratio": round(worst, 4),
+            "ok": bool(ok and codes_bad == 0 and scales_bad == 0)}
 
 
 COPY_BYTES = 1 << 30
@@ -626,12 +893,15 @@ def main():
     torch.cuda.synchronize()
 
     events = {}
+    clocks = ClockSampler()
     torch.cuda.synchronize()
+    clocks.start()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(fb, layers, events)
+        step(fb, layers, events, whole_step=True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    clock_rec = clocks.stop()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
     if args.copy_yardstick:
@@ -651,9 +921,7 @@ def main():
             traffic_rec = {k: v for k, v in rec.get("kernels", {}).items()
                            if v.get("source_hash") == source_hash(k)}
     kb = kernel_bytes(layers)
-    gemm_alg_bytes = sum(L["m"] * L["k"] + L["n"] * L["k"] * max(L["e"], 1) + 4 * L["m"] * L["k"] // 128
-                         + 4 * L["n"] * L["k"] * max(L["e"], 1) // 16384 + 2 * L["m"] * L["n"]
-                         for L in layers) / len(layers)
+    alg_bytes_launch = sum(gemm_alg_bytes(L) for L in layers) / len(layers)
     breakdown = {
         "gemm_ms_per_step": round(gemm_ms, 4),
         "gemm_tflops": round(flops_step / (gemm_ms * 1e-3) / 1e12, 1),
@@ -664,6 +932,11 @@ def main():
         "per_layer_gemm_us": {L["name"]: round(sum(per_kind["gemm"][i::len(layers)]) / args.steps * 1e3, 1)
                               for i, L in enumerate(layers)},
     }
+    step_ms = percentiles(per_kind["step"])
+    gemm_pct = {L["name"]: percentiles(per_kind["gemm"][i::len(layers)]) for i, L in enumerate(layers)}
+    breakdown["step_ms_events"] = step_ms
+    breakdown["per_layer_gemm_us_p10_p90"] = {k: [round(v["p10"] * 1e3, 1), round(v["p90"] * 1e3, 1)]
+                                               for k, v in gemm_pct.items()}
     value = flops_step / (ms_step * 1e-3) / 1e12
     out = {
         "metric": METRIC,
@@ -685,14 +958,29 @@ def main():
                    "step": "quant_weight x%d + quant_act x%d + %s x%d" % (
                        len(layers), len(layers), "grouped_gemm" if layers[0]["e"] else "gemm", len(layers))},
         "pct_fp8_peak": round(100 * value / FP8_PEAK_TFLOPS, 2),
-        "roofline": roofline(gemm_flops_launch, gemm_alg_bytes, gemm_avg_ms, traffic),
+        "roofline": roofline(gemm_flops_launch, alg_bytes_launch, gemm_avg_ms, traffic),
         "breakdown": breakdown,
+        "clocks": clock_rec,
     }
+    sample = None if args.no_cpu_baseline else snapshot_sample(layers, args.workload, args.cpu_sample_rows,
+                                                               args.cpu_sample_wrows)
+    for L in layers:                          # free the step's buffers
+        L.clear()
+    torch.cuda.empty_cache()
+    if not args.no_workloads:
+        traffic_db = {}
+        if os.path.exists(TRAFFIC_FILE):
+            with open(TRAFFIC_FILE) as f:
+                traffic_db = json.load(f)
+        out["workloads"] = {}
+        for name in ("llama8b_decode", "qwen8b_pow2", "moe"):
+            if name == args.workload:
+                continue
+            print("bench: workload %s" % name, file=sys.stderr, flush=True)
+            out["workloads"][name] = time_workload(fb, name, dev, args.workload_steps, 3, args.cold_reps,
+                                                   traffic_db)
     if not args.no_producers:
         print("bench: timing the fused producers", file=sys.stderr, flush=True)
-        for L in layers:                      # free the step's buffers first
-            L.clear()
-        torch.cuda.empty_cache()
         out["producers"] = time_producers(fb, build_producers(args.workload, dev), args.producer_reps)
         for name, key in (("rmsnorm_quant_act", "rmsnorm_quant_act_rows_kernel"),
                           ("silu_mul_quant_act", "silu_mul_quant_act_kernel")):
@@ -728,7 +1016,10 @@ def main():
             entry["traffic"] = None if t is None else round(t)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows, sample)
+        if not out["cpu_baseline"]["check"]["ok"]:
+            print("bench: the timed outputs DIFFER from the oracle on the sample: %s"
+                  % out["cpu_baseline"]["check"], file=sys.stderr, flush=True)
     print(json.dumps(out), flush=True)
 
 

@@ -1,6 +1,9 @@
 """Helpers for the GPU parity tests: guarded output buffers and sampled
 full-size comparisons against the oracle."""
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
 
@@ -94,3 +97,15 @@ def check_linear_sampled(x, w, pow2, dev, gen, rows=24, wblocks=2):
     y_ref = oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r)
     y_s = y[torch.from_numpy(r).to(dev)][:, torch.from_numpy(wrows).to(dev)].float().cpu().numpy()
     return assert_within_tolerance(y_s, y_ref, what="sampled gemm")
+
+
+def oracle_quant_whole(t, pow2, weight=False, rows_per_job=1024):
+    """The oracle's quantisation of a whole [rows, K] bf16 tensor, its row
+    chunks (whole 128-row blocks for weights) run on a thread pool: numpy
+    releases the interpreter lock in the heavy steps, and threads need no
+    new process next to the one holding the GPU."""
+    f = oracle.quant_weight_ref if weight else oracle.quant_act_ref
+    chunks = [t[i:i + rows_per_job] for i in range(0, t.shape[0], rows_per_job)]
+    with ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        res = list(ex.map(lambda c: f(c, pow2), chunks))
+    return np.concatenate([r[0] for r in res]), np.concatenate([r[1] for r in res])

@@ -8,7 +8,7 @@ import torch
 import oracle
 import synth
 from tests.gpu_util import (
-    assert_codes_equal, assert_scales_equal, check_linear_sampled, guarded, quant_act_guarded,
+    assert_codes_equal, assert_scales_equal, check_linear_sampled, guarded, oracle_quant_whole, quant_act_guarded,
 )
 
 pytestmark = pytest.mark.gpu
@@ -182,4 +182,27 @@ def test_full_size_sampled(fp8blk_lib, workload):
         x, w = synth.linear_inputs(workload, li)
         check_linear_sampled(x, w, wl.pow2, DEV, gen)
         del x, w
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("workload", ["llama8b_prefill", "qwen8b_pow2"])
+def test_full_size_whole_tensors(fp8blk_lib, workload):
+    """Every linear of the workload at full size, every activation and weight
+    code and scale compared with the oracle bit for bit (not sampled)."""
+    import block_scaled_fp8_quant_amd as fb
+    wl = synth.WORKLOADS[workload]
+    for li, (name, k, n) in enumerate(wl.linears):
+        print("whole-tensor %s %s M=%d K=%d N=%d" % (workload, name, wl.m, k, n), flush=True)
+        x, w = synth.linear_inputs(workload, li)
+        qa, sa = fb.quant_act(x.to(DEV), wl.pow2)
+        qw, sw = fb.quant_weight(w.to(DEV), wl.pow2)
+        torch.cuda.synchronize()
+        qa_r, sa_r = oracle_quant_whole(x, wl.pow2)
+        assert_codes_equal(qa.cpu().numpy(), qa_r, "%s activation codes" % name)
+        assert_scales_equal(sa.cpu().numpy(), sa_r, "%s activation scales" % name)
+        del qa_r, sa_r
+        qw_r, sw_r = oracle_quant_whole(w, wl.pow2, weight=True)
+        assert_codes_equal(qw.cpu().numpy(), qw_r, "%s weight codes" % name)
+        assert_scales_equal(sw.cpu().numpy(), sw_r, "%s weight scales" % name)
+        del x, w, qa, sa, qw, sw, qw_r, sw_r
         torch.cuda.empty_cache()
