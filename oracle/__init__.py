@@ -32,7 +32,8 @@ What it computes (sources are web pages about NVIDIA NeMo RL's FP8 recipe):
   the same quantization rule along each GEMM's contraction dimension.
 * Both pages (upppp.jp «KVキャッシュとAttentionにも拡張», greentreeone.com
   «Реальные прирост производительности»): attention in FP8 over the FP8 KV
-  cache; ``attention`` holds the decode step's attention over the paged cache.
+  cache; ``attention`` holds the decode step's attention over the paged cache
+  and the prefill step's (a prompt's new tokens, causally).
 
 The pages give no scale formula, no E4M3 variant, no rounding mode and no
 accumulation scheme. The readings taken where they are silent are written
@@ -84,7 +85,7 @@ from .backward import (
     grouped_dgrad_ref,
     grouped_wgrad_ref,
 )
-from .attention import decode_attention_ref
+from .attention import decode_attention_ref, prefill_attention_ref
 from .gemm import (
     dequant_act,
     dequant_weight,
@@ -106,4 +107,5 @@ __all__ = [
     "quant_act_t_ref", "quant_weight_t_ref", "gemm_rowscaled_ref", "dgrad_ref", "wgrad_ref",
     "padded_offsets", "quant_act_t_grouped_ref", "grouped_dgrad_ref", "grouped_wgrad_ref",
     "decode_attention_ref",
+    "prefill_attention_ref",
 ]
