@@ -26,7 +26,9 @@ into the cache) at the workload's attention shapes; ``backward`` times the
 dgrad and wgrad GEMMs of every linear (and their transposing quantizers)
 against the same rooflines; ``attention`` times the FP8 decode attention over
 the paged FP8 KV cache at the workload's heads for four context mixes,
-against the HBM roofline (one call: the split path's two kernels together).
+against the HBM roofline (one call: the split path's two kernels together);
+``prefill_attention`` the FP8 prefill attention (8 prompts of 2048 tokens,
+causal) against the matrix-core roofline.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
@@ -473,6 +475,47 @@ def time_attention(fb, workload, dev, reps):
         del A
         torch.cuda.empty_cache()
     return out
+
+
+FP16_PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA
+
+
+def time_prefill_attention(fb, workload, dev, reps):
+    """FP8 prefill attention at the workload's heads: 8 fresh prompts of 2048
+    tokens (each new token attends causally over its prompt in the paged FP8
+    cache; random finite E4M3 codes, the kernel's speed does not depend on
+    them). Timed from HIP-graph replays. Algorithmic work: the causal QK^T
+    and PV products, 2 * D * Hq multiply-adds per (query, attended token)
+    each; roofline: QK^T on the FP8 matrix cores (5.0 PFLOP/s) and PV, whose
+    probabilities stay unquantized, at the 16-bit rate (2.5 PFLOP/s)."""
+    import torch
+    import synth
+    hq, hkv, d = synth.ATTENTION[workload]
+    nseq, n = 8, 2048
+    g = synth.generator(0x7A)
+    pages = nseq * n // ATTN_BLOCK
+    perm = torch.randperm(pages, generator=g).to(torch.int32)
+    table = perm.reshape(nseq, n // ATTN_BLOCK).to(dev)
+    kc = synth.random_cache_codes((pages, hkv, ATTN_BLOCK, d), 21, dev)
+    vc = synth.random_cache_codes((pages, hkv, ATTN_BLOCK, d), 22, dev)
+    q = torch.randn(nseq * n, hq, d, generator=g).to(torch.bfloat16).to(dev)
+    cu = torch.arange(0, nseq * n + 1, n, dtype=torch.int32).to(dev)
+    lens = torch.full((nseq,), n, dtype=torch.int32).to(dev)
+    sc = torch.tensor([4.0 / 448, 0.004, 0.01], dtype=torch.float32, device=dev)
+    out = torch.empty_like(q)
+    ms = graph_time_ms(lambda: fb.prefill_attention(q, cu, n, kc, vc, table, ATTN_BLOCK, lens, sc[0:1], sc[1:2],
+                                                     sc[2:3], out=out), reps)
+    pairs = nseq * n * (n + 1) // 2                  # (query, attended token) pairs
+    f_qk = f_pv = 2.0 * pairs * d * hq
+    t_roof = f_qk / (FP8_PEAK_TFLOPS * 1e12) + f_pv / (FP16_PEAK_TFLOPS * 1e12)
+    achieved = (f_qk + f_pv) / (ms * 1e-3) / 1e12
+    peak = (f_qk + f_pv) / t_roof / 1e12
+    del q, kc, vc, out
+    torch.cuda.empty_cache()
+    return {"input_shape": [nseq, n, hq, hkv, d], "avg_launch_us": round(ms * 1e3, 2), "bound": "mfma",
+            "achieved": round(achieved, 1), "peak": round(peak, 1), "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None, "flops_per_launch": f_qk + f_pv,
+            "peak_note": "QK^T at the FP8 and PV at the fp16 dense MFMA peak, weighted by their FLOPs"}
 
 
 def time_backward(fb, workload, dev, reps):
@@ -1014,6 +1057,10 @@ def main():
             # the three direct-path mixes move the same algorithmic bytes within 0.4%
             t = (part + merge if part is not None and merge is not None else None) if entry["split"] else direct
             entry["traffic"] = None if t is None else round(t)
+    if not args.no_attention:
+        print("bench: timing the FP8 prefill attention", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+        out["prefill_attention"] = time_prefill_attention(fb, args.workload, dev, 5)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows, sample)

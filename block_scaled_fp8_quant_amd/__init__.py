@@ -66,6 +66,8 @@ def load():
         "fp8blk_quant_act_t": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_decode_attention": [vp, i64, i64, i64, i64, i64, vp, vp, i64, vp, i64, i64, vp, vp, vp, vp, f32,
                                     vp, i64, i64, vp, ctypes.c_size_t, vp],
+        "fp8blk_prefill_attention": [vp, i64, i64, i64, i64, i64, i64, vp, i64, vp, vp, i64, vp, i64, i64, vp, vp,
+                                     vp, vp, f32, vp, i64, vp],
         "fp8blk_quant_weight_t": [vp, i64, i64, vp, vp, i32, vp],
         "fp8blk_quant_weight_t_grouped": [vp, i64, i64, i64, vp, vp, i32, vp],
         "fp8blk_quant_act_t_grouped": [vp, i64, i64, vp, i64, i64, vp, vp, i32, vp],
@@ -140,6 +142,14 @@ def fp8blk_decode_attention(q, ldq, B, Hq, Hkv, D, k_cache, v_cache, num_slots, 
     return _call("fp8blk_decode_attention", q, ldq, B, Hq, Hkv, D, k_cache, v_cache, num_slots, block_table,
                  max_blocks, block_size, context_lens, q_scale, k_scale, v_scale, sm_scale, out, ldo, split_tokens,
                  workspace, workspace_bytes, stream)
+
+
+def fp8blk_prefill_attention(q, ldq, total_q, B, Hq, Hkv, D, cu_seqlens_q, max_seqlen_q, k_cache, v_cache,
+                             num_slots, block_table, max_blocks, block_size, context_lens, q_scale, k_scale, v_scale,
+                             sm_scale, out, ldo, stream):
+    return _call("fp8blk_prefill_attention", q, ldq, total_q, B, Hq, Hkv, D, cu_seqlens_q, max_seqlen_q, k_cache,
+                 v_cache, num_slots, block_table, max_blocks, block_size, context_lens, q_scale, k_scale, v_scale,
+                 sm_scale, out, ldo, stream)
 
 
 def fp8blk_decode_attention_workspace_size(B, Hq, Hkv, D, max_blocks, block_size, split_tokens):
@@ -567,6 +577,51 @@ def decode_attention(q, k_cache, v_cache, block_table, block_size, context_lens,
                             block_table.data_ptr(), block_table.shape[1], block_size, context_lens.data_ptr(),
                             q_scale.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), sm, out.data_ptr(), hq * d,
                             split_tokens, ws_ptr, ws_bytes, _stream(dev))
+    return out
+
+
+def prefill_attention(q, cu_seqlens_q, max_seqlen_q, k_cache, v_cache, block_table, block_size, context_lens,
+                      q_scale, k_scale, v_scale, sm_scale=None, out=None):
+    """FP8 prefill attention: q [total_q, Hq, D] bf16 (or [total_q, Hq*D]
+    rows with a row stride, e.g. a view into a qkv output) holding the new
+    tokens of every sequence, sequence b's rows cu_seqlens_q[b] ..
+    cu_seqlens_q[b+1]-1 (int32 [B+1] on the device); new token i of
+    sequence b attends causally to cached tokens 0 .. context_lens[b] - n_b
+    + i of the head-major paged caches [num_blocks, Hkv, block_size, D].
+    max_seqlen_q: a host bound on the new tokens per sequence. Returns out
+    [total_q, Hq, D] bf16."""
+    torch = _torch()
+    if k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("caches must be [num_blocks, Hkv, block_size, D] and alike")
+    nblk, hkv, bs, d = k_cache.shape
+    if bs != block_size:
+        raise ValueError("block_size %d does not match the caches' pages of %d tokens" % (block_size, bs))
+    tq = q.shape[0]
+    hq = (q.shape[1] * q.shape[2] if q.dim() == 3 else q.shape[1]) // d
+    dev = q.device
+    if q.dtype != torch.bfloat16 or dev.type != "cuda":
+        raise TypeError("q must be bf16 on a HIP device")
+    if q.stride(-1) != 1 or (q.dim() == 3 and q.stride(1) != d):
+        raise ValueError("each row of q must hold its Hq heads contiguously")
+    ldq = q.stride(0) if tq > 1 else hq * d
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if c.dtype != torch.uint8 or c.device != dev or not c.is_contiguous():
+            raise ValueError("%s must be a contiguous uint8 tensor on the device of q" % name)
+    if block_table.dim() != 2 or cu_seqlens_q.dim() != 1:
+        raise ValueError("block_table must be [B, max_blocks] and cu_seqlens_q [B + 1]")
+    b = block_table.shape[0]
+    _check(block_table, "block_table", torch.int32, (b, block_table.shape[1]), dev)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, (b + 1,), dev)
+    _check(context_lens, "context_lens", torch.int32, (b,), dev)
+    for name, sc in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        _check(sc.reshape(-1), name, torch.float32, (1,), dev)
+    out = torch.empty((tq, hq, d), dtype=torch.bfloat16, device=dev) if out is None else out
+    _check(out, "out", torch.bfloat16, (tq, hq, d), dev)
+    sm = 1.0 / d ** 0.5 if sm_scale is None else float(sm_scale)
+    fp8blk_prefill_attention(q.data_ptr(), ldq, tq, b, hq, hkv, d, cu_seqlens_q.data_ptr(), int(max_seqlen_q),
+                             k_cache.data_ptr(), v_cache.data_ptr(), nblk * bs, block_table.data_ptr(),
+                             block_table.shape[1], block_size, context_lens.data_ptr(), q_scale.data_ptr(),
+                             k_scale.data_ptr(), v_scale.data_ptr(), sm, out.data_ptr(), hq * d, _stream(dev))
     return out
 
 

@@ -14,7 +14,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8blk.so")
 
-SOURCES = ("quant.hip", "gemm.hip", "kv_cache.hip", "attention.hip")
+SOURCES = ("quant.hip", "gemm.hip", "kv_cache.hip", "attention.hip", "prefill_attention.hip")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

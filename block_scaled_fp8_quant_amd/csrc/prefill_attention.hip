@@ -1,0 +1,340 @@
+// FP8 prefill attention over the paged FP8 KV cache, for gfx950.
+//
+// Method (upppp.jp NeMo RL FP8 article, «KVキャッシュとAttentionにも拡張»;
+// greentreeone.com article, «Реальные прирост производительности»): attention
+// runs in FP8 over the FP8 KV cache with the recalibrated Q/K/V scales. The
+// prefill step: a sequence's n new tokens are the last n of its L cached
+// tokens (their K and V already written by the cache write), and new token i,
+// at position p = L - n + i, attends causally to cached tokens 0..p:
+//     s[t] = (q8 . k8[t]) * q_scale * k_scale * sm_scale,   t <= p
+//     out  = bf16( sum_t softmax(s)[t] * v8[t] * v_scale )
+// with q8 the per-tensor E4M3 quantization of the query (as the decode step).
+//
+// Work decomposition: a workgroup of four waves takes one (sequence, KV
+// head, block of 128/G consecutive new tokens); its 128 rows are the (token,
+// query head) pairs of that block, row = token * G + head, 32 per wave. The
+// KV loop walks 64-token tiles up to the block's last position; each tile's
+// K and V rows (one cache row of 128 bytes per token) are loaded by the
+// whole workgroup into registers while the previous tile is computed, then
+// written to LDS (two stages, one barrier per tile). Per tile and wave:
+//   * S^T = K Q^T on the FP8 matrix cores: v_mfma_scale_f32_16x16x128_f8f6f4,
+//     source 0 = 16 K rows (tokens), source 1 = 16 query rows, the whole head
+//     (D = 128) in one instruction; lane (c, g) then holds the scores of
+//     tokens 16u + 4g + r (r < 4) for query row c, so a row's maximum is an
+//     in-lane maximum and two cross-lane steps;
+//   * online softmax in the log2 domain (v_exp_f32), fp32;
+//   * O^T += V^T P^T on the fp16 matrix cores (v_mfma_f32_16x16x32_f16),
+//     source 1 = the probabilities straight from the score registers (the
+//     token order of the contraction is chosen to match the score layout),
+//     each probability split into an fp16 head and an fp16 remainder (two
+//     MFMAs, ~2^-22 relative: the probabilities stay unquantized to within
+//     fp32 accuracy), source 0 = V^T: the transpose of the tile's V rows read
+//     from LDS with ds_read_b64_tr_b8, converted to fp16 (exact for E4M3).
+// LDS rows are 128 bytes with 16-byte chunk c of row r stored at c ^ key(r),
+// so the 16-row fragment reads spread over the banks.
+#include "common.h"
+#include "quant_common.h"
+
+namespace fp8blk {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+constexpr int kD = 128;         // head size
+constexpr int kTile = 64;       // tokens per KV tile
+constexpr int kRows = 128;      // score rows per workgroup: (token, head) pairs
+constexpr float kLog2e = 1.44269504088896341f;
+
+// A cache row pointer marked as global memory (global, not flat, loads).
+typedef const __attribute__((address_space(1))) uint8_t* gbytes;
+
+__device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * kD + ((chunk ^ swz_key(row)) << 4); }
+
+// fp32 maximum / sum over the four lanes c, c+16, c+32, c+48
+__device__ __forceinline__ float cross4_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+__device__ __forceinline__ float cross4_sum(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+// 8 E4M3 codes (two dwords) -> 8 fp16 values (exact)
+__device__ __forceinline__ v8h fp8x8_to_f16(v2i w) {
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w[0], 1.0f, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w[0], 1.0f, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w[1], 1.0f, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)w[1], 1.0f, true);
+  return v8h{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+template <int G>  // query heads per KV head: 1, 2, 4 or 8
+__global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
+    const uint16_t* __restrict__ q, int64_t ldq, int64_t total_q, int64_t B, int64_t Hkv,
+    const int32_t* __restrict__ cu_seqlens_q, int64_t nqb, const uint8_t* __restrict__ k_cache,
+    const uint8_t* __restrict__ v_cache, int64_t num_slots, const int32_t* __restrict__ block_table,
+    int64_t max_blocks, int64_t block_size, const int32_t* __restrict__ context_lens,
+    const float* __restrict__ q_scale, const float* __restrict__ k_scale, const float* __restrict__ v_scale,
+    float sm_scale, uint16_t* __restrict__ out, int64_t ldo) {
+  constexpr int BQ = kRows / G;  // new tokens per workgroup
+  __shared__ __attribute__((aligned(1024))) uint8_t kt[2][kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt[2][kTile * kD];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+  // longest blocks first: the last token blocks attend the most tokens
+  const int64_t pairs = B * Hkv;
+  const int64_t bh = blockIdx.x % pairs, qblk = nqb - 1 - (int64_t)blockIdx.x / pairs;
+  const int64_t b = bh / Hkv, gk = bh % Hkv;
+  const int64_t row0 = cu_seqlens_q[b];
+  int64_t n = (int64_t)cu_seqlens_q[b + 1] - row0;  // new tokens
+  const int64_t L = context_lens[b] > 0 ? context_lens[b] : 0;
+  const int64_t i0 = qblk * BQ;
+  if (n <= i0 || row0 < 0) return;  // uniform: no new token in this block
+  if (n > total_q - row0) n = total_q - row0;  // rows past q/out (offsets that break their contract)
+  if (n <= i0) return;
+  // positions of the block's first and last tokens; tiles up to the last
+  const int64_t p_last = L - n + (i0 + BQ < n ? i0 + BQ : n) - 1;
+  const int64_t t_end = p_last + 1 < L ? p_last + 1 : L;  // tokens [0, t_end) are needed
+  const int ntiles = t_end > 0 ? (int)((t_end + kTile - 1) / kTile) : 0;
+  const float qs = *q_scale, ks = *k_scale, vs = *v_scale;
+
+  // this lane's two score rows (one per 16-row tile qt): row 32*wave + 16qt + c16
+  int64_t pos[2];
+  bool active[2];
+  int64_t orow[2];
+  int ohead[2];
+  v8i qfrag[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int r = 32 * wave + 16 * qt + c16;
+    const int64_t i = i0 + r / G;
+    active[qt] = i < n;
+    pos[qt] = L - n + i;
+    orow[qt] = row0 + i;
+    ohead[qt] = (int)(gk * G + r % G);
+    // source 1 fragment: query row r, head dims 16g..16g+15 and 64+16g..+15 -> E4M3
+    qfrag[qt] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    if (active[qt]) {
+      const uint16_t* src = q + orow[qt] * ldq + (int64_t)ohead[qt] * kD;
+      const uint4 lo0 = *reinterpret_cast<const uint4*>(src + 16 * g);
+      const uint4 lo1 = *reinterpret_cast<const uint4*>(src + 16 * g + 8);
+      const uint4 hi0 = *reinterpret_cast<const uint4*>(src + 64 + 16 * g);
+      const uint4 hi1 = *reinterpret_cast<const uint4*>(src + 64 + 16 * g + 8);
+      const bool fast = qs >= kCalibratedMinScale && qs <= kCalibratedMaxScale;
+      const float inv = 1.0f / qs;
+      const uint32_t w0[4] = {lo0.x, lo0.y, lo0.z, lo0.w}, w1[4] = {lo1.x, lo1.y, lo1.z, lo1.w};
+      const uint32_t w2[4] = {hi0.x, hi0.y, hi0.z, hi0.w}, w3[4] = {hi1.x, hi1.y, hi1.z, hi1.w};
+      const u32x2 c0 = encode8_calibrated(w0, qs, inv, fast), c1 = encode8_calibrated(w1, qs, inv, fast);
+      const u32x2 c2 = encode8_calibrated(w2, qs, inv, fast), c3 = encode8_calibrated(w3, qs, inv, fast);
+      qfrag[qt] = v8i{(int)c0.x, (int)c0.y, (int)c1.x, (int)c1.y, (int)c2.x, (int)c2.y, (int)c3.x, (int)c3.y};
+    }
+  }
+  const float s2scale = qs * ks * sm_scale * kLog2e;
+
+  // K/V tile loads: thread tid takes token tid/4 of the tile, bytes 32*(tid%4)..+31
+  const int ltok = tid >> 2, lpart = tid & 3;
+  const uint32_t bs32 = (uint32_t)block_size;
+  const int32_t* const table_row = block_table + b * max_blocks;
+  auto cache_row = [&](int64_t t) -> int64_t {  // cache row of token t, -1 if masked
+    if (t >= t_end) return -1;
+    const uint32_t bi = (uint32_t)t / bs32;
+    if (bi >= (uint64_t)max_blocks) return -1;
+    const int32_t blk = table_row[bi];
+    const uint32_t off = (uint32_t)t - bi * bs32;
+    if (blk < 0 || (int64_t)blk * block_size + off >= num_slots) return -1;
+    return ((int64_t)blk * Hkv + gk) * block_size + off;
+  };
+  u32x4 kr[2], vr[2];
+  auto load_tile = [&](int tile) {
+    const int64_t row = cache_row((int64_t)tile * kTile + ltok);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      kr[h] = zero;
+      vr[h] = zero;
+    }
+    if (row >= 0) {
+      const gbytes kp = (gbytes)(k_cache + row * kD + 32 * lpart);
+      const gbytes vp = (gbytes)(v_cache + row * kD + 32 * lpart);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        kr[h] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kp + 16 * h);
+        vr[h] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(vp + 16 * h));
+      }
+    }
+  };
+  auto store_tile = [&](int st) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      *reinterpret_cast<u32x4*>(&kt[st][swz(ltok, 2 * lpart + h)]) = kr[h];
+      *reinterpret_cast<u32x4*>(&vt[st][swz(ltok, 2 * lpart + h)]) = vr[h];
+    }
+  };
+
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+  v4f acc[2][8];  // O^T tiles: [qt][dt], lane (c, g) holds O[row 16qt + c][dim 16dt + 4g + r]
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[qt][dt] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  for (int tile = 0; tile < ntiles; ++tile) {
+    const int st = tile & 1;
+    __syncthreads();  // stage st holds this tile; stage st^1 is no longer read
+    if (tile + 1 < ntiles) load_tile(tile + 1);  // in flight while this tile is computed
+    const uint8_t* K = kt[st];
+    const uint8_t* V = vt[st];
+    const int64_t t0 = (int64_t)tile * kTile;
+
+    // S^T: lane (c, g) gets s[u][qt][r] = score of token t0 + 16u + 4g + r, row 16qt + c
+    float s[4][2][4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int krow = 16 * u + c16;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(K + swz(krow, g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(K + swz(krow, g + 4));
+      const v8i kfrag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kfrag, qfrag[qt], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                       0, 0, 0, 127, 0, 127);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t t = t0 + 16 * u + 4 * g + r;
+          s[u][qt][r] = (t <= pos[qt] && t < L) ? d[r] * s2scale : -INFINITY;
+        }
+      }
+    }
+    // online softmax per row; p replaces s
+    float alpha[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float mt = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[u][qt][r]);
+      mt = cross4_max(mt);
+      const float mn = fmaxf(m_run[qt], mt);
+      const float ms = mn == -INFINITY ? 0.f : mn;  // no token yet: keep exp2 finite
+      alpha[qt] = __builtin_amdgcn_exp2f(m_run[qt] - ms);
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          s[u][qt][r] = __builtin_amdgcn_exp2f(s[u][qt][r] - ms);
+          ps += s[u][qt][r];
+        }
+      l_run[qt] = l_run[qt] * alpha[qt] + ps;  // this lane's share; the four lanes of a row add up at the end
+      m_run[qt] = mn;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) acc[qt][dt] *= alpha[qt];
+    }
+    // O^T += V^T P^T over two 32-token chunks. Contraction slot (g, j) of
+    // chunk c is token 32c + 16(j/4) + 4g + j%4: the probabilities a lane
+    // holds for its row; V^T comes from the transpose read (source lanes 2j
+    // and 2j+1 of a 16-lane group read the two 8-byte halves of token slot
+    // j's 16 values of the dim tile).
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      v8h ph[2], pl[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = s[2 * c + j / 4][qt][j % 4];
+          const _Float16 h = (_Float16)p;
+          ph[qt][j] = h;
+          pl[qt][j] = (_Float16)(p - (float)h);
+        }
+      const int j = c16 >> 1, half = c16 & 1;
+      const int vrow = 32 * c + 16 * (j / 4) + 4 * g + (j % 4);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (lds_v2i*)(V + swz(vrow, dt) + 8 * half));
+        const v8h vf = fp8x8_to_f16(raw);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[qt], acc[qt][dt], 0, 0, 0);
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt], acc[qt][dt], 0, 0, 0);
+        }
+      }
+    }
+    if (tile + 1 < ntiles) store_tile(st ^ 1);  // the other stage was last read before this tile's barrier
+  }
+
+  // normalise and store: lane (c, g) holds dims 16dt + 4g .. +3 of row 16qt + c
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const float l = cross4_sum(l_run[qt]);
+    if (!active[qt]) continue;
+    const float inv = l > 0.f ? vs / l : 0.f;
+    uint16_t* dst = out + orow[qt] * ldo + (int64_t)ohead[qt] * kD + 4 * g;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+      const uint32_t lo = (uint32_t)to_bf16_bits(acc[qt][dt][0] * inv) | ((uint32_t)to_bf16_bits(acc[qt][dt][1] * inv) << 16);
+      const uint32_t hi = (uint32_t)to_bf16_bits(acc[qt][dt][2] * inv) | ((uint32_t)to_bf16_bits(acc[qt][dt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(lo, hi);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace fp8blk
+
+using namespace fp8blk;
+
+extern "C" fp8blk_status fp8blk_prefill_attention(const uint16_t* q, int64_t ldq, int64_t total_q, int64_t B,
+                                                  int64_t Hq, int64_t Hkv, int64_t D, const int32_t* cu_seqlens_q,
+                                                  int64_t max_seqlen_q, const uint8_t* k_cache, const uint8_t* v_cache,
+                                                  int64_t num_slots, const int32_t* block_table, int64_t max_blocks,
+                                                  int64_t block_size, const int32_t* context_lens,
+                                                  const float* q_scale, const float* k_scale, const float* v_scale,
+                                                  float sm_scale, uint16_t* out, int64_t ldo, hipStream_t stream) {
+  if (B < 0 || total_q < 0 || Hq < 1 || Hkv < 1 || D < 1 || max_seqlen_q < 0 || max_blocks < 1 || block_size < 1 ||
+      num_slots < 0 || !(sm_scale == sm_scale) || ldq < Hq * D || ldo < Hq * D)
+    return FP8BLK_ERR_INVALID_ARG;
+  const int64_t G = Hq / Hkv;
+  if (D != kD || Hq % Hkv || (G != 1 && G != 2 && G != 4 && G != 8) || ldq % 8 || ldo % 8 ||
+      num_slots % block_size || num_slots > INT32_MAX / Hkv || max_blocks > INT32_MAX || block_size > INT32_MAX)
+    return FP8BLK_ERR_SHAPE;
+  if (B == 0 || total_q == 0 || max_seqlen_q == 0) return FP8BLK_OK;
+  if (!q || !cu_seqlens_q || !k_cache || !v_cache || !block_table || !context_lens || !q_scale || !k_scale ||
+      !v_scale || !out)
+    return FP8BLK_ERR_INVALID_ARG;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      !aligned(cu_seqlens_q, 4) || !aligned(block_table, 4) || !aligned(context_lens, 4) || !aligned(q_scale, 4) ||
+      !aligned(k_scale, 4) || !aligned(v_scale, 4))
+    return FP8BLK_ERR_ALIGNMENT;
+  const int64_t bq = kRows / G;
+  const int64_t nqb = (max_seqlen_q + bq - 1) / bq;
+  if (B * Hkv * nqb > INT32_MAX) return FP8BLK_ERR_SHAPE;
+  const dim3 grid((uint32_t)(B * Hkv * nqb));
+#define FP8BLK_PREFILL_LAUNCH(GV)                                                                                 \
+  hipLaunchKernelGGL((prefill_attention_kernel<GV>), grid, dim3(256), 0, stream, q, ldq, total_q, B, Hkv,        \
+                     cu_seqlens_q, nqb, k_cache, v_cache, num_slots, block_table, max_blocks, block_size,         \
+                     context_lens, q_scale, k_scale, v_scale, sm_scale, out, ldo)
+  switch (G) {
+    case 1: FP8BLK_PREFILL_LAUNCH(1); break;
+    case 2: FP8BLK_PREFILL_LAUNCH(2); break;
+    case 4: FP8BLK_PREFILL_LAUNCH(4); break;
+    default: FP8BLK_PREFILL_LAUNCH(8); break;
+  }
+#undef FP8BLK_PREFILL_LAUNCH
+  return launch_status();
+}

@@ -458,6 +458,50 @@ size_t fp8blk_decode_attention_workspace_size(int64_t B, int64_t Hq, int64_t Hkv
                                               int64_t max_blocks, int64_t block_size,
                                               int64_t split_tokens);
 
+/*
+ * FP8 prefill attention over the paged FP8 KV cache (upppp.jp,
+ * «KVキャッシュとAttentionにも拡張»; greentreeone.com, «Реальные прирост
+ * производительности»): a prompt's (or a prompt chunk's) new tokens attend
+ * causally over the cache. Sequence b's n_b = cu_seqlens_q[b+1] -
+ * cu_seqlens_q[b] new tokens are the last n_b of its context_lens[b] cached
+ * tokens (their K and V already written by fp8blk_kv_cache_write), so new
+ * token i sits at position p = context_lens[b] - n_b + i and attends to
+ * cached tokens 0..p (the decode step is n_b = 1):
+ *   q8 = E4M3(RN_fp32(q / q_scale)) (as the cache write quantizes K and V)
+ *   s[h][t] = (sum_d q8[h][d] * k8[t][g][d]) * q_scale * k_scale * sm_scale,
+ *             g = h / (Hq / Hkv), t <= p
+ *   out[h][d] = bf16( sum_t softmax_t(s[h])[t] * v8[t][g][d] * v_scale )
+ * with the softmax and the sums in fp32 (the probabilities enter the
+ * weighted sum to within fp32 accuracy, unquantized).
+ *   q            [total_q][ldq] bf16: row cu_seqlens_q[b] + i holds new token
+ *                i of sequence b, its Hq query heads in the first Hq*D values
+ *                (q may point into a qkv projection output)
+ *   total_q      rows of q and of out (host); rows past it are never touched
+ *   cu_seqlens_q [B+1] int32 (device): cu_seqlens_q[0] = 0, nondecreasing,
+ *                cu_seqlens_q[B] <= total_q (not checked: offsets that break
+ *                this give wrong rows, never an access outside q or out)
+ *   max_seqlen_q a host bound on n_b (tokens past it are not computed)
+ *   k_cache, v_cache, num_slots, block_table, max_blocks, block_size,
+ *   context_lens, q_scale, k_scale, v_scale, sm_scale: as for
+ *                fp8blk_decode_attention (tokens whose block is out of the
+ *                table, negative or past num_slots are skipped)
+ *   out          [total_q][ldo] bf16 out: Hq heads x D per row of a new
+ *                token (16-byte aligned); other rows are left untouched
+ *   D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}; ldq and ldo
+ *   multiples of 8 and >= Hq*D; B >= 0, total_q >= 0 and max_seqlen_q >= 0
+ *   (any of them 0: no-op); block_size, max_blocks >= 1. A new token whose
+ *   position is negative (n_b > context_lens[b]) attends to nothing: zeros.
+ */
+fp8blk_status fp8blk_prefill_attention(const uint16_t* q, int64_t ldq, int64_t total_q, int64_t B,
+                                       int64_t Hq, int64_t Hkv, int64_t D,
+                                       const int32_t* cu_seqlens_q, int64_t max_seqlen_q,
+                                       const uint8_t* k_cache, const uint8_t* v_cache,
+                                       int64_t num_slots, const int32_t* block_table,
+                                       int64_t max_blocks, int64_t block_size,
+                                       const int32_t* context_lens, const float* q_scale,
+                                       const float* k_scale, const float* v_scale, float sm_scale,
+                                       uint16_t* out, int64_t ldo, hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code (host memory). */
 const char* fp8blk_status_string(fp8blk_status status);
 

@@ -275,6 +275,42 @@ def attention_inputs(context_lens, hq, hkv, d=128, block_size=16, seed=0, spare_
                 block_size=block_size)
 
 
+def prefill_inputs(seqs, hq, hkv, d=128, block_size=16, seed=0, spare_blocks=3):
+    """A prefill step over a paged KV cache: ``seqs`` lists (n_new,
+    context_len) per sequence (the new tokens are the last n_new of the
+    context). q [total_q, Hq, D] ~ N(0, 1) for the new tokens, sequence b's
+    rows cu_seqlens_q[b]..; K ~ N(0, 2^2) and V ~ N(0, 0.5^2) rows [T, Hkv*D]
+    for every cached token (bf16), pages shuffled over a pool with
+    ``spare_blocks`` unused pages. Returns a dict like attention_inputs plus
+    cu_seqlens_q [B+1] int32 and max_seqlen_q."""
+    g = generator(0xA1, seed)
+    news = [int(n) for n, _ in seqs]
+    lens = [int(L) for _, L in seqs]
+    b = len(lens)
+    blocks = [(n + block_size - 1) // block_size for n in lens]
+    max_blocks = max(1, max(blocks))
+    pool = sum(blocks) + spare_blocks
+    perm = torch.randperm(pool, generator=g)
+    table = torch.full((b, max_blocks), -1, dtype=torch.int32)
+    slots, used = [], 0
+    for i, n in enumerate(lens):
+        table[i, :blocks[i]] = perm[used:used + blocks[i]].to(torch.int32)
+        used += blocks[i]
+        for t in range(n):
+            slots.append(int(table[i, t // block_size]) * block_size + t % block_size)
+    tot = len(slots)
+    cu = [0]
+    for n in news:
+        cu.append(cu[-1] + n)
+    q = torch.randn(cu[-1], hq, d, generator=g).to(torch.bfloat16)
+    k = (torch.randn(tot, hkv * d, generator=g) * 2.0).to(torch.bfloat16)
+    v = (torch.randn(tot, hkv * d, generator=g) * 0.5).to(torch.bfloat16)
+    return dict(q=q, k=k, v=v, slot=torch.tensor(slots, dtype=torch.int64), block_table=table,
+                context_lens=torch.tensor(lens, dtype=torch.int32), num_slots=pool * block_size,
+                block_size=block_size, cu_seqlens_q=torch.tensor(cu, dtype=torch.int32),
+                max_seqlen_q=max(news) if news else 0)
+
+
 def random_cache_codes(shape, seed, device):
     """E4M3 codes drawn on ``device``: magnitude codes 0..126 (finite values)
     with random signs, for caches too large to draw on the host."""

@@ -35,7 +35,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "fp8blk_quant_act", "fp8blk_quant_weight", "fp8blk_gemm", "fp8blk_gemm_ws", "fp8blk_gemm_workspace_size",
-        "fp8blk_gemm_noalloc",
+        "fp8blk_gemm_noalloc", "fp8blk_prefill_attention",
         "fp8blk_grouped_gemm",
         "fp8blk_rmsnorm_quant_act", "fp8blk_silu_mul_quant_act", "fp8blk_qkv_amax", "fp8blk_kv_scales",
         "fp8blk_kv_cache_write", "fp8blk_quant_act_t", "fp8blk_quant_weight_t", "fp8blk_gemm_rowscaled",
@@ -378,3 +378,29 @@ def test_split_workspace_fits_the_static_scratch(lib):
                 worst = max(worst, size(mm, n, k))
     assert 0 < worst <= fb.GEMM_SCRATCH_BYTES
     assert size(256, 4096, 14336) == fb.GEMM_SCRATCH_BYTES    # the decode down projection: the largest
+
+
+def test_prefill_attention_validation(lib):
+    f = lib.fp8blk_prefill_attention
+
+    def call(q=P, ldq=4096, total_q=16, B=2, Hq=32, Hkv=8, D=128, cu=P, mx=8, kc=P, vc=P, slots=1024, table=P,
+             mb=4, bs=16, lens=P, qs=P, ks=P, vs=P, sm=0.088, out=P, ldo=4096):
+        return f(q, ldq, total_q, B, Hq, Hkv, D, cu, mx, kc, vc, slots, table, mb, bs, lens, qs, ks, vs, sm, out, ldo,
+                 NULL)
+
+    assert call(B=-1) == INVALID
+    assert call(total_q=-1) == INVALID
+    assert call(mx=-1) == INVALID
+    assert call(ldq=4000) == INVALID          # < Hq * D
+    assert call(sm=float("nan")) == INVALID
+    assert call(D=64, ldq=2048, ldo=2048) == SHAPE
+    assert call(Hq=24) == SHAPE               # Hq / Hkv = 3
+    assert call(Hq=128, ldq=16384, ldo=16384) == SHAPE   # Hq / Hkv = 16
+    assert call(slots=1000) == SHAPE          # not whole pages
+    assert call(ldq=4100) == SHAPE            # not a multiple of 8
+    assert call(cu=NULL) == INVALID
+    assert call(out=NULL) == INVALID
+    assert call(q=P4) == ALIGN
+    assert call(cu=P + 2) == ALIGN
+    assert call(B=0, q=NULL, cu=NULL, out=NULL) == OK      # nothing to do
+    assert call(mx=0, q=NULL, cu=NULL, out=NULL) == OK
