@@ -12,21 +12,26 @@ Two layers:
     ``fp8blk_silu_mul_quant_act``, ``fp8blk_qkv_amax``, ``fp8blk_kv_scales``,
     ``fp8blk_kv_cache_write``, ``fp8blk_quant_act_t``,
     ``fp8blk_quant_weight_t``, ``fp8blk_gemm_rowscaled``,
-    ``fp8blk_decode_attention``: the C entry points under their own names
+    ``fp8blk_decode_attention``, ``fp8blk_prefill_attention``,
+    ``fp8blk_gemm_noalloc``: the C entry points under their own names
     (integer device pointers, sizes, stream handle); they raise
     ``Fp8BlkError`` on a non-OK status;
   * ``quant_act``, ``quant_weight``, ``gemm``, ``grouped_gemm``,
     ``rmsnorm_quant_act``, ``silu_mul_quant_act``, ``qkv_amax``,
     ``kv_scales``, ``kv_cache_write``, ``quant_act_t``, ``quant_weight_t``,
     ``gemm_rowscaled`` (and ``dgrad``, ``wgrad`` built from them),
-    ``decode_attention``: tensor versions that validate shapes and allocate
-    outputs.
+    ``decode_attention``, ``prefill_attention``: tensor versions that
+    validate shapes and allocate outputs.
+
+The library loaded is the in-tree libfp8blk.so, or the file the environment
+variable FP8BLK_LIB names (a variant build of the same sources, e.g. the
+host-sanitizer build the CPU tests use); a missing file raises.
 """
 
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.so")
+LIB_PATH = os.environ.get("FP8BLK_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8blk.so")
 BLOCK = 128
 
 STATUS = {0: "FP8BLK_OK", 1: "FP8BLK_ERR_INVALID_ARG", 2: "FP8BLK_ERR_SHAPE",
@@ -43,15 +48,9 @@ class Fp8BlkError(RuntimeError):
         self.status = status
 
 
-def load():
-    """Load libfp8blk.so (once). Raises if it has not been built."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError("libfp8blk.so is not built (%s); run __graft_entry__.build() "
-                           "or python -m block_scaled_fp8_quant_amd.build" % LIB_PATH)
-    lib = ctypes.CDLL(LIB_PATH)
+def declare(lib):
+    """Give every C entry point the library exports its ctypes signature
+    (a variant build may export a subset)."""
     vp, i64, i32, f32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float
     sigs = {
         "fp8blk_quant_act": [vp, i64, i64, vp, vp, i32, vp],
@@ -77,17 +76,32 @@ def load():
         "fp8blk_kv_cache_write": [vp, vp, i64, i64, i64, i64, vp, i64, i64, vp, vp, vp, vp, vp],
     }
     for name, args in sigs.items():
-        fn = getattr(lib, name)
-        fn.argtypes = args
-        fn.restype = ctypes.c_int
-    lib.fp8blk_gemm_workspace_size.argtypes = [i64, i64, i64]
-    lib.fp8blk_gemm_workspace_size.restype = ctypes.c_size_t
-    lib.fp8blk_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64]
-    lib.fp8blk_decode_attention_workspace_size.restype = ctypes.c_size_t
-    lib.fp8blk_status_string.argtypes = [ctypes.c_int]
-    lib.fp8blk_status_string.restype = ctypes.c_char_p
-    _lib = lib
+        if hasattr(lib, name):
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+    if hasattr(lib, "fp8blk_gemm_workspace_size"):
+        lib.fp8blk_gemm_workspace_size.argtypes = [i64, i64, i64]
+        lib.fp8blk_gemm_workspace_size.restype = ctypes.c_size_t
+    if hasattr(lib, "fp8blk_decode_attention_workspace_size"):
+        lib.fp8blk_decode_attention_workspace_size.argtypes = [i64, i64, i64, i64, i64, i64, i64]
+        lib.fp8blk_decode_attention_workspace_size.restype = ctypes.c_size_t
+    if hasattr(lib, "fp8blk_status_string"):
+        lib.fp8blk_status_string.argtypes = [ctypes.c_int]
+        lib.fp8blk_status_string.restype = ctypes.c_char_p
     return lib
+
+
+def load():
+    """Load libfp8blk.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfp8blk.so is not built (%s); run __graft_entry__.build() "
+                           "or python -m block_scaled_fp8_quant_amd.build" % LIB_PATH)
+    _lib = declare(ctypes.CDLL(LIB_PATH))
+    return _lib
 
 
 def _call(name, *args):

@@ -46,6 +46,16 @@
 #define FP8BLK_GEMM_GROUP_M 8
 #endif
 
+// Race-detection build (-DFP8BLK_DEBUG_BARRIERS=1): every LDS stage
+// transition of the K loop also waits for all of the wave's loads and passes
+// a full workgroup barrier, so no stage can be read while a refill writes it
+// or refilled while a wave still reads it. The arithmetic is unchanged: its
+// outputs must equal the normal build's bit for bit (a GPU test compares
+// them); a difference would expose a missing wait or barrier.
+#ifndef FP8BLK_DEBUG_BARRIERS
+#define FP8BLK_DEBUG_BARRIERS 0
+#endif
+
 namespace fp8blk {
 namespace {
 
@@ -178,6 +188,14 @@ __device__ __forceinline__ void wait_vm0() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(kWaitVm0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// The race-detection build's extra synchronisation (nothing otherwise).
+__device__ __forceinline__ void debug_stage_sync() {
+  if constexpr (FP8BLK_DEBUG_BARRIERS != 0) {
+    wait_vm0();
+    __syncthreads();
+  }
 }
 
 // Wait until at most N of this wave's global loads are outstanding (loads
@@ -443,6 +461,7 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
 
   for (int kb = 0; kb < KB; ++kb) {
+    debug_stage_sync();
     const int st = kb % S;
     const uint8_t* sA = smem_generic + st * C::STAGE;
     {  // (1); on the first step the operands are zero
@@ -533,6 +552,7 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
       issue_stage<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
     else if constexpr (LOADER)
       issue_stage_pair<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
+    debug_stage_sync();
     sched_fence();
   }
   if constexpr (POW2) {

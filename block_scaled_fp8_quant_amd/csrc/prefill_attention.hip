@@ -56,6 +56,19 @@ typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 __device__ __forceinline__ int swz_key(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kD + ((chunk ^ swz_key(row)) << 4); }
 
+// Race-detection build (-DFP8BLK_DEBUG_BARRIERS=1): extra workgroup
+// barriers (after every wave's loads have landed) around each stage's use,
+// same arithmetic, so the outputs must equal the normal build's bit for bit.
+#ifndef FP8BLK_DEBUG_BARRIERS
+#define FP8BLK_DEBUG_BARRIERS 0
+#endif
+__device__ __forceinline__ void debug_stage_sync() {
+  if constexpr (FP8BLK_DEBUG_BARRIERS != 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
 // fp32 maximum / sum over the four lanes c, c+16, c+32, c+48
 __device__ __forceinline__ float cross4_max(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));
@@ -194,6 +207,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
   for (int tile = 0; tile < ntiles; ++tile) {
     const int st = tile & 1;
     __syncthreads();  // stage st holds this tile; stage st^1 is no longer read
+    debug_stage_sync();
     if (tile + 1 < ntiles) load_tile(tile + 1);  // in flight while this tile is computed
     const uint8_t* K = kt[st];
     const uint8_t* V = vt[st];
@@ -275,7 +289,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
         }
       }
     }
+    debug_stage_sync();
     if (tile + 1 < ntiles) store_tile(st ^ 1);  // the other stage was last read before this tile's barrier
+    debug_stage_sync();
   }
 
   // normalise and store: lane (c, g) holds dims 16dt + 4g .. +3 of row 16qt + c

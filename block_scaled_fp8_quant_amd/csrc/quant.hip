@@ -702,8 +702,14 @@ extern "C" fp8blk_status fp8blk_silu_mul_quant_act(const uint16_t* gu, int64_t M
   return launch_status();
 }
 
+// Callers may pass any integer (the header promises "unknown status" for
+// unknown codes), and a value outside the enumerators' range is undefined
+// behaviour when read as the enum: the code is read as an int.
 extern "C" const char* fp8blk_status_string(fp8blk_status status) {
-  switch (status) {
+  int code;
+  static_assert(sizeof(code) == sizeof(status), "status codes are int-sized");
+  __builtin_memcpy(&code, &status, sizeof(code));
+  switch (code) {
     case FP8BLK_OK: return "ok";
     case FP8BLK_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size or bad flag)";
     case FP8BLK_ERR_SHAPE: return "unsupported shape (K and N must be multiples of 128, GEMM K <= 2^24, E >= 1)";
