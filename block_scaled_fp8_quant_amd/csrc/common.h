@@ -44,6 +44,22 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8
+// lanes within each 16-lane row (DPP, lanes shifted in from outside the row
+// read 0), then the totals of the earlier rows (readlane) added to each row.
+// No LDS round trips, unlike lane shuffles.
+__device__ __forceinline__ int wave_prefix_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (int)(threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
 // Find which expert owns M-tile `t` (0 <= t < 2^24) of the concatenated
 // per-expert tile lists (expert e has ceil(M_e / BM) tiles). Every lane of
 // the wave computes the same answer: lanes take 64 experts at a time and a
@@ -63,20 +79,15 @@ __device__ __forceinline__ bool locate_tile(const int32_t* __restrict__ off, int
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
     const int cnt = e < E ? tile_count(off[e], off[e + 1], BM) : 0;
-    int incl = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    const int total = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));  // uniform: so is the branch
+    const int incl = wave_prefix_sum(cnt);
+    const int total = __builtin_amdgcn_readlane(incl, 63);  // uniform: so is the branch
     if (t < base + total) {
       const bool mine = cnt > 0 && t >= base + incl - cnt && t < base + incl;
       const unsigned long long owners = (unsigned long long)__ballot(mine);
       if (owners == 0ull) return false;  // uniform; unreachable with consistent counts
-      const int src = __ffsll(owners) - 1;
+      const int src = __builtin_amdgcn_readfirstlane(__ffsll(owners) - 1);
       expert = __builtin_amdgcn_readfirstlane(e0 + src);
-      tile_in_expert = __builtin_amdgcn_readfirstlane(t - base - __shfl(incl - cnt, src));
+      tile_in_expert = __builtin_amdgcn_readfirstlane(t - base - __builtin_amdgcn_readlane(incl - cnt, src));
       return true;
     }
     base += total;

@@ -361,17 +361,20 @@ __device__ __forceinline__ bool wave_all(bool ok) { return __builtin_amdgcn_ball
 // wave w checks BM/WAVES of the tile's activation-scale rows (each row's KB
 // scales are contiguous, so a wave's share is one run of floats; rows past
 // M read as zero) and the last wave also the weight scales of the tile's
-// column blocks. The first 8 KB of each share is loaded before the tile's
-// first direct loads, so waiting for it leaves those in flight; the rest
-// (K > 8192) is read after. Each wave's verdict goes to LDS and is read by
-// all after the barrier that follows the first direct loads.
+// column blocks. The first 1 KB of each share is loaded before the tile's
+// first direct loads, so waiting for it leaves those in flight; the rest is
+// read only while everything seen so far is a power of two (scales from the
+// amax/448 rule almost never are, so most tiles decide on that first 1 KB:
+// eight early loads per wave measured ~5000 clocks of tile start-up, most of
+// them out of range but still through the address unit). Each wave's
+// verdict goes to LDS and is read by all after the barrier that follows the
+// first direct loads.
 template <class C>
 struct ScaleScan {
   static constexpr int ROWS = C::BM / C::WAVES;  // activation-scale rows per wave
-  static constexpr int FIRST = 8;                // 1 KB loads per wave issued early
   rsrc_t a, w;
   uint32_t a_bytes, w_bytes;
-  v4i a0[FIRST], w0;
+  v4i a0, w0;
 };
 
 template <class C>
@@ -389,27 +392,25 @@ __device__ __forceinline__ void scan_begin(ScaleScan<C>& sc, const float* sa, co
   const int64_t w_blocks = blocks < kColBlocks ? blocks : kColBlocks;
   sc.w_bytes = wave == C::WAVES - 1 ? (uint32_t)(w_blocks * KB * 4) : 0u;
   sc.w = make_rsrc(sw + (n0 / kBlock) * KB, sc.w_bytes);
-#pragma unroll
-  for (int u = 0; u < S::FIRST; ++u)
-    sc.a0[u] = __builtin_amdgcn_raw_buffer_load_b128(sc.a, (uint32_t)u * 1024u + (uint32_t)lane * 16u, 0, 0);
+  sc.a0 = __builtin_amdgcn_raw_buffer_load_b128(sc.a, (uint32_t)lane * 16u, 0, 0);
   sc.w0 = __builtin_amdgcn_raw_buffer_load_b128(sc.w, (uint32_t)lane * 16u, 0, 0);
 }
 
 // This wave's verdict (wave-uniform). Loads past a resource's end read as
-// zero, which passes, so no load is conditional.
+// zero, which passes. The rest of the share is read only if the first 1 KB
+// (and the weight scales' first 1 KB) left the answer open.
 template <class C>
 __device__ __forceinline__ bool scan_end(const ScaleScan<C>& sc, int lane) {
-  using S = ScaleScan<C>;
-  bool ok = v4_e8m0_exact(sc.w0);
-#pragma unroll
-  for (int u = 0; u < S::FIRST; ++u) ok = ok & v4_e8m0_exact(sc.a0[u]);
-  for (uint32_t off = S::FIRST * 1024u; off < sc.a_bytes; off += 8192u) {
+  const bool ok = wave_all(v4_e8m0_exact(sc.w0) & v4_e8m0_exact(sc.a0));
+  if (!ok) return false;  // uniform
+  bool rest = true;
+  for (uint32_t off = 1024u; off < sc.a_bytes; off += 8192u) {
     v4i v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u)
       v[u] = __builtin_amdgcn_raw_buffer_load_b128(sc.a, off + (uint32_t)u * 1024u + (uint32_t)lane * 16u, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) ok = ok & v4_e8m0_exact(v[u]);
+    for (int u = 0; u < 8; ++u) rest = rest & v4_e8m0_exact(v[u]);
   }
   for (uint32_t off = 1024u; off < sc.w_bytes; off += 4096u) {
     v4i v[4];
@@ -417,9 +418,9 @@ __device__ __forceinline__ bool scan_end(const ScaleScan<C>& sc, int lane) {
     for (int u = 0; u < 4; ++u)
       v[u] = __builtin_amdgcn_raw_buffer_load_b128(sc.w, off + (uint32_t)u * 1024u + (uint32_t)lane * 16u, 0, 0);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) ok = ok & v4_e8m0_exact(v[u]);
+    for (int u = 0; u < 4; ++u) rest = rest & v4_e8m0_exact(v[u]);
   }
-  return wave_all(ok);
+  return wave_all(rest);
 }
 
 // The K loop of one wave, entered after the barrier that follows block 0's
