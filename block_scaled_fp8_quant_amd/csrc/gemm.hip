@@ -223,13 +223,13 @@ __device__ __forceinline__ void dma4(rsrc_t r, uint32_t voff, uint32_t soff, lds
 // (8 rows of 128 bytes); lane l writes slot l = (row l/8, physical chunk
 // l%8), so it fetches logical chunk (l%8) ^ key(row): byte offset
 // row * K + chunk * 16 within the tile's rows, plus 128 bytes per K step.
-template <class C>
-struct LoadPlan {
-  uint32_t a_off[C::A_WIN], b_off[C::B_WIN], s_off;
+// The scalar part of a tile's load plan: where its operands' rows and
+// scales start and how many bytes follow them (wave-uniform values).
+struct TileBases {
   const void *a, *b, *s;        // first byte of the tile's rows (scales: row or column block)
   uint32_t a_len, b_len, s_len;  // bytes from there to the operand's end (clamped to 4 GB - 1)
   const void* w;                 // PAIR: the weight-scale window's plan
-  uint32_t w_len, w_off;
+  uint32_t w_len;
   // PAIR: the rows of wave w + WAVES/2 (the tile's second half), with their
   // own resources. The buffer range check covers the VGPR offset only, not
   // the scalar one, so a row distance passed as the scalar offset would let
@@ -239,6 +239,14 @@ struct LoadPlan {
   uint32_t a2_len, b2_len;
 };
 
+// A tile's load plan: per-lane offsets (they depend only on the lane and
+// the row length, so every tile of a launch shares them) and its bases.
+template <class C>
+struct LoadPlan {
+  uint32_t a_off[C::A_WIN], b_off[C::B_WIN], s_off, w_off;
+  TileBases t;
+};
+
 
 
 // Direct loads of K block kb into `stage`; with live == false every
@@ -246,12 +254,18 @@ struct LoadPlan {
 // loop around this must stay one basic block. The first BM/64 waves load
 // the tile's activation scales (64 rows each); the others all load the
 // same BN/128 weight scales into the stage's last window.
+// `ln` is the plan of the workgroup's next tile (a persistent kernel loads
+// that tile's first blocks during the current tile's last steps): with
+// cur == false the block comes from it. Two tiles of one launch share the
+// per-lane offsets (they depend on the lane and the row length only), so
+// only the scalar bases and lengths are selected (no branch).
 template <class C>
-__device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp, int kb, int wave, bool live) {
+__device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp, const TileBases& ln, bool cur,
+                                            int kb, int wave, bool live) {
   const uint32_t koff = (uint32_t)kb * BK;
-  const rsrc_t a = make_rsrc(lp.a, live ? lp.a_len : 0u);
-  const rsrc_t b = make_rsrc(lp.b, live ? lp.b_len : 0u);
-  const rsrc_t s = make_rsrc(lp.s, live ? lp.s_len : 0u);
+  const rsrc_t a = make_rsrc(cur ? lp.t.a : ln.a, live ? (cur ? lp.t.a_len : ln.a_len) : 0u);
+  const rsrc_t b = make_rsrc(cur ? lp.t.b : ln.b, live ? (cur ? lp.t.b_len : ln.b_len) : 0u);
+  const rsrc_t s = make_rsrc(cur ? lp.t.s : ln.s, live ? (cur ? lp.t.s_len : ln.s_len) : 0u);
 #pragma unroll
   for (int i = 0; i < C::A_WIN; ++i) dma16(a, lp.a_off[i], koff, stage + (wave * C::A_WIN + i) * 1024);
 #pragma unroll
@@ -270,15 +284,16 @@ __device__ __forceinline__ void issue_stage(lds_u8* stage, const LoadPlan<C>& lp
 // rows), its activation-scale window and the weight-scale window; the other
 // waves issue nothing.
 template <class C>
-__device__ __forceinline__ void issue_stage_pair(lds_u8* stage, const LoadPlan<C>& lp, int kb, int wave, bool live) {
+__device__ __forceinline__ void issue_stage_pair(lds_u8* stage, const LoadPlan<C>& lp, const TileBases& ln,
+                                                 bool cur, int kb, int wave, bool live) {
   constexpr int H = C::WAVES / 2;
   const uint32_t koff = (uint32_t)kb * BK;
-  const rsrc_t a = make_rsrc(lp.a, live ? lp.a_len : 0u);
-  const rsrc_t b = make_rsrc(lp.b, live ? lp.b_len : 0u);
-  const rsrc_t s = make_rsrc(lp.s, live ? lp.s_len : 0u);
-  const rsrc_t w = make_rsrc(lp.w, live ? lp.w_len : 0u);
-  const rsrc_t a2 = make_rsrc(lp.a2, live ? lp.a2_len : 0u);
-  const rsrc_t b2 = make_rsrc(lp.b2, live ? lp.b2_len : 0u);
+  const rsrc_t a = make_rsrc(cur ? lp.t.a : ln.a, live ? (cur ? lp.t.a_len : ln.a_len) : 0u);
+  const rsrc_t b = make_rsrc(cur ? lp.t.b : ln.b, live ? (cur ? lp.t.b_len : ln.b_len) : 0u);
+  const rsrc_t s = make_rsrc(cur ? lp.t.s : ln.s, live ? (cur ? lp.t.s_len : ln.s_len) : 0u);
+  const rsrc_t w = make_rsrc(cur ? lp.t.w : ln.w, live ? (cur ? lp.t.w_len : ln.w_len) : 0u);
+  const rsrc_t a2 = make_rsrc(cur ? lp.t.a2 : ln.a2, live ? (cur ? lp.t.a2_len : ln.a2_len) : 0u);
+  const rsrc_t b2 = make_rsrc(cur ? lp.t.b2 : ln.b2, live ? (cur ? lp.t.b2_len : ln.b2_len) : 0u);
 #pragma unroll
   for (int i = 0; i < C::A_WIN; ++i) {
     dma16(a, lp.a_off[i], koff, stage + (wave * C::A_WIN + i) * 1024);
@@ -297,9 +312,9 @@ __device__ __forceinline__ void issue_stage_pair(lds_u8* stage, const LoadPlan<C
 template <class C>
 __device__ __forceinline__ void refill(lds_u8* stage, const LoadPlan<C>& lp, int kb, int wave, bool live) {
   if constexpr (C::PAIR) {
-    if (wave < C::WAVES / 2) issue_stage_pair<C>(stage, lp, kb, wave, live);  // uniform
+    if (wave < C::WAVES / 2) issue_stage_pair<C>(stage, lp, lp.t, true, kb, wave, live);  // uniform
   } else {
-    issue_stage<C>(stage, lp, kb, wave, live);
+    issue_stage<C>(stage, lp, lp.t, true, kb, wave, live);
   }
 }
 
@@ -430,9 +445,15 @@ __device__ __forceinline__ bool scan_end(const ScaleScan<C>& sc, int lane) {
 // a power of two): the MFMA applies SW and SA itself as E8M0 block scales
 // (source 0 = weights: the wave's SW; source 1 = activations: the lane's
 // row's SA) and accumulates into acc directly, with no fold.
+// lpn / has_next / s0 (persistent kernels): the refills past block KB - 1
+// load the next tile's first blocks (same K) from plan lpn instead of
+// nothing, and this tile's block kb lives in stage (kb + s0) mod STAGES
+// (s0 carries the stage of the previous tiles' blocks). has_next == false,
+// s0 == 0: one tile, the refills past the end fetch nothing.
 template <class C, bool POW2, bool LOADER = true>
 __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, const LoadPlan<C>& lp, int wave, int KB,
-                                       int wm, int wn, int g, int c16, v4f (&acc)[C::TM][C::TN]) {
+                                       int wm, int wn, int g, int c16, v4f (&acc)[C::TM][C::TN],
+                                       const TileBases& lpn, bool has_next, int s0) {
   constexpr int S = C::STAGES, LPS = C::LOADS_PER_STAGE;
   // Step kb, one basic block: (1) the previous step's last-row MFMAs, then
   // this stage's weight fragments, first activation fragment and scales are
@@ -463,7 +484,7 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
 
   for (int kb = 0; kb < KB; ++kb) {
     debug_stage_sync();
-    const int st = kb % S;
+    const int st = (kb + s0) % S;
     const uint8_t* sA = smem_generic + st * C::STAGE;
     {  // (1); on the first step the operands are zero
       // The last row's MFMA j is the last use of weight fragment j, so the
@@ -549,10 +570,15 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
       sc_last = C::RB ? srow[(C::TM - 1) / 4][(C::TM - 1) % 4] : srow[(C::TM - 1) / 4][(C::TM - 1) % 4] * swv;
     wait_vm<LPS * (C::PAIR ? 2 : 1) * (S - 2)>();  // (3) block kb+1 has landed
     lds_barrier();
-    if constexpr (!C::PAIR)
-      issue_stage<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
-    else if constexpr (LOADER)
-      issue_stage_pair<C>(smem + st * C::STAGE, lp, kb + S, wave, kb + S < KB);
+    {  // block kb + S of this tile, or block kb + S - KB of the next
+      const bool cur = kb + S < KB;
+      const int kl = cur ? kb + S : kb + S - KB;
+      const bool live = cur | (has_next & (kl < KB));
+      if constexpr (!C::PAIR)
+        issue_stage<C>(smem + st * C::STAGE, lp, lpn, cur, kl, wave, live);
+      else if constexpr (LOADER)
+        issue_stage_pair<C>(smem + st * C::STAGE, lp, lpn, cur, kl, wave, live);
+    }
     debug_stage_sync();
     sched_fence();
   }
@@ -573,7 +599,111 @@ __device__ __forceinline__ void k_loop(lds_u8* smem, uint8_t* smem_generic, cons
       fold_row<C>(acc[C::TM - 1], p, sc_last);
     }
   }
-  wait_vm0();  // no load may still be writing LDS when the workgroup ends
+  // no load may still be writing LDS when the workgroup ends (a next tile's
+  // blocks stay in flight: the caller waits for them)
+  if (!has_next) wait_vm0();
+}
+
+// The scalar bases and lengths of the tile at (m0, n0): its operands'
+// rows and scales (rows past M or N fall outside the resources and read as
+// zeros). Wave-uniform.
+template <class C>
+__device__ __forceinline__ void plan_bases(TileBases& t, const uint8_t* qa, const float* sa, const uint8_t* qw,
+                                           const float* sw, int64_t M, int64_t N, int64_t m0, int64_t n0, int64_t ld,
+                                           int64_t kb0, int wave) {
+  const int64_t KBld = ld / BK;  // scales per operand row
+  t.a = qa + m0 * ld + kb0 * BK;
+  t.b = qw + n0 * ld + kb0 * BK;
+  t.a_len = clamp_len((M - m0) * ld - kb0 * BK);
+  t.b_len = clamp_len((N - n0) * ld - kb0 * BK);
+  if (wave < C::BM / 64) {  // activation scales of the tile's rows
+    t.s = sa + m0 * KBld + kb0;
+    t.s_len = clamp_len(((M - m0) * KBld - kb0) * 4);
+  } else if constexpr (C::RB) {  // B-row scales (sw is SB[N][KB])
+    t.s = sw + n0 * KBld + kb0;
+    t.s_len = clamp_len(((N - n0) * KBld - kb0) * 4);
+  } else {  // weight scales of the tile's column blocks
+    t.s = sw + (n0 / kBlock) * KBld + kb0;
+    t.s_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
+  }
+  if constexpr (C::PAIR && C::RB) {  // B-row scales of tile rows 64w + lane
+    t.w = sw + n0 * KBld + kb0;
+    t.w_len = clamp_len(((N - n0) * KBld - kb0) * 4);
+  } else if constexpr (C::PAIR) {
+    t.w = sw + (n0 / kBlock) * KBld + kb0;
+    t.w_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
+  }
+  if constexpr (C::PAIR) {  // the second half's rows, each range-checked against its operand's end
+    constexpr int64_t ha = C::WAVES / 2 * C::A_WIN * 8, hb = C::WAVES / 2 * C::B_WIN * 8;
+    t.a2 = qa + (m0 + ha) * ld + kb0 * BK;
+    t.b2 = qw + (n0 + hb) * ld + kb0 * BK;
+    t.a2_len = clamp_len((M - m0 - ha) * ld - kb0 * BK);
+    t.b2_len = clamp_len((N - n0 - hb) * ld - kb0 * BK);
+  }
+}
+
+// A tile's whole load plan: the per-lane offsets of its direct loads (they
+// depend only on the lane and the row length ld) and its bases.
+template <class C>
+__device__ __forceinline__ void plan_tile(LoadPlan<C>& lp, const uint8_t* qa, const float* sa, const uint8_t* qw,
+                                          const float* sw, int64_t M, int64_t N, int64_t m0, int64_t n0, int64_t ld,
+                                          int64_t kb0, int wave, int lane) {
+  const int64_t KBld = ld / BK;  // scales per operand row
+#pragma unroll
+  for (int i = 0; i < C::A_WIN; ++i) {
+    const int row = (wave * C::A_WIN + i) * 8 + (lane >> 3);
+    lp.a_off[i] = (uint32_t)row * (uint32_t)ld + (((lane & 7) ^ swz_key(row)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < C::B_WIN; ++i) {
+    const int row = (wave * C::B_WIN + i) * 8 + (lane >> 3);
+    lp.b_off[i] = (uint32_t)row * (uint32_t)ld + (((lane & 7) ^ swz_key(row)) << 4);
+  }
+  if (wave < C::BM / 64) {
+    // Activation scales, permuted so that the TM scales one lane needs
+    // (rows wm + 16i + l%16, i < TM) are contiguous: slot t = h*WM + c*TM + i
+    // holds tile row h*WM + 16i + c.
+    const int t = wave * 64 + lane, h = t / C::WM, rem = t % C::WM;
+    const int row = h * C::WM + 16 * (rem % C::TM) + rem / C::TM;
+    lp.s_off = (uint32_t)row * (uint32_t)(KBld * 4);
+  } else if constexpr (C::RB) {
+    // B-row scales of tile rows bw*64 + lane, in natural order (sw is SB[N][KB])
+    const int bw = wave - C::BM / 64 < C::BN / 64 ? wave - C::BM / 64 : C::BN / 64 - 1;
+    lp.s_off = (uint32_t)(bw * 64 + lane) * (uint32_t)(KBld * 4);
+  } else {  // weight scales of column blocks n0/128 + lane (lanes past the tile's blocks repeat)
+    constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;  // a 64-wide tile lies in one block
+    lp.s_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
+  }
+  lp.w_off = 0u;
+  if constexpr (C::PAIR && C::RB) {  // B-row scales of tile rows 64w + lane
+    lp.w_off = (uint32_t)(wave * 64 + lane) * (uint32_t)(KBld * 4);
+  } else if constexpr (C::PAIR) {
+    constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;
+    lp.w_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
+  }
+  plan_bases<C>(lp.t, qa, sa, qw, sw, M, N, m0, n0, ld, kb0, wave);
+}
+
+// bf16 (nearest even) store of a finished tile: lane holds
+// Y[m0 + wm + 16i + l%16][n0 + wn + 16j + 4*(l/16) + r], r < 4 (rows N
+// long); rows past M are not stored. The caller skips waves whose columns
+// are past N.
+template <class C>
+__device__ __forceinline__ void store_tile(const v4f (&acc)[C::TM][C::TN], uint16_t* __restrict__ y, int64_t M,
+                                           int64_t N, int64_t m0, int64_t n0, int wm, int wn, int g, int c16) {
+#pragma unroll
+  for (int i = 0; i < C::TM; ++i) {
+    const int64_t row = m0 + wm + 16 * i + c16;
+    if (row < M) {
+      uint16_t* yr = y + row * N + n0 + wn + 4 * g;
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) {
+        const uint32_t lo = (uint32_t)to_bf16_bits(acc[i][j][0]) | ((uint32_t)to_bf16_bits(acc[i][j][1]) << 16);
+        const uint32_t hi = (uint32_t)to_bf16_bits(acc[i][j][2]) | ((uint32_t)to_bf16_bits(acc[i][j][3]) << 16);
+        *reinterpret_cast<uint2*>(yr + 16 * j) = make_uint2(lo, hi);
+      }
+    }
+  }
 }
 
 // One BM x BN output tile at (m0, n0) of Y[M][N] = A[M][K] W[N][K]^T; rows
@@ -613,58 +743,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
   const int64_t KBld = ld / BK;                                   // scales per operand row
 
   LoadPlan<C> lp;
-#pragma unroll
-  for (int i = 0; i < C::A_WIN; ++i) {
-    const int row = (wave * C::A_WIN + i) * 8 + (lane >> 3);
-    lp.a_off[i] = (uint32_t)row * (uint32_t)ld + (((lane & 7) ^ swz_key(row)) << 4);
-  }
-#pragma unroll
-  for (int i = 0; i < C::B_WIN; ++i) {
-    const int row = (wave * C::B_WIN + i) * 8 + (lane >> 3);
-    lp.b_off[i] = (uint32_t)row * (uint32_t)ld + (((lane & 7) ^ swz_key(row)) << 4);
-  }
-  lp.a = qa + m0 * ld + kb0 * BK;
-  lp.b = qw + n0 * ld + kb0 * BK;
-  lp.a_len = clamp_len((M - m0) * ld - kb0 * BK);
-  lp.b_len = clamp_len((N - n0) * ld - kb0 * BK);
-  if (wave < C::BM / 64) {
-    // Activation scales, permuted so that the TM scales one lane needs
-    // (rows wm + 16i + l%16, i < TM) are contiguous: slot t = h*WM + c*TM + i
-    // holds tile row h*WM + 16i + c.
-    const int t = wave * 64 + lane, h = t / C::WM, rem = t % C::WM;
-    const int row = h * C::WM + 16 * (rem % C::TM) + rem / C::TM;
-    lp.s = sa + m0 * KBld + kb0;
-    lp.s_len = clamp_len(((M - m0) * KBld - kb0) * 4);
-    lp.s_off = (uint32_t)row * (uint32_t)(KBld * 4);
-  } else if constexpr (C::RB) {
-    // B-row scales of tile rows bw*64 + lane, in natural order (sw is SB[N][KB])
-    const int bw = wave - C::BM / 64 < C::BN / 64 ? wave - C::BM / 64 : C::BN / 64 - 1;
-    lp.s = sw + n0 * KBld + kb0;
-    lp.s_len = clamp_len(((N - n0) * KBld - kb0) * 4);
-    lp.s_off = (uint32_t)(bw * 64 + lane) * (uint32_t)(KBld * 4);
-  } else {  // weight scales of column blocks n0/128 + lane (lanes past the tile's blocks repeat)
-    constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;  // a 64-wide tile lies in one block
-    lp.s = sw + (n0 / kBlock) * KBld + kb0;
-    lp.s_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
-    lp.s_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
-  }
-  if constexpr (C::PAIR && C::RB) {  // B-row scales of tile rows 64w + lane
-    lp.w = sw + n0 * KBld + kb0;
-    lp.w_len = clamp_len(((N - n0) * KBld - kb0) * 4);
-    lp.w_off = (uint32_t)(wave * 64 + lane) * (uint32_t)(KBld * 4);
-  } else if constexpr (C::PAIR) {
-    constexpr int kColBlocks = (C::BN + kBlock - 1) / kBlock;
-    lp.w = sw + (n0 / kBlock) * KBld + kb0;
-    lp.w_len = clamp_len(((N / kBlock - n0 / kBlock) * KBld - kb0) * 4);
-    lp.w_off = (uint32_t)(lane % kColBlocks) * (uint32_t)(KBld * 4);
-  }
-  if constexpr (C::PAIR) {  // the second half's rows, each range-checked against its operand's end
-    constexpr int64_t ha = C::WAVES / 2 * C::A_WIN * 8, hb = C::WAVES / 2 * C::B_WIN * 8;
-    lp.a2 = qa + (m0 + ha) * ld + kb0 * BK;
-    lp.b2 = qw + (n0 + hb) * ld + kb0 * BK;
-    lp.a2_len = clamp_len((M - m0 - ha) * ld - kb0 * BK);
-    lp.b2_len = clamp_len((N - n0 - hb) * ld - kb0 * BK);
-  }
+  plan_tile<C>(lp, qa, sa, qw, sw, M, N, m0, n0, ld, kb0, wave, lane);
   // N % 128 == 0 and WN divides 128: a wave's columns are all in or all out
   const bool cols_valid = n0 + wn < N;
 
@@ -689,9 +768,9 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     wait_vm<C::LOADS_PER_STAGE * (C::PAIR ? 2 : 1) * (C::STAGES - 1)>();  // block 0 has landed
     lds_barrier();
     if (loader)
-      k_loop<C, false, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+      k_loop<C, false, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc, lp.t, false, 0);
     else
-      k_loop<C, false, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+      k_loop<C, false, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc, lp.t, false, 0);
   } else {
     ScaleScan<C> scan;
     scan_begin<C>(scan, sa, sw, M, N, m0, n0, wave, KB, lane);
@@ -708,14 +787,14 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     for (int w = 0; w < C::WAVES; ++w) pow2 = pow2 & (verdict[w] != 0u);
     if (pow2) {
       if (loader)
-        k_loop<C, true, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+        k_loop<C, true, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc, lp.t, false, 0);
       else
-        k_loop<C, true, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+        k_loop<C, true, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc, lp.t, false, 0);
     } else {
       if (loader)
-        k_loop<C, false, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+        k_loop<C, false, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc, lp.t, false, 0);
       else
-        k_loop<C, false, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc);
+        k_loop<C, false, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc, lp.t, false, 0);
     }
   }
 
@@ -733,19 +812,7 @@ __device__ __forceinline__ void gemm_tile(const uint8_t* __restrict__ qa, const 
     }
     return;
   }
-#pragma unroll
-  for (int i = 0; i < C::TM; ++i) {
-    const int64_t row = m0 + wm + 16 * i + c16;
-    if (row < M) {
-      uint16_t* yr = y + row * N + n0 + wn + 4 * g;
-#pragma unroll
-      for (int j = 0; j < C::TN; ++j) {
-        const uint32_t lo = (uint32_t)to_bf16_bits(acc[i][j][0]) | ((uint32_t)to_bf16_bits(acc[i][j][1]) << 16);
-        const uint32_t hi = (uint32_t)to_bf16_bits(acc[i][j][2]) | ((uint32_t)to_bf16_bits(acc[i][j][3]) << 16);
-        *reinterpret_cast<uint2*>(yr + 16 * j) = make_uint2(lo, hi);
-      }
-    }
-  }
+  store_tile<C>(acc, y, M, N, m0, n0, wm, wn, g, c16);
 }
 
 // Tile order: blocks are dealt to XCDs round-robin (block b runs on XCD
@@ -837,6 +904,115 @@ __global__ __launch_bounds__(Cfg::NT) void grouped_gemm_kernel(const uint8_t* __
                  rows, N, K, y + row0 * N, m0, (int64_t)n_tile * Cfg::BN, smem, K, 0);
 }
 
+// The expert-grouped GEMM's tile `v` (M-tile v / n_tiles of the concatenated
+// per-expert tile lists, column tile v % n_tiles): its expert and rows
+// (expert_tile's clamped range). False when the tile list is shorter or the
+// tile holds no row. All values uniform.
+struct GroupTile {
+  int e;
+  int64_t row0, rows, m0, n0;
+};
+template <class Cfg>
+__device__ __forceinline__ bool grouped_tile(const int32_t* __restrict__ offsets, int E, int64_t total_M, int n_tiles,
+                                             int64_t v, GroupTile& gt, bool& past_end) {
+  const int t = __builtin_amdgcn_readfirstlane((int)(v / n_tiles));
+  const int n_tile = __builtin_amdgcn_readfirstlane((int)(v % n_tiles));
+  int e = 0, tile = 0;
+  const int found = __builtin_amdgcn_readfirstlane((int)locate_tile<Cfg::BM>(offsets, E, t, e, tile));
+  past_end = !found;  // tile lists are concatenated: no later M-tile exists either
+  if (!found) return false;
+  gt.e = __builtin_amdgcn_readfirstlane(e);
+  if (!expert_tile(__builtin_amdgcn_readfirstlane(offsets[gt.e]), __builtin_amdgcn_readfirstlane(offsets[gt.e + 1]),
+                   total_M, __builtin_amdgcn_readfirstlane(tile), Cfg::BM, gt.row0, gt.rows, gt.m0))
+    return false;
+  gt.n0 = (int64_t)n_tile * Cfg::BN;
+  return true;
+}
+
+// The next live tile at or after v, stepping by `stride` (false: none).
+template <class Cfg>
+__device__ __forceinline__ bool next_grouped_tile(const int32_t* __restrict__ offsets, int E, int64_t total_M,
+                                                  int n_tiles, int64_t vtiles, int64_t stride, int64_t& v,
+                                                  GroupTile& gt) {
+  for (; v < vtiles; v += stride) {
+    bool past_end = false;
+    if (grouped_tile<Cfg>(offsets, E, total_M, n_tiles, v, gt, past_end)) return true;
+    if (past_end) break;
+  }
+  return false;
+}
+
+// Persistent expert-grouped GEMM: workgroup b computes the live tiles
+// b, b + G, b + 2G, ... of the same tile space as grouped_gemm_kernel (G =
+// the grid), one after another, and loads each next tile's first K blocks
+// during the current tile's last steps, so the next tile does not start by
+// waiting for its operands (MoE layers have short K loops: 6 K blocks for a
+// 768-wide down projection, where the start of a tile otherwise took about
+// as long as its K loop). The fold path is used for every tile (no
+// power-of-two scan: it would wait for the prefetched blocks).
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) void grouped_gemm_persistent_kernel(
+    const uint8_t* __restrict__ qa, const float* __restrict__ sa, const uint8_t* __restrict__ qw,
+    const float* __restrict__ sw, const int32_t* __restrict__ offsets, int E, int64_t total_M, int64_t N, int64_t K,
+    uint16_t* __restrict__ y, int n_tiles, int64_t vtiles) {
+  using C = Cfg;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem_generic[Cfg::LDS];
+  lds_u8* smem = (lds_u8*)smem_generic;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = (wave / C::WAVES_N) * C::WM;
+  const int wn = (wave % C::WAVES_N) * C::WN;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int KB = __builtin_amdgcn_readfirstlane((int)(K / BK));
+  const int64_t KBs = K / BK;  // scales per row
+  const int64_t stride = gridDim.x;
+  const bool loader = !C::PAIR || wave < C::WAVES / 2;
+
+  int64_t v = blockIdx.x;
+  GroupTile cur;
+  if (!next_grouped_tile<Cfg>(offsets, E, total_M, n_tiles, vtiles, stride, v, cur)) return;  // uniform
+  LoadPlan<C> lp;
+  plan_tile<C>(lp, qa + cur.row0 * K, sa + cur.row0 * KBs, qw + (int64_t)cur.e * N * K,
+               sw + (int64_t)cur.e * (N / kBlock) * KBs, cur.rows, N, cur.m0, cur.n0, K, 0, wave, lane);
+#pragma unroll
+  for (int b = 0; b < C::STAGES; ++b) refill<C>(smem + b * C::STAGE, lp, b, wave, b < KB);
+  int s0 = 0;
+  for (;;) {
+    // the next tile (its expert lookup overlaps this tile's loads in flight)
+    int64_t vn = v + stride;
+    GroupTile nxt = cur;
+    const bool has_next = next_grouped_tile<Cfg>(offsets, E, total_M, n_tiles, vtiles, stride, vn, nxt);
+    TileBases nb;  // (the current tile's when there is no next: then nothing is loaded from it)
+    plan_bases<C>(nb, qa + nxt.row0 * K, sa + nxt.row0 * KBs, qw + (int64_t)nxt.e * N * K,
+                  sw + (int64_t)nxt.e * (N / kBlock) * KBs, nxt.rows, N, nxt.m0, nxt.n0, K, 0, wave);
+    v4f acc[C::TM][C::TN];
+#pragma unroll
+    for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::TN; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    // Every memory operation of this wave has completed: this tile's first
+    // blocks (the first tile's issued above, later tiles' during the
+    // previous loop) and the previous tile's stores. The vector memory
+    // counter counts stores too, and waves whose columns are past N store
+    // nothing, so a partial count would not tell every wave that its share
+    // of block 0 has landed; waiting for all is exact for every wave (and
+    // measured as fast as an exact count with counted buffer stores).
+    wait_vm0();
+    lds_barrier();
+    if (loader)
+      k_loop<C, false, true>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc, nb, has_next, s0);
+    else
+      k_loop<C, false, false>(smem, smem_generic, lp, wave, KB, wm, wn, g, c16, acc, nb, has_next, s0);
+    if (cur.n0 + wn < N)  // N % 128 == 0 and WN divides 128: a wave's columns are all in or all out
+      store_tile<C>(acc, y + cur.row0 * N, cur.rows, N, cur.m0, cur.n0, wm, wn, g, c16);
+    if (!has_next) break;  // uniform; k_loop waited for every load
+    s0 = (s0 + KB) % C::STAGES;
+    lp.t = nb;
+    cur = nxt;
+    v = vn;
+  }
+}
+
 // Grouped wgrad: dW_e [N][K] = the row-scaled product of rows of A = Q(dY^T)
 // [N][ld] and B = Q(X^T) [K][ld] over expert e's 128-token blocks of the
 // padded token axis (they start at block tiles_before<128>(offsets, e)).
@@ -896,6 +1072,15 @@ fp8blk_status launch_gemm(const uint8_t* qa, const float* sa, const uint8_t* qw,
   return launch_status();
 }
 
+// Workgroups of a tile configuration one CU holds at once (LDS-bound).
+template <class Cfg>
+constexpr int64_t per_cu() {
+  return (160 * 1024) / Cfg::LDS;
+}
+
+// More tiles than the CUs hold at once: the persistent kernel (each
+// workgroup walks its tiles with the next tile's first blocks prefetched);
+// otherwise one workgroup per tile, which keeps the power-of-two scan.
 template <class Cfg>
 fp8blk_status launch_grouped(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                              const int32_t* offsets, int64_t E, int64_t total_M, int64_t N, int64_t K, uint16_t* y,
@@ -903,9 +1088,16 @@ fp8blk_status launch_grouped(const uint8_t* qa, const float* sa, const uint8_t* 
   const int64_t n_tiles = (N + Cfg::BN - 1) / Cfg::BN;
   // upper bound on the number of M-tiles: sum_e ceil(M_e/BM) <= total_M/BM + E
   const int64_t m_tiles = total_M / Cfg::BM + E;
-  if (n_tiles * m_tiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
-  hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3((uint32_t)(n_tiles * m_tiles)), dim3(Cfg::NT), 0, stream, qa,
-                     sa, qw, sw, offsets, (int)E, total_M, N, K, y, (int)n_tiles);
+  const int64_t vtiles = n_tiles * m_tiles;
+  if (vtiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
+  const int64_t slots = kCUs * per_cu<Cfg>();
+  if (vtiles > slots) {
+    hipLaunchKernelGGL(grouped_gemm_persistent_kernel<Cfg>, dim3((uint32_t)slots), dim3(Cfg::NT), 0, stream, qa, sa,
+                       qw, sw, offsets, (int)E, total_M, N, K, y, (int)n_tiles, vtiles);
+  } else {
+    hipLaunchKernelGGL(grouped_gemm_kernel<Cfg>, dim3((uint32_t)vtiles), dim3(Cfg::NT), 0, stream, qa, sa, qw, sw,
+                       offsets, (int)E, total_M, N, K, y, (int)n_tiles);
+  }
   return launch_status();
 }
 
