@@ -88,6 +88,8 @@ def parse():
                    help="after timing, run a 1 GiB device copy (counter calibration)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 --pmc CSVs into profiles/traffic.json and exit")
+    p.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                   help="print a per-kernel markdown summary of rocprofv3 counter_collection.csv files")
     return p.parse_args()
 
 
@@ -642,17 +644,21 @@ def time_workload(fb, workload, dev, steps, warmup, cold_reps, traffic_db):
     events = {}
     for _ in range(steps):
         step(fb, layers, events)
-    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    cold = {L["name"]: [] for L in layers}
+    flush = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.zeros((), dtype=torch.int64, device=dev)
+    flushes = {"write": flush.zero_,  # leaves the caches full of dirty lines
+               "read": lambda: sink.copy_(flush.view(torch.int64).sum())}  # clean lines
+    cold = {(L["name"], kind): [] for L in layers for kind in flushes}
     for _ in range(cold_reps):
         for L in layers:
-            flush.zero_()
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            run_gemm(fb, L)
-            b.record(stream)
-            cold[L["name"]].append((a, b))
+            for kind, fl in flushes.items():
+                fl()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                run_gemm(fb, L)
+                b.record(stream)
+                cold[(L["name"], kind)].append((a, b))
     torch.cuda.synchronize()
     nl = len(layers)
     ms = {k: [a.elapsed_time(b) for a, b in v] for k, v in events.items()}
@@ -662,7 +668,9 @@ def time_workload(fb, workload, dev, steps, warmup, cold_reps, traffic_db):
     hot_total = cold_total = 0.0
     for i, L in enumerate(layers):
         hot = percentiles(ms["gemm"][i::nl])
-        cl = percentiles([a.elapsed_time(b) for a, b in cold[L["name"]]])
+        cold_pct = {key[1]: percentiles([a.elapsed_time(b) for a, b in v])
+                    for key, v in cold.items() if key[0] == L["name"]}
+        cl = cold_pct["write"]
         hot_total += hot["median"]
         cold_total += cl["median"]
         ab = gemm_alg_bytes(L)
@@ -672,6 +680,7 @@ def time_workload(fb, workload, dev, steps, warmup, cold_reps, traffic_db):
                                 "gemm_us_p10_p90": [round(hot["p10"] * 1e3, 1), round(hot["p90"] * 1e3, 1)],
                                 "gemm_cold_us": round(cl["median"] * 1e3, 1),
                                 "gemm_cold_us_p10_p90": [round(cl["p10"] * 1e3, 1), round(cl["p90"] * 1e3, 1)],
+                                "gemm_cold_read_flush_us": round(cold_pct["read"]["median"] * 1e3, 1),
                                 "roofline_us": round(roof_us, 2),
                                 "frac_of_roofline_cold": round(roof_us / (cl["median"] * 1e3), 4)}
     ridge = FP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
@@ -692,6 +701,9 @@ def time_workload(fb, workload, dev, steps, warmup, cold_reps, traffic_db):
         "gemm_tflops_cold": round(flops / (cold_total * 1e-3) / 1e12, 1),
         "roofline": roofline(flops / nl, alg / nl, avg_ms, traffic),
         "timing": "cold (1 GiB written before each launch)" if hbm_bound else "in step (eager)",
+        "cold_note": ("gemm_cold_us: a 1 GiB write before each launch (the last-level cache then holds "
+                      "dirty lines, written back while the weights stream in); gemm_cold_read_flush_us: a "
+                      "1 GiB read instead (clean lines); HIP events, launch overhead included"),
         "per_layer": per_layer,
         "quant_act": {"gbs": round(kb["quant_act"] / (qa_ms * 1e-3) / 1e9, 1),
                       "frac": round(kb["quant_act"] / (qa_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -903,8 +915,95 @@ def summarize_traffic(fetch_csv, write_csv):
     return rec
 
 
+def short_kernel_name(name):
+    """A kernel name without its namespace, return type and argument list,
+    template arguments kept (tile configurations tell the GEMMs apart)."""
+    name = name.replace("void ", "").replace("fp8blk::(anonymous namespace)::", "")
+    depth, out = 0, []
+    for ch in name:
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+# CUs and SIMDs of the MI355X; GRBM_GUI_ACTIVE counts GPU-busy cycles once per
+# XCD, so cycles = GRBM_GUI_ACTIVE / 8.
+N_XCD, N_CU, N_SIMD = 8, 256, 4
+
+
+def summarize_counters(paths):
+    """Markdown summary of rocprofv3 counter passes: per kernel and grid size,
+    the mean per dispatch of every counter collected, the mean duration, and
+    the ratios derived from them where their inputs were collected:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles * CUs * SIMDs);
+    MFMA FP8 FLOPs = SQ_INSTS_VALU_MFMA_MOPS_F8 * 512 and their rate;
+    clock = cycles / duration; LDS-wait share = SQ_WAIT_INST_LDS /
+    SQ_WAVE_CYCLES; bank-conflict cycles per LDS instruction; TA busy =
+    TA_BUSY_avr / cycles; TA stalled by TCP = TA_ADDR_STALLED_BY_TC_CYCLES_sum
+    / (cycles * CUs); L2 hit rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)."""
+    import csv
+    import statistics
+    groups = {}   # (kernel, grid) -> {dispatch key -> {counter: value, "_ns": duration}}
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (short_kernel_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+                d = groups.setdefault(key, {}).setdefault((path, r["Dispatch_Id"]), {})
+                d[r["Counter_Name"]] = float(r["Counter_Value"])
+                if r.get("End_Timestamp") and r.get("Start_Timestamp"):
+                    d["_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    lines = []
+    for (kernel, grid), disp in sorted(groups.items(), key=lambda kv: -sum(d.get("_ns", 0) for d in kv[1].values())):
+        counters = sorted({c for d in disp.values() for c in d if c != "_ns"})
+        mean = {c: statistics.mean(d[c] for d in disp.values() if c in d) for c in counters}
+        ns = [d["_ns"] for d in disp.values() if "_ns" in d]
+        dur = statistics.mean(ns) if ns else None
+        row = ["`%s`" % kernel, str(grid // 64 if grid % 64 == 0 else grid), str(len(disp)),
+               "%.1f" % (dur / 1e3) if dur else "-"]
+        derived = []
+        cycles = mean.get("GRBM_GUI_ACTIVE", 0) / N_XCD
+        if cycles and dur:
+            # the GUI-active window also covers the dispatch's set-up and
+            # drain: for short kernels it is longer than the kernel itself
+            ghz = cycles / dur
+            derived.append("clock %.2f GHz" % ghz if ghz <= 2.5 else "GUI window %.1fx the kernel" % (ghz / 2.4))
+        if cycles and "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            derived.append("MFMA busy %.1f%%" % (100 * mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_CU * N_SIMD)))
+        if mean.get("SQ_INSTS_VALU_MFMA_MOPS_F8"):
+            fl = mean["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512
+            derived.append("FP8 MFMA %.3g GFLOP" % (fl / 1e9) + (" = %.0f TFLOP/s" % (fl / dur / 1e3) if dur else ""))
+        if cycles and mean.get("SQ_WAVE_CYCLES"):
+            derived.append("%.1f waves per CU" % (mean["SQ_WAVE_CYCLES"] / (cycles * N_CU)))
+        for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"):
+            if mean.get("SQ_WAVE_CYCLES") and c in mean:
+                derived.append("%s %.1f%%" % (c, 100 * mean[c] / mean["SQ_WAVE_CYCLES"]))
+        if mean.get("SQ_WAVE_CYCLES") and mean.get("SQ_WAIT_INST_LDS"):
+            derived.append("LDS wait %.1f%% of wave cycles" % (100 * mean["SQ_WAIT_INST_LDS"] / mean["SQ_WAVE_CYCLES"]))
+        if mean.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in mean and mean.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 1):
+            derived.append("%.2f conflict cycles per LDS instruction"
+                           % (mean["SQ_LDS_BANK_CONFLICT"] / mean["SQ_INSTS_LDS"]))
+        if cycles and "TA_BUSY_avr" in mean:
+            derived.append("TA busy %.1f%%" % (100 * mean["TA_BUSY_avr"] / cycles))
+        if cycles and "TA_ADDR_STALLED_BY_TC_CYCLES_sum" in mean:
+            derived.append("TA stalled by TCP %.1f%%" % (100 * mean["TA_ADDR_STALLED_BY_TC_CYCLES_sum"] / (cycles * N_CU)))
+        if mean.get("TCC_HIT_sum", 0) + mean.get("TCC_MISS_sum", 0) > 0:
+            derived.append("L2 hit %.1f%%" % (100 * mean["TCC_HIT_sum"] / (mean["TCC_HIT_sum"] + mean["TCC_MISS_sum"])))
+        row.append("; ".join(derived) or "-")
+        row.append(", ".join("%s %.4g" % (c, v) for c, v in mean.items()))
+        lines.append("| " + " | ".join(row) + " |")
+    head = ["| kernel | workgroups | dispatches | mean us | derived | counters (mean per dispatch) |",
+            "|---|---|---|---|---|---|"]
+    return "\n".join(head + lines)
+
+
 def main():
     args = parse()
+    if args.summarize_counters:
+        print(summarize_counters(args.summarize_counters))
+        return
     if args.summarize_traffic:
         rec = summarize_traffic(*args.summarize_traffic)
         db = {}
