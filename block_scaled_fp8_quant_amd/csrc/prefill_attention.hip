@@ -62,6 +62,9 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kD + ((chu
 #ifndef FP8BLK_DEBUG_BARRIERS
 #define FP8BLK_DEBUG_BARRIERS 0
 #endif
+#ifndef FP8BLK_PA_PSPLIT
+#define FP8BLK_PA_PSPLIT 1
+#endif
 __device__ __forceinline__ void debug_stage_sync() {
   if constexpr (FP8BLK_DEBUG_BARRIERS != 0) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -118,6 +121,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
   const int64_t p_last = L - n + (i0 + BQ < n ? i0 + BQ : n) - 1;
   const int64_t t_end = p_last + 1 < L ? p_last + 1 : L;  // tokens [0, t_end) are needed
   const int ntiles = t_end > 0 ? (int)((t_end + kTile - 1) / kTile) : 0;
+  // tiles before the block's first position need no causal mask (every token
+  // of them is at most that position, hence below L)
+  const int64_t p_first = L - n + i0;
   const float qs = *q_scale, ks = *k_scale, vs = *v_scale;
 
   // this lane's two score rows (one per 16-row tile qt): row 32*wave + 16qt + c16
@@ -215,23 +221,29 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 
     // S^T: lane (c, g) gets s[u][qt][r] = score of token t0 + 16u + 4g + r, row 16qt + c
     float s[4][2][4];
+    auto scores = [&](bool masked) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int krow = 16 * u + c16;
-      const u32x4 lo = *reinterpret_cast<const u32x4*>(K + swz(krow, g));
-      const u32x4 hi = *reinterpret_cast<const u32x4*>(K + swz(krow, g + 4));
-      const v8i kfrag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      for (int u = 0; u < 4; ++u) {
+        const int krow = 16 * u + c16;
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(K + swz(krow, g));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(K + swz(krow, g + 4));
+        const v8i kfrag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kfrag, qfrag[qt], v4f{0.f, 0.f, 0.f, 0.f},
-                                                                       0, 0, 0, 127, 0, 127);
+        for (int qt = 0; qt < 2; ++qt) {
+          const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kfrag, qfrag[qt], v4f{0.f, 0.f, 0.f, 0.f},
+                                                                         0, 0, 0, 127, 0, 127);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int64_t t = t0 + 16 * u + 4 * g + r;
-          s[u][qt][r] = (t <= pos[qt] && t < L) ? d[r] * s2scale : -INFINITY;
+          for (int r = 0; r < 4; ++r) {
+            const int64_t t = t0 + 16 * u + 4 * g + r;
+            s[u][qt][r] = !masked || (t <= pos[qt] && t < L) ? d[r] * s2scale : -INFINITY;
+          }
         }
       }
-    }
+    };
+    if (t0 + kTile - 1 <= p_first)  // uniform
+      scores(false);
+    else
+      scores(true);
     // online softmax per row; p replaces s
     float alpha[2];
 #pragma unroll
@@ -255,8 +267,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
         }
       l_run[qt] = l_run[qt] * alpha[qt] + ps;  // this lane's share; the four lanes of a row add up at the end
       m_run[qt] = mn;
+      // alpha is exactly 1 where the running maximum did not change; a wave
+      // whose rows all kept theirs skips the rescale (bit for bit the same)
+      if (__builtin_amdgcn_ballot_w64(alpha[qt] != 1.0f) != 0) {  // uniform
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[qt][dt] *= alpha[qt];
+        for (int dt = 0; dt < 8; ++dt) acc[qt][dt] *= alpha[qt];
+      }
     }
     // O^T += V^T P^T over two 32-token chunks. Contraction slot (g, j) of
     // chunk c is token 32c + 16(j/4) + 4g + j%4: the probabilities a lane
@@ -273,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
           const float p = s[2 * c + j / 4][qt][j % 4];
           const _Float16 h = (_Float16)p;
           ph[qt][j] = h;
-          pl[qt][j] = (_Float16)(p - (float)h);
+          pl[qt][j] = FP8BLK_PA_PSPLIT ? (_Float16)(p - (float)h) : (_Float16)0.f;
         }
       const int j = c16 >> 1, half = c16 & 1;
       const int vrow = 32 * c + 16 * (j / 4) + 4 * g + (j % 4);
@@ -285,7 +301,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[qt], acc[qt][dt], 0, 0, 0);
-          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt], acc[qt][dt], 0, 0, 0);
+          if constexpr (FP8BLK_PA_PSPLIT)
+            acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt], acc[qt][dt], 0, 0, 0);
         }
       }
     }
