@@ -62,9 +62,6 @@ __device__ __forceinline__ int swz(int row, int chunk) { return row * kD + ((chu
 #ifndef FP8BLK_DEBUG_BARRIERS
 #define FP8BLK_DEBUG_BARRIERS 0
 #endif
-#ifndef FP8BLK_PA_PSPLIT
-#define FP8BLK_PA_PSPLIT 1
-#endif
 __device__ __forceinline__ void debug_stage_sync() {
   if constexpr (FP8BLK_DEBUG_BARRIERS != 0) {
     __builtin_amdgcn_s_waitcnt(0);
@@ -289,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
           const float p = s[2 * c + j / 4][qt][j % 4];
           const _Float16 h = (_Float16)p;
           ph[qt][j] = h;
-          pl[qt][j] = FP8BLK_PA_PSPLIT ? (_Float16)(p - (float)h) : (_Float16)0.f;
+          pl[qt][j] = (_Float16)(p - (float)h);
         }
       const int j = c16 >> 1, half = c16 & 1;
       const int vrow = 32 * c + 16 * (j / 4) + 4 * g + (j % 4);
@@ -301,8 +298,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[qt], acc[qt][dt], 0, 0, 0);
-          if constexpr (FP8BLK_PA_PSPLIT)
-            acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt], acc[qt][dt], 0, 0, 0);
+          acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl[qt], acc[qt][dt], 0, 0, 0);
         }
       }
     }
