@@ -59,9 +59,6 @@ HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 GEMM_KERNELS = ("gemm_kernel", "grouped_gemm_kernel")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # kernels whose counter traffic is recorded (substrings of the kernel names)
-TRAFFIC_KERNELS = ("gemm_kernel", "quant_act_kernel", "quant_weight_kernel", "rmsnorm_quant_act_rows_kernel",
-                   "silu_mul_quant_act_kernel", "qkv_amax_kernel", "kv_cache_write_kernel")
-
 
 def parse():
     p = argparse.ArgumentParser()
@@ -88,25 +85,28 @@ def parse():
                    help="after timing, run a 1 GiB device copy (counter calibration)")
     p.add_argument("--summarize-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                    help="turn two rocprofv3 --pmc CSVs into profiles/traffic.json and exit")
+    p.add_argument("--summarize-trace", metavar="STATS_CSV",
+                   help="print a markdown table of a rocprofv3 --stats kernel_stats.csv")
     p.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                    help="print a per-kernel markdown summary of rocprofv3 counter_collection.csv files")
     return p.parse_args()
 
 
-# the sources each recorded kernel is built from: a counter record stays
-# valid while these files are unchanged
-KERNEL_SOURCES = {"gemm_kernel": ("gemm.hip", "common.h"),
-                  "qkv_amax_kernel": ("kv_cache.hip", "quant_common.h", "common.h"),
-                  "kv_cache_write_kernel": ("kv_cache.hip", "quant_common.h", "common.h")}
-QUANT_SOURCES = ("quant.hip", "quant_common.h", "common.h")
-
-
-ATTENTION_SOURCES = ("attention.hip", "quant_common.h", "common.h")
+# the sources each recorded kernel is built from (by kernel-name substring,
+# first match): a counter record stays valid while these files are unchanged
+KERNEL_SOURCES = (("prefill_attention", ("prefill_attention.hip", "quant_common.h", "common.h")),
+                  ("attention", ("attention.hip", "quant_common.h", "common.h")),
+                  ("kv_", ("kv_cache.hip", "quant_common.h", "common.h")),
+                  ("qkv_amax", ("kv_cache.hip", "quant_common.h", "common.h")),
+                  ("gemm", ("gemm.hip", "ranges.h", "common.h")),
+                  ("rowscaled", ("gemm.hip", "ranges.h", "common.h")),
+                  ("splitk", ("gemm.hip", "ranges.h", "common.h")))
+QUANT_SOURCES = ("quant.hip", "quant_common.h", "ranges.h", "common.h")
 
 
 def source_hash(kernel="gemm_kernel"):
     h = hashlib.sha256()
-    names = ATTENTION_SOURCES if "decode_attention" in kernel else KERNEL_SOURCES.get(kernel, QUANT_SOURCES)
+    names = next((srcs for key, srcs in KERNEL_SOURCES if key in kernel), QUANT_SOURCES)
     for name in names:
         with open(os.path.join(ROOT, "block_scaled_fp8_quant_amd", "csrc", name), "rb") as f:
             h.update(f.read())
@@ -687,9 +687,7 @@ def time_workload(fb, workload, dev, steps, warmup, cold_reps, traffic_db):
     hbm_bound = flops / alg < ridge
     avg_ms = (cold_total if hbm_bound else hot_total) / nl
     rec = (traffic_db or {}).get(workload) or {}
-    kern = "grouped_gemm_kernel" if workload == "moe" else "gemm_kernel"
-    krec = rec.get("kernels", {}).get(kern, {})
-    traffic = krec.get("bytes_per_launch") if krec.get("source_hash") == source_hash("gemm_kernel") else None
+    traffic = rec.get("gemm_bytes_per_launch") if rec.get("source_hash") == source_hash() else None
     kb = kernel_bytes(layers)
     qa_ms = sum(ms["quant_act"]) / steps
     qw_ms = sum(ms["quant_weight"]) / steps
@@ -852,9 +850,17 @@ def copy_yardstick():
     torch.cuda.synchronize()
 
 
+# GEMM-family kernels: a GEMM call is one dispatch of a primary kernel (the
+# split-K path adds its reduction to the same call)
+GEMM_PRIMARY = ("gemm_kernel<", "gemm_splitk_kernel", "grouped_gemm_kernel", "grouped_gemm_persistent_kernel")
+GEMM_FAMILY = GEMM_PRIMARY + ("splitk_reduce_kernel",)
+
+
 def summarize_traffic(fetch_csv, write_csv):
-    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the GEMM kernel, scaled
-    by what the same counters read for the 1 GiB copy, into bytes."""
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel of a
+    counter pass, scaled by what the same counters read for the 1 GiB copy
+    into bytes; the GEMM's bytes per call are the GEMM family's bytes over
+    the number of GEMM calls."""
     import csv
     import statistics
 
@@ -869,47 +875,44 @@ def summarize_traffic(fetch_csv, write_csv):
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
     write = per_kernel(write_csv, "WRITE_SIZE")
-
-    def pick(d, key):
-        for name, v in d.items():
-            if key in name:
-                return v
-        raise KeyError(key)
-
-    copy_key = "copyBuffer"
-    c_f, c_w = max(pick(fetch, copy_key)), max(pick(write, copy_key))
+    copy_f = [v for n, v in fetch.items() if "copyBuffer" in n]
+    copy_w = [v for n, v in write.items() if "copyBuffer" in n]
+    c_f, c_w = max(copy_f[0]), max(copy_w[0])
     f_scale = COPY_BYTES / (c_f * 1024.0)
     w_scale = COPY_BYTES / (c_w * 1024.0)
     kernels = {}
-    for key in TRAFFIC_KERNELS:
-        try:
-            kf, kw = pick(fetch, key), pick(write, key)
-        except KeyError:
-            continue
-        kernels[key] = {"source_hash": source_hash(key), "fetch_kib_per_dispatch": statistics.mean(kf),
-                        "write_kib_per_dispatch": statistics.mean(kw), "dispatches": len(kf),
-                        "bytes_per_launch": statistics.mean(kf) * 1024 * f_scale
-                        + statistics.mean(kw) * 1024 * w_scale}
-    # decode attention: one record per instantiation (head-group size, split),
-    # e.g. "decode_attention_kernel<4, false>", and the merge kernel
+    gemm_bytes, gemm_calls = 0.0, 0
     for name in fetch:
-        if "decode_attention" not in name or name not in write:
+        if name not in write or "copyBuffer" in name or name.startswith("void at::") or "at::native" in name:
             continue
-        key = name.replace("void ", "").replace("fp8blk::(anonymous namespace)::", "").split("(")[0]
+        key = short_kernel_name(name)
         kf, kw = fetch[name], write[name]
-        kernels[key] = {"source_hash": source_hash(key), "fetch_kib_per_dispatch": statistics.mean(kf),
+        src = key.split("<")[0]
+        b = statistics.mean(kf) * 1024 * f_scale + statistics.mean(kw) * 1024 * w_scale
+        kernels[key] = {"source_hash": source_hash(src), "fetch_kib_per_dispatch": statistics.mean(kf),
                         "write_kib_per_dispatch": statistics.mean(kw), "dispatches": len(kf),
-                        "bytes_per_launch": statistics.mean(kf) * 1024 * f_scale
-                        + statistics.mean(kw) * 1024 * w_scale}
-    g = kernels["gemm_kernel"]
+                        "bytes_per_launch": b}
+        if any(k in key for k in GEMM_FAMILY):
+            gemm_bytes += b * len(kf)
+            if any(k in key for k in GEMM_PRIMARY):
+                gemm_calls += len(kf)
+    # records read by the bench: the GEMM call and the kernels it names
+    # without template arguments
+    for base in ("quant_act_kernel", "quant_weight_kernel", "rmsnorm_quant_act_rows_kernel",
+                 "silu_mul_quant_act_kernel", "qkv_amax_kernel", "kv_cache_write_kernel",
+                 "decode_attention_combine_kernel"):
+        recs = [v for k, v in kernels.items() if k.split("<")[0] == base]
+        if recs and base not in kernels:
+            n = sum(r["dispatches"] for r in recs)
+            kernels[base] = {"source_hash": recs[0]["source_hash"], "dispatches": n,
+                             "bytes_per_launch": sum(r["bytes_per_launch"] * r["dispatches"] for r in recs) / n,
+                             "note": "mean over its instantiations"}
     rec = {
         "source_hash": source_hash(),
-        "gemm_fetch_kib_per_dispatch": g["fetch_kib_per_dispatch"],
-        "gemm_write_kib_per_dispatch": g["write_kib_per_dispatch"],
-        "gemm_dispatches": g["dispatches"],
+        "gemm_calls": gemm_calls,
         "copy_fetch_kib": c_f, "copy_write_kib": c_w, "copy_bytes": COPY_BYTES,
         "fetch_scale": f_scale, "write_scale": w_scale,
-        "gemm_bytes_per_launch": g["bytes_per_launch"],
+        "gemm_bytes_per_launch": gemm_bytes / gemm_calls if gemm_calls else None,
         "kernels": kernels,
     }
     return rec
@@ -975,8 +978,6 @@ def summarize_counters(paths):
         if mean.get("SQ_INSTS_VALU_MFMA_MOPS_F8"):
             fl = mean["SQ_INSTS_VALU_MFMA_MOPS_F8"] * 512
             derived.append("FP8 MFMA %.3g GFLOP" % (fl / 1e9) + (" = %.0f TFLOP/s" % (fl / dur / 1e3) if dur else ""))
-        if cycles and mean.get("SQ_WAVE_CYCLES"):
-            derived.append("%.1f waves per CU" % (mean["SQ_WAVE_CYCLES"] / (cycles * N_CU)))
         for c in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS"):
             if mean.get("SQ_WAVE_CYCLES") and c in mean:
                 derived.append("%s %.1f%%" % (c, 100 * mean[c] / mean["SQ_WAVE_CYCLES"]))
@@ -999,8 +1000,35 @@ def summarize_counters(paths):
     return "\n".join(head + lines)
 
 
+def summarize_trace(stats_csv):
+    """Markdown table of a rocprofv3 kernel_stats.csv: one row per kernel
+    (template arguments kept; torch's own kernels folded into one row)."""
+    import csv
+    agg = {}
+    with open(stats_csv) as f:
+        for r in csv.DictReader(f):
+            name = r["Name"]
+            key = "torch kernels (fills, copies, random numbers)" if "at::native" in name else \
+                "`%s`" % short_kernel_name(name)
+            a = agg.setdefault(key, {"calls": 0, "tot": 0.0, "min": float("inf"), "max": 0.0})
+            a["calls"] += int(r["Calls"])
+            a["tot"] += float(r["TotalDurationNs"])
+            a["min"] = min(a["min"], float(r["MinNs"]))
+            a["max"] = max(a["max"], float(r["MaxNs"]))
+    total = sum(a["tot"] for a in agg.values())
+    out = ["| kernel | calls | total ms | avg us | min us | max us | share % |", "|---|---|---|---|---|---|---|"]
+    for k, a in sorted(agg.items(), key=lambda kv: -kv[1]["tot"]):
+        out.append("| %s | %d | %.3f | %.1f | %.1f | %.1f | %.2f |" % (
+            k, a["calls"], a["tot"] / 1e6, a["tot"] / a["calls"] / 1e3, a["min"] / 1e3, a["max"] / 1e3,
+            100 * a["tot"] / total))
+    return "\n".join(out)
+
+
 def main():
     args = parse()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace))
+        return
     if args.summarize_counters:
         print(summarize_counters(args.summarize_counters))
         return
