@@ -1078,9 +1078,10 @@ constexpr int64_t per_cu() {
   return (160 * 1024) / Cfg::LDS;
 }
 
-// More tiles than the CUs hold at once: the persistent kernel (each
-// workgroup walks its tiles with the next tile's first blocks prefetched);
-// otherwise one workgroup per tile, which keeps the power-of-two scan.
+// More tiles than the CUs hold at once (and at least STAGES K blocks): the
+// persistent kernel (each workgroup walks its tiles with the next tile's
+// first blocks prefetched); otherwise one workgroup per tile, which keeps
+// the power-of-two scan.
 template <class Cfg>
 fp8blk_status launch_grouped(const uint8_t* qa, const float* sa, const uint8_t* qw, const float* sw,
                              const int32_t* offsets, int64_t E, int64_t total_M, int64_t N, int64_t K, uint16_t* y,
@@ -1091,7 +1092,9 @@ fp8blk_status launch_grouped(const uint8_t* qa, const float* sa, const uint8_t* 
   const int64_t vtiles = n_tiles * m_tiles;
   if (vtiles > (1 << 24)) return FP8BLK_ERR_SHAPE;
   const int64_t slots = kCUs * per_cu<Cfg>();
-  if (vtiles > slots) {
+  // the persistent kernel loads a next tile's first STAGES blocks during the
+  // current tile's last STAGES steps: it needs at least STAGES K blocks
+  if (vtiles > slots && K / BK >= Cfg::STAGES) {
     hipLaunchKernelGGL(grouped_gemm_persistent_kernel<Cfg>, dim3((uint32_t)slots), dim3(Cfg::NT), 0, stream, qa, sa,
                        qw, sw, offsets, (int)E, total_M, N, K, y, (int)n_tiles, vtiles);
   } else {

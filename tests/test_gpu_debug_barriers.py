@@ -72,8 +72,11 @@ def test_split_k(dbg):
     same(y0, y1, "split-K gemm")
 
 
+# the last two run the persistent kernel (more tiles than the CUs hold at
+# once): 128x128 tiles at K = 512, 256x256 tiles at K = 2048
 @pytest.mark.parametrize("tokens,experts,topk,hidden,n", [(64, 8, 2, 256, 512), (600, 4, 2, 2048, 512),
-                                                          (300, 16, 4, 512, 256)])
+                                                          (300, 16, 4, 512, 256), (2048, 16, 2, 512, 2048),
+                                                          (2048, 8, 2, 2048, 4096)])
 def test_grouped(dbg, tokens, experts, topk, hidden, n):
     x, w, off = synth.small_moe_inputs(1, tokens=tokens, hidden=hidden, experts=experts, topk=topk, n=n)
     qa, sa = fb.quant_act(x.to(DEV))

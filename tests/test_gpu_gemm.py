@@ -184,6 +184,41 @@ def test_grouped_256_row_tiles_ragged_experts(fp8blk_lib):
     _grouped_check(x, w, off)
 
 
+def _counts_inputs(counts, k, n, seed):
+    off = torch.tensor(np.concatenate([[0], np.cumsum(counts)]), dtype=torch.int32)
+    g = synth.generator(seed)
+    x = synth.activation(int(off[-1]), k, g, 0.01, 50.0)
+    w = synth.weight(len(counts) * n, k, g).reshape(len(counts), n, k)
+    return x, w, off
+
+
+@pytest.mark.parametrize("k", [128, 256, 384, 1024])
+def test_grouped_persistent_128_row_tiles(fp8blk_lib, k):
+    """More 128x128 tiles than the CUs hold at once (24 row tiles x 48 column
+    tiles): the persistent kernel, each workgroup walking two or three tiles
+    with the next tile's first K blocks loaded during the current tile's last
+    steps (K = 256: every step of a tile loads the next one's; K = 384 and
+    1024: longer). K = 128 has fewer K blocks than stages and runs one
+    workgroup per tile instead."""
+    counts = [600, 0, 256, 130, 1, 511, 300, 250]
+    print("persistent 128x128 K=%d" % k, flush=True)
+    x, w, off = _counts_inputs(counts, k, 6144, 12)
+    _grouped_check(x, w, off)
+
+
+def test_grouped_persistent_256_row_tiles_sampled(fp8blk_lib):
+    """The persistent kernel on 256x256 tiles (experts averaging >= 256 rows,
+    K = 2048; 14 row tiles x 24 column tiles > 256 CUs): the first and last
+    rows of every expert and random rows, all columns."""
+    counts = [600, 0, 256, 130, 1, 511, 300]
+    x, w, off = _counts_inputs(counts, 2048, 6144, 13)
+    offs = off.numpy().astype(np.int64)
+    edges = [r for e in range(len(counts)) if counts[e] for r in (offs[e], offs[e + 1] - 1, offs[e] + 255)
+             if offs[e] <= r < offs[e + 1]]
+    rnd = torch.randint(0, int(offs[-1]), (24,), generator=synth.generator(14)).tolist()
+    _grouped_check(x, w, off, rows=np.array(sorted(set(edges) | set(rnd)), dtype=np.int64))
+
+
 def test_grouped_single_expert_equals_gemm(fp8blk_lib):
     x, w = synth.linear_inputs("tiny", 0)
     qa, sa = fb.quant_act(x.to(DEV))
