@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         kr[h] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kp + 16 * h);
-        vr[h] = __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(vp + 16 * h));
+        vr[h] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(vp + 16 * h);
       }
     }
   };
