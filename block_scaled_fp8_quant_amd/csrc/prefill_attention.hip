@@ -41,6 +41,7 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v2i lds_v2i;
@@ -155,6 +156,18 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
     }
   }
   const float s2scale = qs * ks * sm_scale * kLog2e;
+  // Tiles that need no causal mask keep the raw MFMA dot products and fold
+  // the score scale into the exponent's argument (one FMA per score instead
+  // of a multiply and a subtraction); with a positive scale the row maximum
+  // of the raw products times the scale is the maximum of the scaled scores
+  // exactly (rounding is monotonic). Other tiles scale each score and use
+  // the same FMA with a multiplier of one, which is exact. `one` is opaque
+  // to the compiler so that those FMAs, and the ones splitting the
+  // probabilities below, stay FMAs (v_fma_mix for the fp16 operand) instead
+  // of being folded into subtractions.
+  const bool s2pos = s2scale > 0.f;
+  float one = 1.0f;
+  asm volatile("" : "+s"(one));
 
   // K/V tile loads: thread tid takes token tid/4 of the tile, bytes 32*(tid%4)..+31
   const int ltok = tid >> 2, lpart = tid & 3;
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 
     // S^T: lane (c, g) gets s[u][qt][r] = score of token t0 + 16u + 4g + r, row 16qt + c
     float s[4][2][4];
-    auto scores = [&](bool masked) {
+    auto scores = [&](bool masked, bool raw) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int krow = 16 * u + c16;
@@ -232,15 +245,20 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int64_t t = t0 + 16 * u + 4 * g + r;
-            s[u][qt][r] = !masked || (t <= pos[qt] && t < L) ? d[r] * s2scale : -INFINITY;
+            s[u][qt][r] = raw ? d[r] : !masked || (t <= pos[qt] && t < L) ? d[r] * s2scale : -INFINITY;
           }
         }
       }
     };
-    if (t0 + kTile - 1 <= p_first)  // uniform
-      scores(false);
+    const bool unmasked = t0 + kTile - 1 <= p_first;  // uniform
+    const bool raw = unmasked && s2pos;
+    if (raw)
+      scores(false, true);
+    else if (unmasked)
+      scores(false, false);
     else
-      scores(true);
+      scores(true, false);
+    const float mulv = raw ? s2scale : one;  // s * mulv is the scaled score
     // online softmax per row; p replaces s
     float alpha[2];
 #pragma unroll
@@ -250,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[u][qt][r]);
-      mt = cross4_max(mt);
+      mt = cross4_max(mt) * mulv;
       const float mn = fmaxf(m_run[qt], mt);
       const float ms = mn == -INFINITY ? 0.f : mn;  // no token yet: keep exp2 finite
       alpha[qt] = __builtin_amdgcn_exp2f(m_run[qt] - ms);
@@ -259,7 +277,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          s[u][qt][r] = __builtin_amdgcn_exp2f(s[u][qt][r] - ms);
+          s[u][qt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[u][qt][r], mulv, -ms));
           ps += s[u][qt][r];
         }
       l_run[qt] = l_run[qt] * alpha[qt] + ps;  // this lane's share; the four lanes of a row add up at the end
@@ -278,15 +296,21 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
     // j's 16 values of the dim tile).
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
+      // head = fp16(p) two at a time; remainder = fp16(p - head), the
+      // difference exact in the FMA (v_fma_mix_f32 reads the fp16 head)
       v8h ph[2], pl[2];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p = s[2 * c + j / 4][qt][j % 4];
-          const _Float16 h = (_Float16)p;
-          ph[qt][j] = h;
-          pl[qt][j] = (_Float16)(p - (float)h);
+        for (int j = 0; j < 8; j += 2) {
+          const float p0 = s[2 * c + j / 4][qt][j % 4], p1 = s[2 * c + j / 4][qt][j % 4 + 1];
+          const v2h h = __builtin_convertvector(v2f{p0, p1}, v2h);
+          const v2h l = __builtin_convertvector(
+              v2f{__builtin_fmaf(-(float)h[0], one, p0), __builtin_fmaf(-(float)h[1], one, p1)}, v2h);
+          ph[qt][j] = h[0];
+          ph[qt][j + 1] = h[1];
+          pl[qt][j] = l[0];
+          pl[qt][j + 1] = l[1];
         }
       const int j = c16 >> 1, half = c16 & 1;
       const int vrow = 32 * c + 16 * (j / 4) + 4 * g + (j % 4);
