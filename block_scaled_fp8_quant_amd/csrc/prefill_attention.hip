@@ -29,9 +29,12 @@
 //     each probability split into an fp16 head and an fp16 remainder (two
 //     MFMAs, ~2^-22 relative: the probabilities stay unquantized to within
 //     fp32 accuracy), source 0 = V^T: the transpose of the tile's V rows read
-//     from LDS with ds_read_b64_tr_b8, converted to fp16 (exact for E4M3).
-// LDS rows are 128 bytes with 16-byte chunk c of row r stored at c ^ key(r),
-// so the 16-row fragment reads spread over the banks.
+//     from LDS with ds_read_b64_tr_b16. V is converted to fp16 (exact for
+//     E4M3) once, by the thread that stores it to LDS, not by every wave.
+// K rows in LDS are 128 bytes with 16-byte chunk c of row r stored at
+// c ^ key(r); fp16 V rows are 256 bytes padded to 288, so 8 consecutive
+// tokens start in 8 different 32-byte bank groups and every V read offset
+// stays an immediate. Both spread the 16-row fragment reads over the banks.
 #include "common.h"
 #include "quant_common.h"
 
@@ -44,11 +47,14 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) v2i lds_v2i;
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lds_v4s;
 
 constexpr int kD = 128;         // head size
 constexpr int kTile = 64;       // tokens per KV tile
 constexpr int kRows = 128;      // score rows per workgroup: (token, head) pairs
+constexpr int kVRow = 2 * kD + 32;  // bytes per fp16 V row in LDS (256 + 32 of padding)
 constexpr float kLog2e = 1.44269504088896341f;
 
 // A cache row pointer marked as global memory (global, not flat, loads).
@@ -99,7 +105,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
     float sm_scale, uint16_t* __restrict__ out, int64_t ldo) {
   constexpr int BQ = kRows / G;  // new tokens per workgroup
   __shared__ __attribute__((aligned(1024))) uint8_t kt[2][kTile * kD];
-  __shared__ __attribute__((aligned(1024))) uint8_t vt[2][kTile * kD];
+  __shared__ __attribute__((aligned(1024))) uint8_t vt[2][kTile * kVRow];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -205,7 +211,12 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       *reinterpret_cast<u32x4*>(&kt[st][swz(ltok, 2 * lpart + h)]) = kr[h];
-      *reinterpret_cast<u32x4*>(&vt[st][swz(ltok, 2 * lpart + h)]) = vr[h];
+      // V dims 32*lpart + 16h .. +15 as fp16: bytes 64*lpart + 32h .. +31 of the row
+      const v8h lo = fp8x8_to_f16(v2i{(int)vr[h].x, (int)vr[h].y});
+      const v8h hi = fp8x8_to_f16(v2i{(int)vr[h].z, (int)vr[h].w});
+      uint8_t* dst = &vt[st][ltok * kVRow + 64 * lpart + 32 * h];
+      *reinterpret_cast<v8h*>(dst) = lo;
+      *reinterpret_cast<v8h*>(dst + 16) = hi;
     }
   };
 
@@ -291,9 +302,11 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
     }
     // O^T += V^T P^T over two 32-token chunks. Contraction slot (g, j) of
     // chunk c is token 32c + 16(j/4) + 4g + j%4: the probabilities a lane
-    // holds for its row; V^T comes from the transpose read (source lanes 2j
-    // and 2j+1 of a 16-lane group read the two 8-byte halves of token slot
-    // j's 16 values of the dim tile).
+    // holds for its row. V^T comes from two transposing reads per fragment
+    // (slots j = 4h .. 4h+3): in a 16-lane group the four lanes 4j'..4j'+3
+    // read the 16 fp16 values of the dim tile for token slot 4h + j' (8
+    // bytes each), and lane i receives value i of each of the four slots
+    // (the lane layout of ds_read_b64_tr_b16, checked on the GPU).
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       // head = fp16(p) two at a time; remainder = fp16(p - head), the
@@ -312,13 +325,13 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
           pl[qt][j] = l[0];
           pl[qt][j + 1] = l[1];
         }
-      const int j = c16 >> 1, half = c16 & 1;
-      const int vrow = 32 * c + 16 * (j / 4) + 4 * g + (j % 4);
+      const uint8_t* vrow = V + (32 * c + 4 * g + (c16 >> 2)) * kVRow + 8 * (c16 & 3);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
-        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (lds_v2i*)(V + swz(vrow, dt) + 8 * half));
-        const v8h vf = fp8x8_to_f16(raw);
+        const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow + 32 * dt));
+        const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(vrow + 16 * kVRow + 32 * dt));
+        const v4h h0 = __builtin_bit_cast(v4h, r0), h1 = __builtin_bit_cast(v4h, r1);
+        const v8h vf = v8h{h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
           acc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph[qt], acc[qt][dt], 0, 0, 0);
