@@ -56,6 +56,7 @@ constexpr int kTile = 64;       // tokens per KV tile
 constexpr int kRows = 128;      // score rows per workgroup: (token, head) pairs
 constexpr int kVRow = 2 * kD + 32;  // bytes per fp16 V row in LDS (256 + 32 of padding)
 constexpr float kLog2e = 1.44269504088896341f;
+constexpr float kSlack = 8.0f;  // log2 of the largest unnormalised probability
 
 // A cache row pointer marked as global memory (global, not flat, loads).
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
@@ -280,7 +281,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[u][qt][r]);
       mt = cross4_max(mt) * mulv;
-      const float mn = fmaxf(m_run[qt], mt);
+      // The running maximum moves only when a tile's maximum exceeds it by
+      // more than kSlack (log2 units): probabilities are then at most
+      // 2^kSlack, well inside fp16 and fp32, and the accumulators are
+      // rescaled only on such a jump instead of on nearly every tile (with
+      // 16 rows per accumulator some row's maximum rises in most tiles).
+      // The normalisation by the row sum at the end makes the result
+      // independent of the reference point.
+      const float mn = mt > m_run[qt] + kSlack ? mt : m_run[qt];
       const float ms = mn == -INFINITY ? 0.f : mn;  // no token yet: keep exp2 finite
       alpha[qt] = __builtin_amdgcn_exp2f(m_run[qt] - ms);
       float ps = 0.f;
