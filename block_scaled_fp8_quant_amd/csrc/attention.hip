@@ -26,11 +26,17 @@
 //     The caches are head-major pages [blocks][Hkv][block_size][D]: a
 //     workgroup's rows of one page are one contiguous block_size x 128-byte
 //     run;
-//   * QK^T: one v_mfma_scale_f32_16x16x128_f8f6f4 per 16 tokens, source 0 =
-//     the group's Q rows (heads, padded to 16 with zeros), source 1 = 16 K
-//     rows loaded straight from the cache. Lane l then holds the scores of
-//     heads 4(l/16)..+3 for token l%16 of the subtile, so every head's
-//     maximum and sum over the tile are reductions over one 16-lane DPP row;
+//   * QK^T on the fp16 matrix cores, four v_mfma_f32_16x16x32_f16 steps of
+//     32 head dims per 16 tokens, source 0 = the group's Q rows (heads,
+//     padded to 16 with zeros), source 1 = 16 K rows loaded straight from the
+//     cache, both converted from E4M3 to fp16 in registers (exact). The FP8
+//     instruction would take the whole head in one step, but it sums each
+//     group of 8 products in a window 13 bits below the group's largest
+//     product, which with a large score scale moves the scores by whole units
+//     and the softmax with them; the fp16 instruction adds exact products in
+//     fp32. Lane l then holds the scores of heads 4(l/16)..+3 for token l%16
+//     of the subtile, so every head's maximum and sum over the tile are
+//     reductions over one 16-lane DPP row;
 //   * PV on the VALU in fp32: 16 lanes cover the 128 values of one V row
 //     (8 bytes each, one coalesced 128-byte read), four rows per load
 //     instruction (each 16-lane group walks 16 consecutive tokens), and each
@@ -129,6 +135,12 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     const uint4 hi = *reinterpret_cast<const uint4*>(&q8[(c16 * D + 64 + 16 * g) / 4]);
     qfrag = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
   }
+  // fp16 Q for the four score steps: step s of lane group g covers head dims
+  // 16g + 8s .. +7 (s < 2) and 64 + 16g + 8(s-2) .. +7, bytes 8s .. 8s+7 of
+  // the fragment above; the K fragments take the same bytes of their rows
+  f16x8 qh[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) qh[st] = e4m3x8_to_f16((uint32_t)qfrag[2 * st], (uint32_t)qfrag[2 * st + 1]);
   const float s2scale = qs * ks * sm_scale * kLog2eAttn;  // scores in the log2 domain
   const uint8_t* const zero = reinterpret_cast<const uint8_t*>(kZeroRow);
 
@@ -218,10 +230,11 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       float s[4][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const v8i kfrag = v8i{(int)klo[u].x, (int)klo[u].y, (int)klo[u].z, (int)klo[u].w,
-                              (int)khi[u].x, (int)khi[u].y, (int)khi[u].z, (int)khi[u].w};
-        const v4f d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qfrag, kfrag, v4f{0.f, 0.f, 0.f, 0.f}, 0,
-                                                                       0, 0, 127, 0, 127);
+        v4f d = v4f{0.f, 0.f, 0.f, 0.f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[0], e4m3x8_to_f16(klo[u].x, klo[u].y), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[1], e4m3x8_to_f16(klo[u].z, klo[u].w), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[2], e4m3x8_to_f16(khi[u].x, khi[u].y), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[3], e4m3x8_to_f16(khi[u].z, khi[u].w), d, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[u][r] = krow[u] >= 0 ? d[r] * s2scale : -INFINITY;
       }

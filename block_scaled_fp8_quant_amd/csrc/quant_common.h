@@ -20,6 +20,18 @@ constexpr float kFastMinScale = 0x1p-90f;
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 codes (two dwords, byte i = element i) -> 8 fp16 values. Exact:
+// every E4M3 value (subnormals included) is an fp16 value.
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(uint32_t lo, uint32_t hi) {
+  const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+  const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+  const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+  const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 // RN32(amax / 448) without a division: q0 = amax * RN32(1/448), then one
 // fma-corrected step. Equal to the IEEE quotient for every positive finite

@@ -17,10 +17,14 @@ DEV = "cuda:0"
 D = 128
 
 
-def build(lens, hq, hkv, seed=0, bs=16):
+def build(lens, hq, hkv, seed=0, bs=16, k_ramp=None):
     """Inputs on the device, caches filled by the cache write with scales
-    calibrated on the data."""
+    calibrated on the data; with ``k_ramp`` each cached token t of a
+    sequence has its key scaled by 1 + t / k_ramp."""
     a = synth.attention_inputs(lens, hq, hkv, D, bs, seed)
+    if k_ramp is not None:
+        t = torch.cat([torch.arange(int(n), dtype=torch.float32) for n in a["context_lens"].tolist()])
+        a["k"] = (a["k"].float() * (1.0 + t / k_ramp)[:, None]).to(torch.bfloat16)
     k, v = a["k"].to(DEV), a["v"].to(DEV)
     num_slots = a["num_slots"]
     kc = torch.zeros(num_slots // bs, hkv, bs, D, dtype=torch.uint8, device=DEV)
@@ -96,6 +100,19 @@ def test_softmax_scale_and_block_size(fp8blk_lib):
         out = run(a, kc, vc, sc, sm)
         assert_within_tolerance(out.float().cpu().numpy().reshape(3, -1), reference(a, kc, vc, sc, sm).reshape(3, -1),
                                 what="sm_scale %g" % sm)
+
+
+@pytest.mark.parametrize("mode", ["direct", "split_256"])
+@pytest.mark.parametrize("sm,ramp", [(1.0, None), (0.3, 64.0), (1.0, 16.0)])
+def test_large_score_jumps(fp8blk_lib, sm, ramp, mode):
+    """Scores with a large spread and row maxima that keep rising along the
+    context (a large sm_scale, keys growing with the token index): the
+    scores must be exact products, or the softmax moves with their errors."""
+    a, kc, vc, sc = build([1, 63, 300, 777, 1024], 32, 8, seed=9, k_ramp=ramp)
+    out = run(a, kc, vc, sc, sm=sm, mode=mode)
+    worst = assert_within_tolerance(out.float().cpu().numpy().reshape(-1), reference(a, kc, vc, sc, sm=sm).reshape(-1),
+                                    what="decode attention (score jumps)")
+    print("sm %.2f ramp %s %s: worst error / tolerance %.3f" % (sm, ramp, mode, worst), flush=True)
 
 
 def test_single_token_is_its_value_row(fp8blk_lib):

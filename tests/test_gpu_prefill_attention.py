@@ -18,8 +18,14 @@ DEV = "cuda:0"
 D = 128
 
 
-def build(seqs, hq, hkv, seed=0, bs=16):
+def build(seqs, hq, hkv, seed=0, bs=16, k_ramp=None):
+    """Inputs and the FP8 cache; with ``k_ramp`` each cached token t of a
+    sequence has its key scaled by 1 + t / k_ramp (row maxima that keep
+    rising along the sequence)."""
     a = synth.prefill_inputs(seqs, hq, hkv, D, bs, seed)
+    if k_ramp is not None:
+        t = torch.cat([torch.arange(int(n), dtype=torch.float32) for n in a["context_lens"].tolist()])
+        a["k"] = (a["k"].float() * (1.0 + t / k_ramp)[:, None]).to(torch.bfloat16)
     k, v = a["k"].to(DEV), a["v"].to(DEV)
     num_slots = a["num_slots"]
     kc = torch.zeros(num_slots // bs, hkv, bs, D, dtype=torch.uint8, device=DEV)
@@ -80,6 +86,21 @@ def test_explicit_scale_and_strided_queries(fp8blk_lib):
     out = run(a, kc, vc, sc, sm=0.05, q=wide[:, :32 * D])
     ref = reference(a, kc, vc, sc, sm=0.05)
     assert_within_tolerance(out.float().cpu().numpy().reshape(-1), ref.reshape(-1), what="prefill attention sm")
+
+
+@pytest.mark.parametrize("sm,ramp", [(1.0, None), (0.3, 64.0), (1.0, 16.0)])
+def test_large_score_jumps(fp8blk_lib, sm, ramp):
+    """Row maxima that rise by far more than 2^8 (8 in log2 units) between
+    KV tiles, where the kernel moves its reference maximum and rescales the
+    accumulators: a large sm_scale (scores of standard deviation ~23, i.e.
+    ~33 in log2 units) and keys growing along the sequence."""
+    seqs = [(130, 300), (200, 200), (64, 64), (1, 777)]
+    a, kc, vc, sc = build(seqs, 32, 8, seed=7, k_ramp=ramp)
+    out = run(a, kc, vc, sc, sm=sm)
+    ref = reference(a, kc, vc, sc, sm=sm)
+    worst = assert_within_tolerance(out.float().cpu().numpy().reshape(-1), ref.reshape(-1),
+                                    what="prefill attention (score jumps)")
+    print("sm %.2f ramp %s: worst error / tolerance %.3f" % (sm, ramp, worst), flush=True)
 
 
 def test_tokens_past_max_seqlen_are_left_alone(fp8blk_lib):
