@@ -408,21 +408,23 @@ __global__ __launch_bounds__(64) void decode_attention_combine_kernel(
 }
 
 constexpr int64_t kSplitUnit = 256;  // chunk sizes are multiples of one tile per wave
-constexpr int64_t kFillWGs = 256;    // one workgroup per CU keeps the cache reads at their best
+constexpr int64_t kFillWGs = 512;    // automatic split: about two workgroups per CU
+constexpr int64_t kMinChunk = 2048;  // automatic split: the shortest chunk (a multiple of kSplitUnit)
 
 // Tokens per chunk for the split path: the caller's, else (automatic) the
-// whole addressable context -- no split -- when there are at least 256
-// (sequence, KV head) pairs, otherwise chunks sized so that about 256
-// workgroups run (a measured optimum: the direct path reaches its best
-// bandwidth with one workgroup per CU, and small chunks lose to the
-// pipeline start and the merge).
+// whole addressable context -- no split -- when there are at least 512
+// (sequence, KV head) pairs, otherwise chunks sized so that about 512
+// workgroups run, but at least 2048 tokens long (measured: two workgroups
+// per CU keep a long context's tiles coming faster than one, and chunks
+// below 2048 tokens lose to the pipeline start and the merge).
 int64_t split_chunk(int64_t B, int64_t Hkv, int64_t Lcap, int64_t split_tokens) {
   if (split_tokens > 0) return split_tokens;
   const int64_t pairs = B * Hkv;
   if (pairs >= kFillWGs) return ((Lcap + kSplitUnit - 1) / kSplitUnit) * kSplitUnit;
   const int64_t splits = (kFillWGs + pairs - 1) / pairs;
   const int64_t c = (Lcap + splits - 1) / splits;
-  return ((c + kSplitUnit - 1) / kSplitUnit) * kSplitUnit;
+  const int64_t chunk = ((c + kSplitUnit - 1) / kSplitUnit) * kSplitUnit;
+  return chunk > kMinChunk ? chunk : kMinChunk;
 }
 
 }  // namespace

@@ -298,11 +298,17 @@ def test_decode_attention_workspace_size(lib):
     # 4 sequences, 32/8 heads, 16 blocks of 16 tokens: one 256-token chunk -> not split
     assert size(4, 32, 8, 128, 16, 16, 0) == 0
     # 4096 addressable tokens, 32 (sequence, KV head) pairs: the automatic
-    # chunk brings the grid to 256 workgroups (8 chunks of 512); partials of
-    # (128 + 2) floats per query head and chunk
-    assert size(4, 32, 8, 128, 256, 16, 0) == 4 * 32 * 8 * 130 * 4
+    # chunk would bring the grid to 512 workgroups (16 chunks of 256) but is
+    # at least 2048 tokens: 2 chunks; partials of (128 + 2) floats per query
+    # head and chunk
+    assert size(4, 32, 8, 128, 256, 16, 0) == 4 * 32 * 2 * 130 * 4
+    # 32768 tokens, 32 pairs: 16 chunks of 2048 (512 workgroups)
+    assert size(4, 32, 8, 128, 2048, 16, 0) == 4 * 32 * 16 * 130 * 4
+    # 16384 tokens, 256 pairs: 2 chunks of 8192
+    assert size(32, 32, 8, 128, 1024, 16, 0) == 32 * 32 * 2 * 130 * 4
     assert size(4, 32, 8, 128, 256, 16, 1024) == 4 * 32 * 4 * 130 * 4
-    # 256 x 8 pairs fill the chip without splitting
+    # 64 x 8 pairs fill the chip without splitting
+    assert size(64, 32, 8, 128, 256, 16, 0) == 0
     assert size(256, 32, 8, 128, 256, 16, 0) == 0
     assert size(256, 32, 8, 128, 256, 16, 256) == 256 * 32 * 16 * 130 * 4
     assert size(4, 32, 8, 64, 256, 16, 0) == 0             # D != 128
