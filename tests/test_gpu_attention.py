@@ -96,7 +96,7 @@ def test_split_workspace_reuse_and_size(fp8blk_lib):
 
 def test_softmax_scale_and_block_size(fp8blk_lib):
     a, kc, vc, sc = build([33, 130, 7], 16, 4, seed=5, bs=8)
-    for sm in (0.01, 0.3):
+    for sm in (0.01, 0.3, -0.2, 0.0):
         out = run(a, kc, vc, sc, sm)
         assert_within_tolerance(out.float().cpu().numpy().reshape(3, -1), reference(a, kc, vc, sc, sm).reshape(3, -1),
                                 what="sm_scale %g" % sm)

@@ -103,6 +103,18 @@ def test_large_score_jumps(fp8blk_lib, sm, ramp):
     print("sm %.2f ramp %s: worst error / tolerance %.3f" % (sm, ramp, worst), flush=True)
 
 
+@pytest.mark.parametrize("sm", [-0.2, 0.0])
+def test_negative_and_zero_softmax_scale(fp8blk_lib, sm):
+    """A negative scale (the largest products get the smallest weights) and
+    a zero scale (uniform weights over each token's context); these take
+    the path that scales every score, as masked tiles do."""
+    seqs = [(130, 300), (64, 64), (5, 5)]
+    a, kc, vc, sc = build(seqs, 32, 8, seed=8)
+    out = run(a, kc, vc, sc, sm=sm)
+    ref = reference(a, kc, vc, sc, sm=sm)
+    assert_within_tolerance(out.float().cpu().numpy().reshape(-1), ref.reshape(-1), what="prefill attention sm %g" % sm)
+
+
 def test_tokens_past_max_seqlen_are_left_alone(fp8blk_lib):
     """max_seqlen_q below a sequence's new tokens: the tokens past it are not
     computed (their rows keep what the caller put there); the others match."""
