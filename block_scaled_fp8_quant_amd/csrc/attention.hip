@@ -10,7 +10,8 @@
 // (the cache write's quantizer); the scores are exact FP8 products,
 //     s[h][t] = (q8[h] . k8[t][g]) * q_scale * k_scale * sm_scale,
 // g = h / (Hq/Hkv); softmax in fp32; out[h] = sum_t p[h][t] v8[t][g] v_scale,
-// probabilities kept in fp32; bf16 output.
+// each probability carried as an fp16 head plus an fp16 remainder (22
+// significant bits); bf16 output.
 //
 // Work decomposition: a workgroup of four waves takes one (sequence, KV head)
 // and either the whole context (direct mode: it writes the bf16 output) or
@@ -26,21 +27,23 @@
 //     The caches are head-major pages [blocks][Hkv][block_size][D]: a
 //     workgroup's rows of one page are one contiguous block_size x 128-byte
 //     run;
-//   * QK^T on the fp16 matrix cores, four v_mfma_f32_16x16x32_f16 steps of
-//     32 head dims per 16 tokens, source 0 = the group's Q rows (heads,
-//     padded to 16 with zeros), source 1 = 16 K rows loaded straight from the
-//     cache, both converted from E4M3 to fp16 in registers (exact). The FP8
-//     instruction would take the whole head in one step, but it sums each
-//     group of 8 products in a window 13 bits below the group's largest
-//     product, which with a large score scale moves the scores by whole units
-//     and the softmax with them; the fp16 instruction adds exact products in
-//     fp32. Lane l then holds the scores of heads 4(l/16)..+3 for token l%16
-//     of the subtile, so every head's maximum and sum over the tile are
-//     reductions over one 16-lane DPP row;
-//   * PV on the VALU in fp32: 16 lanes cover the 128 values of one V row
-//     (8 bytes each, one coalesced 128-byte read), four rows per load
-//     instruction (each 16-lane group walks 16 consecutive tokens), and each
-//     lane accumulates G x 8 outputs; p comes from LDS.
+//   * S^T = K Q^T on the fp16 matrix cores, four v_mfma_f32_16x16x32_f16
+//     steps of 32 head dims per 16 tokens, source 0 = 16 K rows loaded
+//     straight from the cache, source 1 = the group's Q rows (heads, padded
+//     to 16 with zeros), both converted from E4M3 to fp16 in registers
+//     (exact). The FP8 instruction would take the whole head in one step,
+//     but it sums each group of 8 products in a window 13 bits below the
+//     group's largest product, which with a large score scale moves the
+//     scores by whole units and the softmax with them; the fp16 instruction
+//     adds exact products in fp32. Lane (c, g) then holds head c's scores of
+//     16 of the tile's tokens, and its three partner lanes (same c) the other
+//     48: a head's maximum is the lane's own plus two cross-lane steps;
+//   * O^T += V^T P^T on the same instruction, two 32-token steps per 16 head
+//     dims: the probabilities are already where source 1 wants them (no LDS
+//     round trip), the V rows go through a wave-private LDS tile and come
+//     back transposed (ds_read_b64_tr_b8) as source 0. The matrix cores take
+//     the G x 128 x 64 products per tile that the vector ALUs were the bound
+//     on, padded to 16 heads.
 // The cache reads are the bound (K and V, 256 bytes per token and KV head).
 #include "common.h"
 #include "quant_common.h"
@@ -51,9 +54,21 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int kHeadDim = 128;
 constexpr float kLog2eAttn = 1.44269504088896341f;
+constexpr float kSlackAttn = 8.0f;  // log2 of the largest unnormalised probability
+
+// Byte offset of 16-byte chunk c of V row t in a wave's 64 x 128-byte tile.
+// Rows t and t ^ 1 trade places when bit 4 of t is set, and chunk c sits at
+// c ^ ((t >> 1) & 7): the row writes (rows k, 16 + k, 32 + k, 48 + k at
+// once) and the transposing reads (32 token rows, one chunk each) then
+// spread over all the banks.
+__device__ __forceinline__ int vswz(int t, int c) {
+  return ((t ^ ((t >> 4) & 1)) << 7) + ((c ^ ((t >> 1) & 7)) << 4);
+}
 
 // what a masked token reads in place of its K and V rows
 __device__ const uint32_t kZeroRow[kHeadDim / 4] = {};
@@ -62,21 +77,6 @@ __device__ const uint32_t kZeroRow[kHeadDim / 4] = {};
 // (not flat) loads and do not hold up the LDS waits of the loop.
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 __device__ __forceinline__ gbytes as_global(const uint8_t* p) { return (gbytes)p; }
-
-__device__ __forceinline__ float row16_max_f(float v) {
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
-  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
-  return v;
-}
-__device__ __forceinline__ float row16_sum_f(float v) {
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
-  return v;
-}
 
 // Make this wave's LDS writes visible to its own later LDS reads by other
 // lanes (LDS operations of one wave complete in order).
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
   constexpr int D = kHeadDim;
   __shared__ __attribute__((aligned(16))) uint32_t q8[G * D / 4];
   __shared__ __attribute__((aligned(16))) int32_t row_tile[4][64];
-  __shared__ __attribute__((aligned(16))) float ptile[4][64][G];
+  __shared__ __attribute__((aligned(1024))) uint8_t vlds[4][64 * kHeadDim];  // each wave's V rows of a tile
   __shared__ float m_w[4][G], l_w[4][G];
   __shared__ __attribute__((aligned(16))) float acc_w[4][G][D];
 
@@ -143,19 +143,20 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
   for (int st = 0; st < 4; ++st) qh[st] = e4m3x8_to_f16((uint32_t)qfrag[2 * st], (uint32_t)qfrag[2 * st + 1]);
   const float s2scale = qs * ks * sm_scale * kLog2eAttn;  // scores in the log2 domain
   const uint8_t* const zero = reinterpret_cast<const uint8_t*>(kZeroRow);
+  // opaque to the compiler, so that the FMAs splitting the probabilities
+  // below stay FMAs instead of being folded into subtractions
+  float one = 1.0f;
+  asm volatile("" : "+s"(one));
 
-  // running state: lane group g holds heads 4g..4g+3 (entries r < 4)
-  float m_run[4], l_run[4];
+  // running state of this lane's head: lane (c16, g) with c16 < G works for
+  // head c16 of the group; the four lanes of a head (c16, c16+16, c16+32,
+  // c16+48) hold the same reference maximum and their own shares of the sum
+  const bool head_lane = c16 < G;
+  float m_run = -INFINITY, l_run = 0.f;
+  v4f acc[8];  // O^T tiles [dt]: lane (c16, g) holds O[head c16][dim 16dt + 4g + r]
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    m_run[r] = -INFINITY;
-    l_run[r] = 0.f;
-  }
-  float acc[G][8];
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[h][e] = 0.f;
+  for (int dt = 0; dt < 8; ++dt) acc[dt] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint8_t* const vtile = vlds[wave];  // this wave's V rows of the tile (64 x 128 bytes)
 
   // Software pipeline over this wave's tiles (tokens t0..t0+63, t0 advancing
   // by 256): while tile i is computed, the K and V rows of tile i+1 and the
@@ -226,17 +227,22 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     for (int k = 0; k < 16; ++k) vw[k] = load_v(k);
 
     for (;;) {
-      // QK^T: scores (log2 domain) of heads 4g+r, tokens 16u + c16
+      // S^T = K Q^T (source 0 = the 16 K rows of a subtile, source 1 = the
+      // heads): lane (c16, g) gets s[u][r], the score of token 16u + 4g + r
+      // for head c16 (log2 domain); the rows of those tokens tell the masked
       float s[4][4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         v4f d = v4f{0.f, 0.f, 0.f, 0.f};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[0], e4m3x8_to_f16(klo[u].x, klo[u].y), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[1], e4m3x8_to_f16(klo[u].z, klo[u].w), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[2], e4m3x8_to_f16(khi[u].x, khi[u].y), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[3], e4m3x8_to_f16(khi[u].z, khi[u].w), d, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) s[u][r] = krow[u] >= 0 ? d[r] * s2scale : -INFINITY;
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(klo[u].x, klo[u].y), qh[0], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(klo[u].z, klo[u].w), qh[1], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(khi[u].x, khi[u].y), qh[2], d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(e4m3x8_to_f16(khi[u].z, khi[u].w), qh[3], d, 0, 0, 0);
+        const int4 rows = *reinterpret_cast<const int4*>(&row_tile[wave][16 * u + 4 * g]);
+        s[u][0] = rows.x >= 0 ? d[0] * s2scale : -INFINITY;
+        s[u][1] = rows.y >= 0 ? d[1] * s2scale : -INFINITY;
+        s[u][2] = rows.z >= 0 ? d[2] * s2scale : -INFINITY;
+        s[u][3] = rows.w >= 0 ? d[3] * s2scale : -INFINITY;
       }
       // the scheduling barriers keep each stage's loads after the last use
       // of the registers they overwrite (one register set per stage)
@@ -251,91 +257,92 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       load_k();
       __builtin_amdgcn_sched_barrier(0);
 
-      // online softmax per head (lane group g, entry r): tile maximum over
-      // the 64 tokens = 4 subtiles x the 16 lanes of the row
-      float alpha[4];
+      // online softmax of this lane's head over the tile (16 scores in the
+      // lane, the other 48 in its three partner lanes). The reference
+      // maximum moves only when the tile's exceeds it by more than kSlack
+      // (log2 units): probabilities stay at most 2^kSlack, and the
+      // accumulators are rescaled only then.
+      float mt = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float mt = fmaxf(fmaxf(s[0][r], s[1][r]), fmaxf(s[2][r], s[3][r]));
-        mt = row16_max_f(mt);
-        const float mn = fmaxf(m_run[r], mt);
-        const float ms = mn == -INFINITY ? 0.f : mn;  // no token yet: keep exp2 finite
-        alpha[r] = __builtin_amdgcn_exp2f(m_run[r] - ms);
-        float psum = 0.f;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          s[u][r] = __builtin_amdgcn_exp2f(s[u][r] - ms);
-          psum += s[u][r];
-        }
-        l_run[r] = l_run[r] * alpha[r] + row16_sum_f(psum);
-        m_run[r] = mn;
-      }
+      for (int u = 0; u < 4; ++u) mt = fmaxf(mt, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = mt > m_run + kSlackAttn ? mt : m_run;
+      const float ms = mn == -INFINITY ? 0.f : mn;  // no token yet: keep exp2 finite
+      const float alpha = __builtin_amdgcn_exp2f(m_run - ms);
+      float ps = 0.f;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (4 * g + r < G) ptile[wave][16 * u + c16][4 * g + r] = s[u][r];
-      wave_lds_sync();
+        for (int r = 0; r < 4; ++r) {
+          s[u][r] = __builtin_amdgcn_exp2f(s[u][r] - ms);
+          ps += s[u][r];
+        }
+      l_run = l_run * alpha + ps;
+      m_run = mn;
+      if (__builtin_amdgcn_ballot_w64(head_lane && alpha != 1.0f) != 0) {  // uniform
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) acc[dt] *= alpha;
+      }
 
-      // PV: lane = (tokens 16g..16g+15, value chunk c16); rescale, then the
-      // 16 tokens (masked tokens have p = 0 and read zeros). Each V register
-      // is reloaded with the next tile's row as soon as it is consumed.
-      float al[G];
+      // this tile's V rows into the wave's LDS rows (16-byte chunk c of row t
+      // at chunk c ^ key(t)), then the next tile's V rows into the registers
 #pragma unroll
-      for (int h = 0; h < G; ++h)  // head h's factor lives in lane group h/4, entry h%4
-        al[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(alpha[h & 3]), 16 * (h >> 2)));
+      for (int k = 0; k < 16; ++k)
+        *reinterpret_cast<u32x2*>(vtile + vswz(16 * g + k, c16 >> 1) + 8 * (c16 & 1)) = vw[k];
+      wave_lds_sync();
 #pragma unroll
-      for (int h = 0; h < G; ++h)
+      for (int k = 0; k < 16; ++k) vw[k] = load_v(k);
+
+      // O^T += V^T P^T over two 32-token chunks on the fp16 matrix cores.
+      // Contraction slot (g, j) of chunk c is token 32c + 16(j/4) + 4g + j%4,
+      // so source 1 (P^T: the probabilities of head c16) is this lane's
+      // s[2c + j/4][j%4], split into an fp16 head and remainder (the
+      // remainder's difference exact in the FMA). Source 0 (V^T) comes from
+      // the transposing read ds_read_b64_tr_b8: in a 16-lane group, lanes 2j
+      // and 2j+1 read the two 8-byte halves of token slot j's 16 values of the
+      // dim tile, and lane i receives value i of each of the 8 slots;
+      // converted to fp16 (exact for E4M3).
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[h][e] *= al[h];
-      // p of this lane's tokens, one token ahead of its use
-      typedef float pvec __attribute__((ext_vector_type(G)));
-      const pvec* prow = reinterpret_cast<const pvec*>(&ptile[wave][16 * g][0]);
-      pvec pn = prow[0];
+      for (int c = 0; c < 2; ++c) {
+        f16x8 ph, pl;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const pvec p = pn;
-        if (k < 15) pn = prow[k + 1];
-        float v[8];
-        const f32x2 v0 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k].x, false);
-        const f32x2 v1 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k].x, true);
-        const f32x2 v2 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k].y, false);
-        const f32x2 v3 = __builtin_amdgcn_cvt_pk_f32_fp8((int)vw[k].y, true);
-        vw[k] = load_v(k);
-        v[0] = v0.x; v[1] = v0.y; v[2] = v1.x; v[3] = v1.y;
-        v[4] = v2.x; v[5] = v2.y; v[6] = v3.x; v[7] = v3.y;
+        for (int j = 0; j < 8; j += 2) {
+          const float p0 = s[2 * c + j / 4][j % 4], p1 = s[2 * c + j / 4][j % 4 + 1];
+          const f16x2 h = __builtin_convertvector(f32x2{p0, p1}, f16x2);
+          const f16x2 l = __builtin_convertvector(
+              f32x2{__builtin_fmaf(-(float)h[0], one, p0), __builtin_fmaf(-(float)h[1], one, p1)}, f16x2);
+          ph[j] = h[0];
+          ph[j + 1] = h[1];
+          pl[j] = l[0];
+          pl[j + 1] = l[1];
+        }
+        const int jj = c16 >> 1;
+        const int tok = 32 * c + 16 * (jj >> 2) + 4 * g + (jj & 3);
 #pragma unroll
-        for (int h = 0; h < G; ++h)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[h][e] = __builtin_fmaf(p[h], v[e], acc[h][e]);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int dt = 0; dt < 8; ++dt) {
+          const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vtile + vswz(tok, dt) + 8 * (c16 & 1)));
+          const f16x8 vf = e4m3x8_to_f16((uint32_t)raw[0], (uint32_t)raw[1]);
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, ph, acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl, acc[dt], 0, 0, 0);
+        }
       }
       t0 = tn;
       if (t0 >= c1) break;
     }
   }
 
-  // this wave's totals: sum the four token groups (lanes c16, +16, +32, +48)
+  // this wave's totals: the four lanes of a head add their shares of the sum
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  if (head_lane) {
 #pragma unroll
-  for (int h = 0; h < G; ++h)
+    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      acc[h][e] += __shfl_xor(acc[h][e], 16);
-      acc[h][e] += __shfl_xor(acc[h][e], 32);
-    }
-  if (lane < 16) {
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc_w[wave][h][8 * c16 + e] = acc[h][e];
-  }
-#pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float mh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_run[h & 3]), 16 * (h >> 2)));
-    const float lh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_run[h & 3]), 16 * (h >> 2)));
-    if (lane == 0) {
-      m_w[wave][h] = mh;
-      l_w[wave][h] = lh;
+      for (int r = 0; r < 4; ++r) acc_w[wave][c16][16 * dt + 4 * g + r] = acc[dt][r];
+    if (g == 0) {
+      m_w[wave][c16] = m_run;
+      l_w[wave][c16] = l_run;
     }
   }
   __syncthreads();
