@@ -405,7 +405,8 @@ fp8blk_status fp8blk_kv_cache_write(const uint16_t* k, const uint16_t* v, int64_
  *   s[h][t] = (sum_d q8[h][d] * k8[t][g][d]) * q_scale * k_scale * sm_scale,
  *             g = h / (Hq / Hkv)
  *   out[h][d] = bf16( sum_t softmax_t(s[h])[t] * v8[t][g][d] * v_scale )
- * with the softmax and the weighted sum in fp32.
+ * with the softmax and the weighted sum in fp32 (each probability enters the
+ * weighted sum as an fp16 head plus an fp16 remainder, about 2^-22 relative).
  *   q            [B][ldq] bf16: the first Hq*D values of row b are sequence b's
  *                query heads (so q may point into a qkv projection output)
  *   k_cache, v_cache [num_slots / block_size][Hkv][block_size][D] E4M3
