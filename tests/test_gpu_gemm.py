@@ -431,6 +431,54 @@ def test_big_tile_one_and_odd_k_blocks(fp8blk_lib, k, pow2):
     _layer_check(x, w, pow2)
 
 
+def _dense_sampled_check(x, w, rows, pow2=False, nudge=None):
+    """GPU GEMM on the whole layer, the oracle on the given rows (all
+    columns). ``nudge`` = (row, block, factor) multiplies one activation
+    scale on both sides after quantization."""
+    qa, sa = fb.quant_act(x.to(DEV), pow2)
+    qw, sw = fb.quant_weight(w.to(DEV), pow2)
+    qa_r, sa_r = oracle.quant_act_ref(x[torch.from_numpy(rows)], pow2)
+    qw_r, sw_r = oracle.quant_weight_ref(w, pow2)
+    if nudge is not None:
+        r, b, f = nudge
+        sa[r, b] *= f
+        sa_r[np.searchsorted(rows, r), b] *= np.float32(f)
+    y = _gemm_guarded(qa, sa, qw, sw)
+    y_s = y[torch.from_numpy(rows).to(DEV)].float().cpu().numpy()
+    return assert_within_tolerance(y_s, oracle.gemm_ref(qa_r, sa_r, qw_r, sw_r), what="sampled dense gemm")
+
+
+@pytest.mark.parametrize("pow2", [False, True])
+@pytest.mark.parametrize("m,k", [(6000, 256), (6144, 384)])
+def test_dense_persistent_tile_walk(fp8blk_lib, m, k, pow2):
+    """At least three 256x256 tiles per CU and a short K: the persistent
+    kernel, each workgroup walking its XCD's tiles with the next tile's
+    first K blocks loaded during the current tile's last steps (K = 256:
+    every step of a tile loads the next one's; K = 384: an odd block
+    count), M = 6000 leaving a partial last row tile. Checked on the first
+    and last rows of every row tile and random rows, all 8192 columns."""
+    print("dense persistent m=%d k=%d pow2=%s" % (m, k, pow2), flush=True)
+    g = synth.generator(16, seed=m + k)
+    x = synth.activation(m, k, g, 0.005, 30.0)
+    w = synth.weight(8192, k, g)
+    edges = {r for t in range(0, m, 256) for r in (t, min(t + 255, m - 1))}
+    rnd = torch.randint(0, m, (32,), generator=g).tolist()
+    _dense_sampled_check(x, w, np.array(sorted(edges | set(rnd)), dtype=np.int64), pow2)
+
+
+def test_dense_persistent_one_scale_off(fp8blk_lib):
+    """Power-of-two scales on a persistent walk except one activation scale:
+    that tile folds, its neighbours in the same workgroup's walk scale inside
+    the MFMA (the K loop variant changes between tiles whose first blocks
+    were loaded by the previous tile's loop)."""
+    g = synth.generator(17)
+    x = synth.activation(6144, 256, g, 0.005, 30.0)
+    w = synth.weight(8192, 256, g)
+    rows = np.array(sorted({0, 1299, 1300, 1301, 1535, 1536, 6143} |
+                           set(torch.randint(0, 6144, (24,), generator=g).tolist())), dtype=np.int64)
+    _dense_sampled_check(x, w, rows, pow2=True, nudge=(1300, 1, 1.25))
+
+
 def test_power_of_two_one_scale_off_big_tile(fp8blk_lib):
     """256x256 tiles with power-of-two scales everywhere except one activation
     scale: that tile folds, every other tile scales inside the MFMA; all match
