@@ -56,7 +56,6 @@ sys.path.insert(0, ROOT)
 METRIC = "block-FP8 W8A8 GEMM TFLOP/s + % FP8 MFMA peak (Llama-8B shapes)"
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
-GEMM_KERNELS = ("gemm_kernel", "grouped_gemm_kernel")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 # kernels whose counter traffic is recorded (substrings of the kernel names)
 
@@ -853,7 +852,8 @@ def copy_yardstick():
 
 # GEMM-family kernels: a GEMM call is one dispatch of a primary kernel (the
 # split-K path adds its reduction to the same call)
-GEMM_PRIMARY = ("gemm_kernel<", "gemm_splitk_kernel", "grouped_gemm_kernel", "grouped_gemm_persistent_kernel")
+GEMM_PRIMARY = ("gemm_kernel<", "gemm_persistent_kernel<", "gemm_splitk_kernel", "grouped_gemm_kernel",
+                "grouped_gemm_persistent_kernel")
 GEMM_FAMILY = GEMM_PRIMARY + ("splitk_reduce_kernel",)
 
 
