@@ -69,6 +69,9 @@ constexpr float kSlack = 8.0f;  // log2 of the largest unnormalised probability
 // A cache row pointer marked as global memory (global, not flat, loads).
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 
+// what a masked token reads in place of its K and V rows
+__device__ const uint32_t kZeroRow[kD / 4] = {};
+
 
 // Race-detection build (-DFP8BLK_DEBUG_BARRIERS=1): extra workgroup
 // barriers (after every wave's loads have landed) around each stage's use,
@@ -184,34 +187,37 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 
   // K/V tile loads: thread tid takes token tid/4 of the tile, bytes 32*(tid%4)..+31
   const int ltok = tid >> 2, lpart = tid & 3;
-  const uint32_t bs32 = (uint32_t)block_size;
+  const uint32_t bs32 = (uint32_t)block_size, mb32 = (uint32_t)max_blocks;  // both < 2^31 (host-checked)
+  // a power-of-two block size divides by a shift (uniform branch)
+  const int bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctzll((uint64_t)block_size) : -1;
   const int32_t* const table_row = block_table + b * max_blocks;
-  auto cache_row = [&](int64_t t) -> int64_t {  // cache row of token t, -1 if masked
-    if (t >= t_end) return -1;
-    const uint32_t bi = (uint32_t)t / bs32;
-    if (bi >= (uint64_t)max_blocks) return -1;
-    const int32_t blk = table_row[bi];
-    const uint32_t off = (uint32_t)t - bi * bs32;
-    if (blk < 0 || (int64_t)blk * block_size + off >= num_slots) return -1;
-    return ((int64_t)blk * Hkv + gk) * block_size + off;
+  // The cache row of token t (t < L + 64 < 2^31), -1 if masked. Branch-free:
+  // the block index is clamped for the table read, and the row is computed
+  // in 32 bits (below num_slots * Hkv < 2^31 for every live token; masked
+  // tokens' values are discarded).
+  auto cache_row = [&](int64_t t) -> int32_t {
+    const uint32_t tu = (uint32_t)t;
+    uint32_t bi;
+    if (bs_shift >= 0)
+      bi = tu >> bs_shift;
+    else
+      bi = tu / bs32;
+    const int32_t blk = table_row[bi < mb32 ? bi : mb32 - 1];
+    const uint32_t off = tu - bi * bs32;
+    const bool live = t < t_end && bi < mb32 && blk >= 0 && (int64_t)blk * block_size + off < num_slots;
+    return live ? (int32_t)(((uint32_t)blk * (uint32_t)Hkv + (uint32_t)gk) * bs32 + off) : -1;
   };
+  // K/V rows: masked tokens read the zero row, so the loads are unconditional
   u32x4 kr[2], vr[2];
+  const uint8_t* const zero_row = reinterpret_cast<const uint8_t*>(kZeroRow);
   auto load_tile = [&](int tile) {
-    const int64_t row = cache_row((int64_t)tile * kTile + ltok);
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int32_t row = cache_row((int64_t)tile * kTile + ltok);
+    const gbytes kp = (gbytes)((row >= 0 ? k_cache + (int64_t)row * kD : zero_row) + 32 * lpart);
+    const gbytes vp = (gbytes)((row >= 0 ? v_cache + (int64_t)row * kD : zero_row) + 32 * lpart);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      kr[h] = zero;
-      vr[h] = zero;
-    }
-    if (row >= 0) {
-      const gbytes kp = (gbytes)(k_cache + row * kD + 32 * lpart);
-      const gbytes vp = (gbytes)(v_cache + row * kD + 32 * lpart);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        kr[h] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kp + 16 * h);
-        vr[h] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(vp + 16 * h);
-      }
+      kr[h] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kp + 16 * h);
+      vr[h] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(vp + 16 * h);
     }
   };
   auto store_tile = [&](int st) {
@@ -336,12 +342,11 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
         for (int j = 0; j < 8; j += 2) {
           const float p0 = s[2 * c + j / 4][qt][j % 4], p1 = s[2 * c + j / 4][qt][j % 4 + 1];
           const v2h h = __builtin_convertvector(v2f{p0, p1}, v2h);
-          const v2h l = __builtin_convertvector(
-              v2f{__builtin_fmaf(-(float)h[0], one, p0), __builtin_fmaf(-(float)h[1], one, p1)}, v2h);
+          // each remainder rounded to fp16 straight from the FMA (v_fma_mixlo/hi_f16)
           ph[qt][j] = h[0];
           ph[qt][j + 1] = h[1];
-          pl[qt][j] = l[0];
-          pl[qt][j + 1] = l[1];
+          pl[qt][j] = (_Float16)__builtin_fmaf(-(float)h[0], one, p0);
+          pl[qt][j + 1] = (_Float16)__builtin_fmaf(-(float)h[1], one, p1);
         }
       const uint8_t* vrow = V + (32 * c + 4 * g + (c16 >> 2)) * kVRow + 8 * (c16 & 3);
 #pragma unroll
