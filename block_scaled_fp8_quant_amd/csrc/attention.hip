@@ -63,9 +63,9 @@ constexpr float kSlackAttn = 8.0f;  // log2 of the largest unnormalised probabil
 
 // Byte offset of 16-byte chunk c of V row t in a wave's 64 x 128-byte tile.
 // Rows t and t ^ 1 trade places when bit 4 of t is set, and chunk c sits at
-// c ^ ((t >> 1) & 7): the row writes (rows k, 16 + k, 32 + k, 48 + k at
-// once) and the transposing reads (32 token rows, one chunk each) then
-// spread over all the banks.
+// c ^ ((t >> 1) & 7): the row writes (rows 8j + k of the eight lane groups
+// j at once, 16 bytes per lane) and the transposing reads (32 token rows,
+// one chunk each) then spread over all the banks.
 __device__ __forceinline__ int vswz(int t, int c) {
   return ((t ^ ((t >> 4) & 1)) << 7) + ((c ^ ((t >> 1) & 7)) << 4);
 }
@@ -179,15 +179,16 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     const bool live = t < c1 && bi < (uint64_t)max_blocks && blk >= 0 && (int64_t)blk * block_size + off < num_slots;
     return live ? (int32_t)(((int64_t)blk * Hkv + gk) * block_size + off) : -1;
   };
-  int32_t krow[4], vrow[16];
+  const int g8 = lane >> 3, c8 = lane & 7;
+  int32_t krow[4], vrow[8];
   auto read_rows = [&](int32_t row) {  // exchange the tile's cache rows through LDS
     row_tile[wave][lane] = row;
     wave_lds_sync();
 #pragma unroll
     for (int u = 0; u < 4; ++u) krow[u] = row_tile[wave][16 * u + c16];
 #pragma unroll
-    for (int k = 0; k < 16; k += 4) {
-      const int4 v4 = *reinterpret_cast<const int4*>(&row_tile[wave][16 * g + k]);
+    for (int k = 0; k < 8; k += 4) {
+      const int4 v4 = *reinterpret_cast<const int4*>(&row_tile[wave][8 * g8 + k]);
       vrow[k] = v4.x;
       vrow[k + 1] = v4.y;
       vrow[k + 2] = v4.z;
@@ -209,10 +210,11 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       khi[u] = *reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(kr + 64 + 16 * g);
     }
   };
-  // V rows of tokens 16g + k, bytes 8 c16..+7: each row is read once (streamed)
+  // V rows of tokens 8 g8 + k, bytes 16 c8..+15 (eight lanes per row): each
+  // row is read once (streamed)
   auto load_v = [&](int k) {
     const gbytes vr = row_or_zero(v_cache, vrow[k]);
-    return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x2*>(vr + 8 * c16));
+    return __builtin_nontemporal_load(reinterpret_cast<const __attribute__((address_space(1))) u32x4*>(vr + 16 * c8));
   };
 
   int64_t t0 = c0 + (int64_t)wave * 64;
@@ -222,9 +224,9 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
     blk = table_entry(t0 + 256 + lane);  // tile i+1's entries
     read_rows(row0);
     load_k();
-    u32x2 vw[16];
+    u32x4 vw[8];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) vw[k] = load_v(k);
+    for (int k = 0; k < 8; ++k) vw[k] = load_v(k);
 
     for (;;) {
       // S^T = K Q^T (source 0 = the 16 K rows of a subtile, source 1 = the
@@ -288,11 +290,10 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       // this tile's V rows into the wave's LDS rows (16-byte chunk c of row t
       // at chunk c ^ key(t)), then the next tile's V rows into the registers
 #pragma unroll
-      for (int k = 0; k < 16; ++k)
-        *reinterpret_cast<u32x2*>(vtile + vswz(16 * g + k, c16 >> 1) + 8 * (c16 & 1)) = vw[k];
+      for (int k = 0; k < 8; ++k) *reinterpret_cast<u32x4*>(vtile + vswz(8 * g8 + k, c8)) = vw[k];
       wave_lds_sync();
 #pragma unroll
-      for (int k = 0; k < 16; ++k) vw[k] = load_v(k);
+      for (int k = 0; k < 8; ++k) vw[k] = load_v(k);
 
       // O^T += V^T P^T over two 32-token chunks on the fp16 matrix cores.
       // Contraction slot (g, j) of chunk c is token 32c + 16(j/4) + 4g + j%4,
