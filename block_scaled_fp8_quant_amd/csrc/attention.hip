@@ -165,19 +165,32 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
   // unconditional and the wait counts are the same in every iteration.
   const uint32_t bs32 = (uint32_t)block_size;
   const int32_t* const table_row = block_table + b * max_blocks;
+  // token t's block index (t < 2^31): a shift for a power-of-two block size
+  // (uniform branch), else a division
+  const int bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctzll((uint64_t)block_size) : -1;
+  const uint32_t mb32 = (uint32_t)max_blocks;  // < 2^31, checked on the host
+  auto block_of = [&](int64_t t) {
+    uint32_t bi;
+    if (bs_shift >= 0)
+      bi = (uint32_t)t >> bs_shift;
+    else
+      bi = (uint32_t)t / bs32;
+    return bi;
+  };
   auto table_entry = [&](int64_t t) {  // the block id of token t (block index clamped)
-    const uint32_t bi = (uint32_t)t / bs32;
-    return table_row[bi < (uint64_t)max_blocks ? bi : max_blocks - 1];
+    const uint32_t bi = block_of(t);
+    return table_row[bi < mb32 ? bi : mb32 - 1];
   };
   // The cache row of token t for this KV head: head-major pages
   // [num_slots / block_size][Hkv][block_size][D], so row (blk*Hkv + gk) *
-  // block_size + offset, in units of D bytes (< num_slots * Hkv < 2^31,
-  // checked on the host); -1 for a masked token.
+  // block_size + offset, in units of D bytes, computed in 32 bits (below
+  // num_slots * Hkv < 2^31, checked on the host, for every live token;
+  // masked tokens' values are discarded); -1 for a masked token.
   auto token_row = [&](int64_t t, int32_t blk) {
-    const uint32_t bi = (uint32_t)t / bs32;
+    const uint32_t bi = block_of(t);
     const uint32_t off = (uint32_t)t - bi * bs32;
-    const bool live = t < c1 && bi < (uint64_t)max_blocks && blk >= 0 && (int64_t)blk * block_size + off < num_slots;
-    return live ? (int32_t)(((int64_t)blk * Hkv + gk) * block_size + off) : -1;
+    const bool live = t < c1 && bi < mb32 && blk >= 0 && (int64_t)blk * block_size + off < num_slots;
+    return live ? (int32_t)(((uint32_t)blk * (uint32_t)Hkv + (uint32_t)gk) * bs32 + off) : -1;
   };
   const int g8 = lane >> 3, c8 = lane & 7;
   int32_t krow[4], vrow[8];

@@ -102,6 +102,17 @@ def test_softmax_scale_and_block_size(fp8blk_lib):
                                 what="sm_scale %g" % sm)
 
 
+@pytest.mark.parametrize("bs", [12, 48])
+@pytest.mark.parametrize("mode", ["direct", "split_256"])
+def test_block_size_not_a_power_of_two(fp8blk_lib, bs, mode):
+    """Pages of 12 or 48 tokens: the kernel divides token positions by the
+    block size instead of shifting (a power of two takes the shift)."""
+    a, kc, vc, sc = build([33, 130, 700, 1], 16, 4, seed=8, bs=bs)
+    out = run(a, kc, vc, sc, mode=mode)
+    assert_within_tolerance(out.float().cpu().numpy().reshape(4, -1), reference(a, kc, vc, sc).reshape(4, -1),
+                            what="block size %d" % bs)
+
+
 @pytest.mark.parametrize("mode", ["direct", "split_256"])
 @pytest.mark.parametrize("sm,ramp", [(1.0, None), (0.3, 64.0), (1.0, 16.0)])
 def test_large_score_jumps(fp8blk_lib, sm, ramp, mode):

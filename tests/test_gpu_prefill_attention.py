@@ -115,6 +115,17 @@ def test_negative_and_zero_softmax_scale(fp8blk_lib, sm):
     assert_within_tolerance(out.float().cpu().numpy().reshape(-1), ref.reshape(-1), what="prefill attention sm %g" % sm)
 
 
+@pytest.mark.parametrize("bs", [12, 48])
+def test_block_size_not_a_power_of_two(fp8blk_lib, bs):
+    """Pages of 12 or 48 tokens: the kernel divides token positions by the
+    block size instead of shifting (a power of two takes the shift)."""
+    seqs = [(130, 300), (64, 64), (1, 777), (17, 1000)]
+    a, kc, vc, sc = build(seqs, 16, 4, seed=9, bs=bs)
+    out = run(a, kc, vc, sc)
+    ref = reference(a, kc, vc, sc)
+    assert_within_tolerance(out.float().cpu().numpy().reshape(-1), ref.reshape(-1), what="block size %d" % bs)
+
+
 def test_tokens_past_max_seqlen_are_left_alone(fp8blk_lib):
     """max_seqlen_q below a sequence's new tokens: the tokens past it are not
     computed (their rows keep what the caller put there); the others match."""
