@@ -449,18 +449,19 @@ def _dense_sampled_check(x, w, rows, pow2=False, nudge=None):
 
 
 @pytest.mark.parametrize("pow2", [False, True])
-@pytest.mark.parametrize("m,k", [(6000, 256), (6144, 384)])
-def test_dense_persistent_tile_walk(fp8blk_lib, m, k, pow2):
+@pytest.mark.parametrize("m,k,n", [(6000, 256, 8192), (6144, 384, 8192), (6144, 256, 8320)])
+def test_dense_persistent_tile_walk(fp8blk_lib, m, k, n, pow2):
     """At least three 256x256 tiles per CU and a short K: the persistent
     kernel, each workgroup walking its XCD's tiles with the next tile's
     first K blocks loaded during the current tile's last steps (K = 256:
     every step of a tile loads the next one's; K = 384: an odd block
-    count), M = 6000 leaving a partial last row tile. Checked on the first
-    and last rows of every row tile and random rows, all 8192 columns."""
-    print("dense persistent m=%d k=%d pow2=%s" % (m, k, pow2), flush=True)
-    g = synth.generator(16, seed=m + k)
+    count), M = 6000 leaving a partial last row tile, N = 8320 a last
+    column tile half past N. Checked on the first and last rows of every
+    row tile and random rows, all columns."""
+    print("dense persistent m=%d k=%d n=%d pow2=%s" % (m, k, n, pow2), flush=True)
+    g = synth.generator(16, seed=m + k + n)
     x = synth.activation(m, k, g, 0.005, 30.0)
-    w = synth.weight(8192, k, g)
+    w = synth.weight(n, k, g)
     edges = {r for t in range(0, m, 256) for r in (t, min(t + 255, m - 1))}
     rnd = torch.randint(0, m, (32,), generator=g).tolist()
     _dense_sampled_check(x, w, np.array(sorted(edges | set(rnd)), dtype=np.int64), pow2)
