@@ -44,9 +44,12 @@ def operands(m, n, k, seed, pow2=False):
 
 
 # (M, N, K): the 256x256, 128x128, 64x64 and 256x128 tiles, the pow2
-# in-MFMA path of the 256x256 tile, partial tiles on every edge
+# in-MFMA path of the 256x256 tile, partial tiles on every edge, and the
+# persistent walk of 256x256 tiles (at least three per CU, K <= 64 blocks)
+# in both scale paths, with a partial row and column tile
 GEMMS = [(4096, 4096, 1024, False), (4096, 2048, 1024, False), (300, 512, 1024, False),
-         (256, 28672, 1024, False), (4096, 4096, 1024, True), (4000, 3968, 640, False)]
+         (256, 28672, 1024, False), (4096, 4096, 1024, True), (4000, 3968, 640, False),
+         (6144, 8192, 512, False), (6144, 8192, 512, True), (6000, 8320, 384, False)]
 
 
 @pytest.mark.parametrize("m,n,k,pow2", GEMMS)
