@@ -16,7 +16,7 @@ LIB = os.path.join(PKG, "libfp8blk.so")
 # race-detection variant: the kernels that stage operands through LDS, with
 # an extra barrier at every stage transition (same C ABI for those calls)
 DEBUG_LIB = os.path.join(PKG, "libfp8blk_debug_barriers.so")
-DEBUG_SOURCES = ("gemm.hip", "prefill_attention.hip")
+DEBUG_SOURCES = ("gemm.hip", "prefill_attention.hip", "attention.hip")
 DEBUG_FLAGS = ["-DFP8BLK_DEBUG_BARRIERS=1"]
 
 SOURCES = ("quant.hip", "gemm.hip", "kv_cache.hip", "attention.hip", "prefill_attention.hip")

@@ -85,6 +85,21 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Race-detection build (-DFP8BLK_DEBUG_BARRIERS=1): before each rewrite of
+// an LDS region this wave has just read (the row exchange, the V tile) the
+// wave also waits for all of its memory operations, so no rewrite can pass
+// a read still in flight; the arithmetic is unchanged and the outputs must
+// equal the normal build's bit for bit.
+#ifndef FP8BLK_DEBUG_BARRIERS
+#define FP8BLK_DEBUG_BARRIERS 0
+#endif
+__device__ __forceinline__ void debug_wave_sync() {
+  if constexpr (FP8BLK_DEBUG_BARRIERS != 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <int G, bool SPLIT>  // G = query heads per KV head: 1, 2, 4 or 8
 __global__ __launch_bounds__(256) void decode_attention_kernel(
     const uint16_t* __restrict__ q, int64_t ldq, int64_t Hkv, const uint8_t* __restrict__ k_cache,
@@ -195,6 +210,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
   const int g8 = lane >> 3, c8 = lane & 7;
   int32_t krow[4], vrow[8];
   auto read_rows = [&](int32_t row) {  // exchange the tile's cache rows through LDS
+    debug_wave_sync();
     row_tile[wave][lane] = row;
     wave_lds_sync();
 #pragma unroll
@@ -341,6 +357,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
           acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pl, acc[dt], 0, 0, 0);
         }
       }
+      debug_wave_sync();
       t0 = tn;
       if (t0 >= c1) break;
     }

@@ -1,6 +1,6 @@
 """Race detection on the GPU: the kernels that stage operands through LDS
 (every GEMM tile configuration, the split-K, grouped and row-scaled GEMMs,
-the prefill attention) built with an extra barrier at every LDS stage
+the prefill and decode attention) built with an extra barrier at every LDS stage
 transition (libfp8blk_debug_barriers.so, -DFP8BLK_DEBUG_BARRIERS=1) must give
 the normal build's outputs bit for bit: the arithmetic is identical, so any
 difference would come from a stage read while being refilled or refilled
@@ -136,3 +136,25 @@ def test_prefill_attention(dbg):
                                         lens.data_ptr(), sc[0:1].data_ptr(), sc[1:2].data_ptr(), sc[2:3].data_ptr(),
                                         128 ** -0.5, o1.data_ptr(), 32 * 128, stream()) == 0
     same(o0, o1, "prefill attention")
+
+
+@pytest.mark.parametrize("split", [0, 256])
+def test_decode_attention(dbg, split):
+    a = synth.attention_inputs([700, 33, 2048, 1], 32, 8, 128, 16, 11)
+    nslots = a["num_slots"]
+    kc = synth.random_cache_codes((nslots // 16, 8, 16, 128), 33, DEV)
+    vc = synth.random_cache_codes((nslots // 16, 8, 16, 128), 34, DEV)
+    sc = torch.tensor([4.0 / 448, 0.004, 0.01], dtype=torch.float32, device=DEV)
+    q, table, lens = a["q"].to(DEV), a["block_table"].to(DEV), a["context_lens"].to(DEV)
+    b = q.shape[0]
+    need = fb.fp8blk_decode_attention_workspace_size(b, 32, 8, 128, table.shape[1], 16, split) if split else 0
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    outs = []
+    for lib in (fb.load(), dbg):
+        o = torch.empty(b, 32, 128, dtype=torch.bfloat16, device=DEV)
+        assert lib.fp8blk_decode_attention(q.data_ptr(), 32 * 128, b, 32, 8, 128, kc.data_ptr(), vc.data_ptr(), nslots,
+                                           table.data_ptr(), table.shape[1], 16, lens.data_ptr(), sc[0:1].data_ptr(),
+                                           sc[1:2].data_ptr(), sc[2:3].data_ptr(), 128 ** -0.5, o.data_ptr(), 32 * 128,
+                                           split, ws.data_ptr() if need else None, need, stream()) == 0
+        outs.append(o)
+    same(outs[0], outs[1], "decode attention split=%d" % split)
