@@ -258,6 +258,14 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
     // S^T: lane (c, g) gets s[u][qt][r] = score of token t0 + 16u + 4g + r, row 16qt + c
     float s[4][2][4];
     auto scores = [&](bool masked, bool raw) {
+      // causal mask: token t0 + 16u + 4g + r is kept when t <= min(pos, L - 1),
+      // i.e. 16u + r <= rel[qt] (tiles that need the mask lie within 64
+      // tokens of the block's positions, so the differences are small ints)
+      int rel[2] = {0, 0};
+      if (masked) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) rel[qt] = (int)((pos[qt] < L - 1 ? pos[qt] : L - 1) - t0) - 4 * g;
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint8_t* krow = K + (16 * u + c16) * kKRow + 16 * g;
@@ -271,10 +279,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attention_kernel(
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + 16 * u + 4 * g + r;
-            s[u][qt][r] = raw ? d[qt][r] : !masked || (t <= pos[qt] && t < L) ? d[qt][r] * s2scale : -INFINITY;
-          }
+          for (int r = 0; r < 4; ++r)
+            s[u][qt][r] = raw ? d[qt][r] : !masked || 16 * u + r <= rel[qt] ? d[qt][r] * s2scale : -INFINITY;
         }
       }
     };
