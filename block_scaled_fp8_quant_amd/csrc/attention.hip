@@ -78,6 +78,25 @@ __device__ const uint32_t kZeroRow[kHeadDim / 4] = {};
 typedef const __attribute__((address_space(1))) uint8_t* gbytes;
 __device__ __forceinline__ gbytes as_global(const uint8_t* p) { return (gbytes)p; }
 
+// fp32 maximum / sum over the four lanes c, c+16, c+32, c+48, by the
+// lane-swap instructions (no LDS round trip): with both operands v,
+// v_permlane16_swap returns (v[l], v[l+16]) in even 16-lane rows and
+// (v[l-16], v[l]) in odd ones, v_permlane32_swap the same for halves (lane
+// layout checked on the GPU), so combining the two results gives each lane
+// the pair's maximum or sum, in the same order in both lanes of the pair.
+__device__ __forceinline__ float cross4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float cross4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Make this wave's LDS writes visible to its own later LDS reads by other
 // lanes (LDS operations of one wave complete in order).
 __device__ __forceinline__ void wave_lds_sync() {
@@ -296,8 +315,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
       float mt = -INFINITY;
 #pragma unroll
       for (int u = 0; u < 4; ++u) mt = fmaxf(mt, fmaxf(fmaxf(s[u][0], s[u][1]), fmaxf(s[u][2], s[u][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      mt = cross4_max(mt);
       const float mn = mt > m_run + kSlackAttn ? mt : m_run;
       const float ms = mn == -INFINITY ? 0.f : mn;  // no token yet: keep exp2 finite
       const float alpha = __builtin_amdgcn_exp2f(m_run - ms);
@@ -364,8 +382,7 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(
   }
 
   // this wave's totals: the four lanes of a head add their shares of the sum
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = cross4_sum(l_run);
   if (head_lane) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)

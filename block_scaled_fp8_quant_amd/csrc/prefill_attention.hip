@@ -86,14 +86,23 @@ __device__ __forceinline__ void debug_stage_sync() {
   }
 }
 
-// fp32 maximum / sum over the four lanes c, c+16, c+32, c+48
+// fp32 maximum / sum over the four lanes c, c+16, c+32, c+48, by the
+// lane-swap instructions (no LDS round trip): with both operands v,
+// v_permlane16_swap returns (v[l], v[l+16]) in even 16-lane rows and
+// (v[l-16], v[l]) in odd ones, v_permlane32_swap the same for halves (lane
+// layout checked on the GPU), so combining the two results gives each lane
+// the pair's maximum or sum, in the same order in both lanes of the pair.
 __device__ __forceinline__ float cross4_max(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float cross4_sum(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int G>  // query heads per KV head: 1, 2, 4 or 8
