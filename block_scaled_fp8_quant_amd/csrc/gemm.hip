@@ -36,7 +36,12 @@
 //   * the epilogue rounds to bf16 (nearest even) and stores 8 bytes a lane;
 //   * workgroups are handed out round-robin over the 8 XCDs; the tile order
 //     gives each XCD a contiguous band of tiles so neighbours share A rows
-//     and B columns in that XCD's L2.
+//     and B columns in that XCD's L2;
+//   * with many short tiles (at least three 256x256 tiles per CU, at most 64
+//     K blocks) a persistent grid walks the same order, each workgroup
+//     loading its next tile's first K blocks during its current tile's last
+//     steps; the expert-grouped GEMM walks its tiles the same way whenever
+//     they outnumber the resident workgroups.
 #include <atomic>
 #include <mutex>
 
