@@ -8,7 +8,7 @@ the recalibrated Q/K/V scales; the greentreeone.com article, section
 «Реальные прирост производительности»: FP8 for the KV cache and the
 attention operations.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * the decode step: each sequence's new query token attends over every token
   cached for it (context_len tokens, the new one included once written);
@@ -37,7 +37,7 @@ tables) and against the two-token closed form: the first token's weight is
 the logistic function of the score difference. Planted mistakes in the
 scaling (k_scale dropped, sm_scale squared, 1/D for the default) fail them.
 
-The prefill step (same sources; readings in the design doc): a sequence's n new
+The prefill step (same sources; readings where they are silent): a sequence's n new
 tokens are the last n of its context_len cached tokens, so new token i sits
 at position p = context_len - n + i and its query attends causally over the
 cached tokens 0..p; scores, softmax and the weighted sum as in the decode

@@ -11,7 +11,7 @@ rollout, at 2-3% of the step. The greentreeone.com article, section
 «Реальные прирост производительности»: FP8 KV cache and attention, with the
 quantization scales recalibrated after every training step.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
 
 * granularity: one scale per tensor -- Q, K and V of one attention layer --
   over all calibration tokens; amax accumulates over every chunk of the

@@ -4,7 +4,7 @@ Granularity: the greentreeone.com NeMo RL article, section ¬´–¢–µ—Ö–Ω–∏—á–µ—Å–∫–
 –ø—Ä–æ—Ä—ã–≤¬ª, gives one scale per 1x128 activation group (one row, 128 consecutive
 columns of the reduction dimension K) and one per 128x128 weight block.
 
-Readings taken where the pages are silent (each one listed in the design doc):
+Readings taken where the pages are silent:
 
 * scale s = amax / 448 rounded once to fp32, stored as the dequantisation
   multiplier (x ~ dec(q) * s); amax is the largest |x| in the group or block;

@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def fp8blk_lib():
-    """The HIP library's Python binding, on a GPU machine."""
+    """The HIP library's Python binding, on a machine with a GPU."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
