@@ -86,6 +86,9 @@ def parse():
                    help="turn two rocprofv3 --pmc CSVs into profiles/traffic.json and exit")
     p.add_argument("--summarize-trace", metavar="STATS_CSV",
                    help="print a markdown table of a rocprofv3 --stats kernel_stats.csv")
+    p.add_argument("--summarize-step-trace", metavar="TRACE_CSV",
+                   help="per-layer durations of the step's GEMM launches in a rocprofv3 --kernel-trace "
+                        "kernel_trace.csv of a bench run with the same --workload, --warmup and --steps")
     p.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                    help="print a per-kernel markdown summary of rocprofv3 counter_collection.csv files")
     return p.parse_args()
@@ -1025,8 +1028,59 @@ def summarize_trace(stats_csv):
     return "\n".join(out)
 
 
+def step_layer_names(workload):
+    """The names of a workload's step layers, in launch order."""
+    import synth
+    if workload == "moe":
+        return ["moe_gate_up", "moe_down"]
+    return [nm for nm, _, _ in synth.WORKLOADS[workload].linears]
+
+
+def summarize_step_trace(trace_csv, workload, warmup, steps):
+    """The step's GEMM launches in a rocprofv3 kernel_trace.csv of a bench run
+    (same workload, warm-up and step counts): the dispatches are taken in
+    start order, a layer's GEMM launch being the GEMM-family dispatches
+    (dense, persistent, grouped, split-K and its reduction) that follow its
+    quant_act dispatch. Reports each layer's mean over the timed steps and
+    the mean per launch, the figure the bench's roofline.avg_launch_ms gives
+    from HIP events around the same launches."""
+    import csv
+    names = step_layer_names(workload)
+    with open(trace_csv) as f:
+        rows = sorted(csv.DictReader(f), key=lambda r: int(r["Start_Timestamp"]))
+    launches, cur = [], None
+    want = (warmup + steps) * len(names)
+    for r in rows:
+        nm = r["Kernel_Name"]
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if "gemm" in nm or "splitk_reduce" in nm:
+            if cur is not None:
+                cur += dur
+            continue
+        if cur is not None:
+            launches.append(cur)
+            cur = None
+            if len(launches) == want:
+                break
+        if "::quant_act_kernel(" in nm:
+            cur = 0
+    if cur is not None and len(launches) < want:
+        launches.append(cur)
+    if len(launches) < want:
+        raise SystemExit("found %d GEMM launches, expected %d" % (len(launches), want))
+    timed = launches[warmup * len(names):want]
+    per_layer = {nm: sum(timed[i::len(names)]) / steps / 1e3 for i, nm in enumerate(names)}
+    mean = sum(timed) / len(timed) / 1e3
+    return ("Step GEMM launches in the per-dispatch trace (the %d timed steps; a launch is the GEMM-family "
+            "dispatches after its layer's quant_act, a split-K launch with its reduction): %s us; mean per "
+            "launch %.1f us." % (steps, ", ".join("%s %.1f" % kv for kv in per_layer.items()), mean))
+
+
 def main():
     args = parse()
+    if args.summarize_step_trace:
+        print(summarize_step_trace(args.summarize_step_trace, args.workload, args.warmup, args.steps))
+        return
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace))
         return

@@ -56,3 +56,33 @@ def test_groups_by_grid_and_sorts_by_time(tmp_path):
     assert len(lines) == 2
     first = [c.strip() for c in lines[0].strip("|").split("|")]
     assert first[1] == "20" and first[2] == "2" and first[3] == "6.0" and "SQ_WAVES 3" in first[5]
+
+
+def test_step_trace_groups_gemm_launches_by_layer(tmp_path):
+    # one warm-up and two timed steps of the two MoE layers; the second layer's
+    # launch is split over two GEMM-family dispatches, and a fused producer
+    # (whose name also holds "quant_act_kernel") and a side-section GEMM follow
+    qw = "fp8blk::(anonymous namespace)::quant_weight_kernel(long)"
+    qa = "fp8blk::(anonymous namespace)::quant_act_kernel(long)"
+    gm = "void fp8blk::(anonymous namespace)::grouped_gemm_persistent_kernel<Tile>(long)"
+    red = "fp8blk::(anonymous namespace)::splitk_reduce_kernel(long)"
+    silu = "fp8blk::(anonymous namespace)::silu_mul_quant_act_kernel(long)"
+    seq = []
+    for step in range(3):
+        seq += [(qw, 5), (qw, 5), (qa, 3), (gm, 100 + step), (qa, 3), (gm, 40), (red, 10 + step)]
+    seq += [(silu, 7), (gm, 999)]
+    path = tmp_path / "kt_kernel_trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        t = 1000
+        rows = []
+        for name, us in seq:
+            rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + us * 1000})
+            t += us * 1000 + 500
+        for r in reversed(rows):  # the summary orders by start time, not by row
+            w.writerow(r)
+    out = bench.summarize_step_trace(str(path), "moe", 1, 2)
+    # timed steps 1 and 2: gate_up (101 + 102) / 2, down (40 + 11 + 40 + 12) / 2
+    assert "moe_gate_up 101.5, moe_down 51.5 us" in out
+    assert "mean per launch 76.5 us" in out
