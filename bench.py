@@ -1243,6 +1243,10 @@ def main():
         print("bench: timing the FP8 prefill attention", file=sys.stderr, flush=True)
         torch.cuda.empty_cache()
         out["prefill_attention"] = time_prefill_attention(fb, args.workload, dev, 5)
+        import synth
+        g = synth.ATTENTION[args.workload][0] // synth.ATTENTION[args.workload][1]
+        t = traffic_rec.get("prefill_attention_kernel<%d>" % g, {}).get("bytes_per_launch")
+        out["prefill_attention"]["traffic"] = None if t is None else round(t)
     if not args.no_cpu_baseline:
         print("bench: timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_sample_rows, args.cpu_sample_wrows, sample)
