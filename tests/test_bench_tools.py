@@ -86,3 +86,15 @@ def test_step_trace_groups_gemm_launches_by_layer(tmp_path):
     # timed steps 1 and 2: gate_up (101 + 102) / 2, down (40 + 11 + 40 + 12) / 2
     assert "moe_gate_up 101.5, moe_down 51.5 us" in out
     assert "mean per launch 76.5 us" in out
+
+
+def test_more_than_one_gpu_is_refused():
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for extra, env in ((["--gpus", "2"], {}), ([], {"WORLD_SIZE": "4"})):
+        r = subprocess.run([sys.executable, os.path.join(root, "bench.py")] + extra, capture_output=True, text=True,
+                           env=dict(os.environ, **env), timeout=120)
+        assert r.returncode == 2
+        assert "exactly one GPU" in r.stderr and r.stdout == ""
